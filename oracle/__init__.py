@@ -1,0 +1,225 @@
+"""Python face of the fp64 CPU oracle (liboracle.so, built from oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the package smoke check
+and the CPU-baseline leg of the benchmark, never by the product path. It shares
+no code with the HIP library; only the seeded input generators are common.
+
+Each wrapper converts numpy inputs to the C types and returns numpy outputs;
+all arithmetic is in oracle.c (see its header for the equations followed).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib: Optional[ctypes.CDLL] = None
+
+i64p = ctypes.POINTER(ctypes.c_int64)
+i32p = ctypes.POINTER(ctypes.c_int32)
+f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, IEEE semantics: no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        L.oracle_anchor_profile.argtypes = [ctypes.c_int64, i64p, i64p, ctypes.c_int64,
+                                            ctypes.c_int64, i64p]
+        for name in ("oracle_chunk_costs", "oracle_chunk_costs_prefix"):
+            getattr(L, name).argtypes = [ctypes.c_int64, i64p, i64p, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int64, i64p]
+        L.oracle_lpt.argtypes = [ctypes.c_int64, i64p, ctypes.c_int32, ctypes.c_int32,
+                                 i32p, i32p, i64p]
+        L.oracle_lpt.restype = ctypes.c_int
+        L.oracle_zigzag_loads.argtypes = [ctypes.c_int64, i64p, i64p, i64p, ctypes.c_int32, i64p]
+        L.oracle_zigzag_loads.restype = ctypes.c_int
+        L.oracle_contiguous_loads.argtypes = [ctypes.c_int64, i64p, ctypes.c_int32, i64p]
+        L.oracle_contiguous_loads.restype = ctypes.c_int
+        L.oracle_imbalance.argtypes = [ctypes.c_int32, i64p, ctypes.c_int64, ctypes.c_int64]
+        L.oracle_imbalance.restype = ctypes.c_double
+        L.oracle_partial_attn.argtypes = [ctypes.c_int64, i64p, ctypes.c_int64, i64p, i64p,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_double, f64p, ctypes.c_int64, i64p,
+                                          f64p, f64p, f64p, f64p]
+        L.oracle_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, f64p, f64p,
+                                   f64p, f64p]
+        L.oracle_delta.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, f64p, f64p,
+                                   f64p]
+        L.oracle_attn_bwd.argtypes = [ctypes.c_int64, ctypes.c_int64, i64p, i64p,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_double, f64p, f64p, f64p, f64p,
+                                      ctypes.c_int64, i64p, f64p, f64p,
+                                      ctypes.c_int64, i64p, f64p, ctypes.c_int64, i64p,
+                                      f64p, f64p]
+        _lib = L
+    return _lib
+
+
+def _p(x: np.ndarray, ctype):
+    return x.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _i64(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.int64)
+
+
+def _f64(x) -> np.ndarray:
+    if getattr(x, "dtype", None) == np.uint16:
+        raise TypeError("pass widened values, not raw bf16 bits")
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- planner --
+def anchor_profile(s, a, B: int, S: int) -> np.ndarray:
+    s, a = _i64(s), _i64(a)
+    out = np.zeros(S, dtype=np.int64)
+    lib().oracle_anchor_profile(len(s), _p(s, ctypes.c_int64), _p(a, ctypes.c_int64), B, S,
+                                _p(out, ctypes.c_int64))
+    return out
+
+
+def chunk_costs(s, a, B: int, n_chunks: int, m: int, form: str = "direct") -> np.ndarray:
+    s, a = _i64(s), _i64(a)
+    out = np.zeros(n_chunks, dtype=np.int64)
+    fn = lib().oracle_chunk_costs if form == "direct" else lib().oracle_chunk_costs_prefix
+    fn(len(s), _p(s, ctypes.c_int64), _p(a, ctypes.c_int64), B, n_chunks, m,
+       _p(out, ctypes.c_int64))
+    return out
+
+
+def lpt(cost, P: int, J: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Returns (owner [PJ] int32, bundles [P, J] int32, load [P] int64)."""
+    cost = _i64(cost)
+    owner = np.zeros(len(cost), dtype=np.int32)
+    bundles = np.zeros((P, J), dtype=np.int32)
+    load = np.zeros(P, dtype=np.int64)
+    rc = lib().oracle_lpt(len(cost), _p(cost, ctypes.c_int64), P, J, _p(owner, ctypes.c_int32),
+                          _p(bundles, ctypes.c_int32), _p(load, ctypes.c_int64))
+    if rc != 0:
+        raise ValueError("oracle_lpt: number of chunks must equal P*J")
+    return owner, bundles, load
+
+
+def plan(s, a, B: int, S: int, m: int, P: int, J: int):
+    """Eq. 6 costs then LPT; returns (cost, owner, bundles, load)."""
+    cost = chunk_costs(s, a, B, S // m, m)
+    owner, bundles, load = lpt(cost, P, J)
+    return cost, owner, bundles, load
+
+
+def zigzag_loads(sample_start, sample_len, prof, P: int) -> np.ndarray:
+    st, ln, pr = _i64(sample_start), _i64(sample_len), _i64(prof)
+    out = np.zeros(P, dtype=np.int64)
+    rc = lib().oracle_zigzag_loads(len(st), _p(st, ctypes.c_int64), _p(ln, ctypes.c_int64),
+                                   _p(pr, ctypes.c_int64), P, _p(out, ctypes.c_int64))
+    if rc != 0:
+        raise ValueError("zigzag needs sample lengths divisible by 2P")
+    return out
+
+
+def contiguous_loads(prof, P: int) -> np.ndarray:
+    pr = _i64(prof)
+    out = np.zeros(P, dtype=np.int64)
+    if lib().oracle_contiguous_loads(len(pr), _p(pr, ctypes.c_int64), P,
+                                     _p(out, ctypes.c_int64)) != 0:
+        raise ValueError("context length must be divisible by P")
+    return out
+
+
+def imbalance(ctx_load, n_blocks: int, B: int) -> float:
+    ld = _i64(ctx_load)
+    return float(lib().oracle_imbalance(len(ld), _p(ld, ctypes.c_int64), n_blocks, B))
+
+
+# -------------------------------------------------------------- attention --
+def partial_attn(rows, B: int, s, a, q_sel, key_pos, k, v, scale: float):
+    """Eq. 3 for the given rows. q_sel [n, hq, d]; k, v [n_keys, hkv, d] (widened to fp64).
+
+    Returns (o [n, hq, d] fp64, lse [n, hq] fp64)."""
+    rows, s, a, key_pos = _i64(rows), _i64(s), _i64(a), _i64(key_pos)
+    q_sel, k, v = _f64(q_sel), _f64(k), _f64(v)
+    n, hq, d = q_sel.shape
+    hkv = k.shape[1]
+    assert k.shape == v.shape and k.shape[0] == len(key_pos) and len(rows) == n
+    o = np.zeros((n, hq, d), dtype=np.float64)
+    lse = np.zeros((n, hq), dtype=np.float64)
+    lib().oracle_partial_attn(n, _p(rows, ctypes.c_int64), B, _p(s, ctypes.c_int64),
+                              _p(a, ctypes.c_int64), hq, hkv, d, float(scale),
+                              _p(q_sel, ctypes.c_double), len(key_pos),
+                              _p(key_pos, ctypes.c_int64), _p(k, ctypes.c_double),
+                              _p(v, ctypes.c_double), _p(o, ctypes.c_double),
+                              _p(lse, ctypes.c_double))
+    return o, lse
+
+
+def merge(o_parts, lse_parts):
+    """Eq. 4. o_parts [P, rows, d], lse_parts [P, rows] -> (o [rows, d], lse [rows])."""
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    P, rows, d = o_parts.shape
+    o = np.zeros((rows, d), dtype=np.float64)
+    lse = np.zeros(rows, dtype=np.float64)
+    lib().oracle_merge(P, rows, d, _p(o_parts, ctypes.c_double), _p(lse_parts, ctypes.c_double),
+                       _p(o, ctypes.c_double), _p(lse, ctypes.c_double))
+    return o, lse
+
+
+def delta(o, dout) -> np.ndarray:
+    """Delta[r, h] = <do[r, h], o[r, h]> for o, do [rows, hq, d]."""
+    o, dout = _f64(o), _f64(dout)
+    rows, hq, d = o.shape
+    out = np.zeros((rows, hq), dtype=np.float64)
+    lib().oracle_delta(rows, hq, d, _p(o, ctypes.c_double), _p(dout, ctypes.c_double),
+                       _p(out, ctypes.c_double))
+    return out
+
+
+def attn_bwd(B: int, s, a, q, dout, lse, dlt, key_pos, k, v, scale: float,
+             dq_rows, dkv_keys):
+    """Backward of the local partial given global lse and Delta.
+
+    q, dout [Q, hq, d]; lse, dlt [Q, hq]; k, v [n_keys, hkv, d].
+    Returns (dq [len(dq_rows), hq, d], dk, dv [len(dkv_keys), hkv, d]) in fp64."""
+    s, a, key_pos = _i64(s), _i64(a), _i64(key_pos)
+    q, dout, k, v = _f64(q), _f64(dout), _f64(k), _f64(v)
+    lse, dlt = _f64(lse), _f64(dlt)
+    dq_rows, dkv_keys = _i64(dq_rows), _i64(dkv_keys)
+    Q, hq, d = q.shape
+    hkv = k.shape[1]
+    dq = np.zeros((len(dq_rows), hq, d), dtype=np.float64)
+    dk = np.zeros((len(dkv_keys), hkv, d), dtype=np.float64)
+    dv = np.zeros((len(dkv_keys), hkv, d), dtype=np.float64)
+    lib().oracle_attn_bwd(Q, B, _p(s, ctypes.c_int64), _p(a, ctypes.c_int64), hq, hkv, d,
+                          float(scale), _p(q, ctypes.c_double), _p(dout, ctypes.c_double),
+                          _p(lse, ctypes.c_double), _p(dlt, ctypes.c_double), len(key_pos),
+                          _p(key_pos, ctypes.c_int64), _p(k, ctypes.c_double),
+                          _p(v, ctypes.c_double), len(dq_rows), _p(dq_rows, ctypes.c_int64),
+                          _p(dq, ctypes.c_double), len(dkv_keys), _p(dkv_keys, ctypes.c_int64),
+                          _p(dk, ctypes.c_double), _p(dv, ctypes.c_double))
+    return dq, dk, dv
+
+
+def local_key_positions(chunk_ids, m: int) -> np.ndarray:
+    """Global context position of each row of a local buffer made of the given chunks
+    (chunk j covers [j*m, (j+1)*m)), in buffer order."""
+    ids = _i64(chunk_ids)
+    return (ids[:, None] * m + np.arange(m, dtype=np.int64)[None, :]).reshape(-1)
