@@ -1,0 +1,275 @@
+"""Thin Python binding of libsplitkv.so (the C ABI in include/splitkv.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, and their device pointers are handed to the library together with
+torch's current HIP stream. Every step of the hot path runs in the library's
+kernels; there is no fallback. If the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsplitkv.so")
+
+SPLITKV_OK = 0
+SPLITKV_ERR_INVALID_ARG = -1
+SPLITKV_ERR_UNSUPPORTED = -2
+SPLITKV_ERR_WORKSPACE = -3
+SPLITKV_ERR_HIP = -4
+
+SPLITKV_BF16 = 0
+SPLITKV_FP32 = 1
+
+SPLITKV_OP_PLAN, SPLITKV_OP_FWD, SPLITKV_OP_BWD, SPLITKV_OP_MERGE = 0, 1, 2, 3
+
+EXPORTED = ("splitkv_workspace_bytes", "splitkv_plan", "splitkv_attn_fwd", "splitkv_lse_merge",
+            "splitkv_attn_bwd", "splitkv_status_str")
+
+
+class SplitKVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (%d)" % (fn, status_str(status), status))
+        self.status = status
+
+
+class Anchors(ctypes.Structure):
+    _fields_ = [("s", ctypes.c_void_p), ("a", ctypes.c_void_p), ("n_blocks", ctypes.c_int64),
+                ("block_size", ctypes.c_int32)]
+
+
+class Heads(ctypes.Structure):
+    _fields_ = [("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class Local(ctypes.Structure):
+    _fields_ = [("chunk_start", ctypes.c_void_p), ("n_chunks", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int64)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsplitkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsplitkv.so is not built; run `python -m "
+                               "block_sparse_cross_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        A, H, Lc = ctypes.POINTER(Anchors), ctypes.POINTER(Heads), ctypes.POINTER(Local)
+        L.splitkv_workspace_bytes.argtypes = [ctypes.c_int, A, H, Lc]
+        L.splitkv_workspace_bytes.restype = sz
+        L.splitkv_plan.argtypes = [A, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_int32, vp, vp, vp, vp, vp]
+        L.splitkv_plan.restype = ctypes.c_int
+        L.splitkv_attn_fwd.argtypes = [A, H, Lc, vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
+        L.splitkv_attn_fwd.restype = ctypes.c_int
+        L.splitkv_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp,
+                                        ctypes.c_int, vp, vp, ctypes.c_int, vp, vp]
+        L.splitkv_lse_merge.restype = ctypes.c_int
+        L.splitkv_attn_bwd.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.splitkv_attn_bwd.restype = ctypes.c_int
+        L.splitkv_status_str.argtypes = [ctypes.c_int]
+        L.splitkv_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().splitkv_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SPLITKV_OK:
+        raise SplitKVError(fn, status)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return SPLITKV_BF16
+    if t == torch.float32:
+        return SPLITKV_FP32
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % t)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_anchors(s: torch.Tensor, a: torch.Tensor, block_size: int) -> Anchors:
+    if s.dtype != torch.int64 or a.dtype != torch.int64 or s.shape != a.shape or s.dim() != 1:
+        raise ValueError("anchors: s and a must be int64 vectors of equal length")
+    return Anchors(_ptr(s), _ptr(a), s.numel(), int(block_size))
+
+
+def make_heads(hq: int, hkv: int, d: int, dtype: torch.dtype, scale: Optional[float] = None) -> Heads:
+    return Heads(int(hq), int(hkv), int(d), _dtype_code(dtype),
+                 float(d ** -0.5 if scale is None else scale))
+
+
+def make_local(chunk_start: torch.Tensor, chunk_len: int) -> Local:
+    if chunk_start.dtype != torch.int64 or chunk_start.dim() != 1:
+        raise ValueError("chunk_start must be an int64 vector")
+    return Local(_ptr(chunk_start), chunk_start.numel(), int(chunk_len))
+
+
+def splitkv_workspace_bytes(op: int, an: Optional[Anchors] = None, hd: Optional[Heads] = None,
+                            loc: Optional[Local] = None) -> int:
+    return int(lib().splitkv_workspace_bytes(
+        int(op), ctypes.byref(an) if an is not None else None,
+        ctypes.byref(hd) if hd is not None else None,
+        ctypes.byref(loc) if loc is not None else None))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    """(pointer, size) of the caller's workspace, or of a fresh one of nbytes.
+    A caller-supplied workspace is passed as is; the library checks its size."""
+    if ws is None:
+        if nbytes == 0:
+            return None, 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _keepalive.append(ws)
+        if len(_keepalive) > 4:
+            del _keepalive[0]
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+# Recently allocated workspaces stay referenced until later calls so that the
+# caching allocator cannot hand their memory out while a kernel still uses it.
+_keepalive = []
+
+
+def splitkv_plan(s: torch.Tensor, a: torch.Tensor, block_size: int, S: int, m: int, P: int,
+                 J: int, out: Optional[Tuple[torch.Tensor, ...]] = None,
+                 stream: Optional[torch.cuda.Stream] = None):
+    """Eq. 6 chunk costs + cost-aware LPT on the GPU.
+
+    Returns (chunk_cost int64 [P*J], chunk_owner int32 [P*J],
+    rank_chunks int32 [P, J], rank_load int64 [P]) as device tensors."""
+    dev = s.device
+    if out is None:
+        out = (torch.empty(P * J, dtype=torch.int64, device=dev),
+               torch.empty(P * J, dtype=torch.int32, device=dev),
+               torch.empty((P, J), dtype=torch.int32, device=dev),
+               torch.empty(P, dtype=torch.int64, device=dev))
+    cost, owner, chunks, load = out
+    an = make_anchors(s, a, block_size)
+    _check("splitkv_plan", lib().splitkv_plan(ctypes.byref(an), int(S), int(m), int(P), int(J),
+                                              _ptr(cost), _ptr(owner), _ptr(chunks), _ptr(load),
+                                              _stream(stream)))
+    return out
+
+
+def splitkv_attn_fwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v,
+                     scale: Optional[float] = None, o_dtype: Optional[torch.dtype] = None,
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None):
+    """Eq. 3 partial attention of all query rows against the local chunks.
+
+    q [Q, hq, d]; k, v [J*m, hkv, d]. Returns (o_part [Q, hq, d], lse_part fp32 [Q, hq])."""
+    Q, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != v.shape or k.shape[2] != d or q.dtype != k.dtype or k.dtype != v.dtype:
+        raise ValueError("q/k/v shapes or dtypes disagree")
+    if k.shape[0] != chunk_start.numel() * chunk_len:
+        raise ValueError("k/v rows must equal n_chunks * chunk_len")
+    if Q != s.numel() * block_size:
+        raise ValueError("q rows must equal n_blocks * block_size")
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if out is None:
+        out = (torch.empty((Q, hq, d), dtype=o_dtype, device=q.device),
+               torch.empty((Q, hq), dtype=torch.float32, device=q.device))
+    o, lse = out
+    if o.shape != (Q, hq, d) or lse.shape != (Q, hq) or lse.dtype != torch.float32:
+        raise ValueError("output shapes disagree")
+    an, hd, loc = make_anchors(s, a, block_size), make_heads(hq, hkv, d, q.dtype, scale), \
+        make_local(chunk_start, chunk_len)
+    nbytes = splitkv_workspace_bytes(SPLITKV_OP_FWD, an, hd, loc)
+    ws_ptr, ws_bytes = _workspace(nbytes, q.device, workspace)
+    _check("splitkv_attn_fwd", lib().splitkv_attn_fwd(
+        ctypes.byref(an), ctypes.byref(hd), ctypes.byref(loc), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(o), _dtype_code(o.dtype), _ptr(lse), ws_ptr, ws_bytes, _stream(stream)))
+    return o, lse
+
+
+def splitkv_lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
+                      out_dtype: Optional[torch.dtype] = None,
+                      out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                      stream: Optional[torch.cuda.Stream] = None):
+    """Eq. 4 merge. o_parts [P, rows..., d], lse_parts fp32 [P, rows...]."""
+    P = o_parts.shape[0]
+    d = o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    if lse_parts.shape[0] != P or o_parts[0].numel() != rows * d or lse_parts.dtype != torch.float32:
+        raise ValueError("partials disagree")
+    out_dtype = o_parts.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = (torch.empty(o_parts.shape[1:], dtype=out_dtype, device=o_parts.device),
+               torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device))
+    o, lse = out
+    if o.numel() != rows * d or lse.numel() != rows:
+        raise ValueError("output shapes disagree")
+    _check("splitkv_lse_merge", lib().splitkv_lse_merge(
+        int(P), int(rows), int(d), _ptr(o_parts), _dtype_code(o_parts.dtype), _ptr(lse_parts),
+        _ptr(o), _dtype_code(o.dtype), _ptr(lse), _stream(stream)))
+    return o, lse
+
+
+def splitkv_attn_bwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v, o, dout, lse,
+                     dq: torch.Tensor, scale: Optional[float] = None,
+                     delta: Optional[torch.Tensor] = None,
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None):
+    """Backward of the local partial with the global lse (and Delta = <do, o>).
+
+    dq (fp32 [Q, hq, d]) is accumulated in place. Pass o=None and delta=... to
+    supply Delta directly. Returns (dk, dv, delta)."""
+    Q, hq, d = q.shape
+    hkv = k.shape[1]
+    if dout.shape != q.shape or dout.dtype != q.dtype:
+        raise ValueError("dout must match q")
+    if o is not None and (o.shape != q.shape or o.dtype != q.dtype):
+        raise ValueError("o must match q")
+    if lse.shape != (Q, hq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [Q, hq]")
+    if dq.shape != q.shape or dq.dtype != torch.float32:
+        raise ValueError("dq must be fp32 [Q, hq, d]")
+    if k.shape[0] != chunk_start.numel() * chunk_len:
+        raise ValueError("k/v rows must equal n_chunks * chunk_len")
+    if delta is None:
+        if o is None:
+            raise ValueError("need o or delta")
+        delta = torch.empty((Q, hq), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = (torch.empty_like(k), torch.empty_like(v))
+    dk, dv = out
+    an, hd, loc = make_anchors(s, a, block_size), make_heads(hq, hkv, d, q.dtype, scale), \
+        make_local(chunk_start, chunk_len)
+    nbytes = splitkv_workspace_bytes(SPLITKV_OP_BWD, an, hd, loc)
+    ws_ptr, ws_bytes = _workspace(nbytes, q.device, workspace)
+    _check("splitkv_attn_bwd", lib().splitkv_attn_bwd(
+        ctypes.byref(an), ctypes.byref(hd), ctypes.byref(loc), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+        ws_ptr, ws_bytes, _stream(stream)))
+    return dk, dv, delta

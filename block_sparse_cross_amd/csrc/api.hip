@@ -1,0 +1,180 @@
+// C ABI of the Split-KV per-device hot path (declared in include/splitkv.h).
+// Validates every scalar on the host, sizes the workspace, and enqueues the
+// kernels on the caller's stream. Nothing is enqueued when validation fails.
+#include "common.hpp"
+#include "internal.hpp"
+
+using namespace splitkv;
+
+namespace splitkv {
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+FwdWorkspace fwd_workspace_layout(int64_t n_blocks) {
+  FwdWorkspace w;
+  w.block_range = 0;
+  w.total = align256((size_t)n_blocks * sizeof(int2));
+  return w;
+}
+
+BwdWorkspace bwd_workspace_layout(int64_t n_blocks, int32_t block_size, int32_t hq, int32_t hkv) {
+  BwdWorkspace w;
+  w.block_range = 0;
+  w.chunk_range = align256((size_t)n_blocks * sizeof(int2));
+  const int64_t n_vec = n_blocks * block_size * (hq / hkv);
+  w.total = w.chunk_range + align256((size_t)((n_vec + 31) / 32) * sizeof(int2));
+  return w;
+}
+
+}  // namespace splitkv
+
+namespace {
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SPLITKV_OK : SPLITKV_ERR_HIP; }
+
+int check_anchors(const splitkv_anchors* an) {
+  if (an == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if (an->n_blocks < 0 || an->block_size < 1) return SPLITKV_ERR_INVALID_ARG;
+  if (an->n_blocks > 0 && (an->s == nullptr || an->a == nullptr)) return SPLITKV_ERR_INVALID_ARG;
+  return SPLITKV_OK;
+}
+
+int check_heads(const splitkv_heads* hd) {
+  if (hd == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if (hd->hq < 1 || hd->hkv < 1 || hd->d < 1) return SPLITKV_ERR_INVALID_ARG;
+  if (hd->hq % hd->hkv != 0) return SPLITKV_ERR_INVALID_ARG;
+  if (!(hd->scale == hd->scale)) return SPLITKV_ERR_INVALID_ARG;  // NaN
+  if (hd->dtype != SPLITKV_BF16 && hd->dtype != SPLITKV_FP32) return SPLITKV_ERR_UNSUPPORTED;
+  if (hd->d != 64 && hd->d != 128) return SPLITKV_ERR_UNSUPPORTED;
+  return SPLITKV_OK;
+}
+
+int check_local(const splitkv_local* loc) {
+  if (loc == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if (loc->n_chunks < 0 || loc->chunk_len < 1) return SPLITKV_ERR_INVALID_ARG;
+  if (loc->n_chunks > 0 && loc->chunk_start == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if ((int64_t)loc->n_chunks * loc->chunk_len >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  return SPLITKV_OK;
+}
+
+int check_attn_common(const splitkv_anchors* an, const splitkv_heads* hd, const splitkv_local* loc) {
+  int st = check_anchors(an);
+  if (st != SPLITKV_OK) return st;
+  if ((st = check_heads(hd)) != SPLITKV_OK) return st;
+  if ((st = check_local(loc)) != SPLITKV_OK) return st;
+  const int64_t Q = an->n_blocks * (int64_t)an->block_size;
+  if (Q * hd->hq >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  return SPLITKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* splitkv_status_str(int status) {
+  switch (status) {
+    case SPLITKV_OK: return "ok";
+    case SPLITKV_ERR_INVALID_ARG: return "invalid argument";
+    case SPLITKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SPLITKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SPLITKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t splitkv_workspace_bytes(int op, const splitkv_anchors* an, const splitkv_heads* hd,
+                               const splitkv_local* loc) {
+  (void)loc;
+  switch (op) {
+    case SPLITKV_OP_FWD:
+      if (an == nullptr) return 0;
+      return fwd_workspace_layout(an->n_blocks).total;
+    case SPLITKV_OP_BWD:
+      if (an == nullptr || hd == nullptr || hd->hkv < 1) return 0;
+      return bwd_workspace_layout(an->n_blocks, an->block_size, hd->hq, hd->hkv).total;
+    default:
+      return 0;
+  }
+}
+
+int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int32_t J,
+                 int64_t* chunk_cost, int32_t* chunk_owner, int32_t* rank_chunks,
+                 int64_t* rank_load, void* stream) {
+  int st = check_anchors(an);
+  if (st != SPLITKV_OK) return st;
+  if (S < 1 || m < 1 || P < 1 || J < 1) return SPLITKV_ERR_INVALID_ARG;
+  if ((int64_t)P * J * m != S) return SPLITKV_ERR_INVALID_ARG;
+  if (chunk_cost == nullptr || chunk_owner == nullptr || rank_chunks == nullptr ||
+      rank_load == nullptr)
+    return SPLITKV_ERR_INVALID_ARG;
+  if (P > kMaxPlanRanks || (int64_t)P * J > kMaxPlanChunks) return SPLITKV_ERR_UNSUPPORTED;
+  return hip_status(launch_plan(an->s, an->a, an->n_blocks, an->block_size, m, P, J, chunk_cost,
+                                chunk_owner, rank_chunks, rank_load,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int splitkv_attn_fwd(const splitkv_anchors* an, const splitkv_heads* hd,
+                     const splitkv_local* loc, const void* q, const void* k, const void* v,
+                     void* o_part, int o_dtype, float* lse_part, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_attn_common(an, hd, loc);
+  if (st != SPLITKV_OK) return st;
+  if (o_dtype != SPLITKV_BF16 && o_dtype != SPLITKV_FP32) return SPLITKV_ERR_UNSUPPORTED;
+  const int64_t n_keys = (int64_t)loc->n_chunks * loc->chunk_len;
+  if (an->n_blocks == 0) return SPLITKV_OK;
+  if (q == nullptr || o_part == nullptr || lse_part == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if (n_keys > 0 && (k == nullptr || v == nullptr)) return SPLITKV_ERR_INVALID_ARG;
+  const FwdWorkspace ws = fwd_workspace_layout(an->n_blocks);
+  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total))
+    return SPLITKV_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int2* block_range = reinterpret_cast<int2*>(static_cast<char*>(workspace) + ws.block_range);
+  hipError_t e = launch_block_ranges(an->s, an->a, an->n_blocks, loc->chunk_start, loc->n_chunks,
+                                     loc->chunk_len, block_range, s);
+  if (e != hipSuccess) return SPLITKV_ERR_HIP;
+  return hip_status(launch_fwd(*an, *hd, n_keys, block_range, q, k, v, o_part, o_dtype,
+                               lse_part, s));
+}
+
+int splitkv_lse_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts, int in_dtype,
+                      const float* lse_parts, void* o, int out_dtype, float* lse, void* stream) {
+  if (P < 1 || rows < 0 || d < 8 || d % 8 != 0) return SPLITKV_ERR_INVALID_ARG;
+  if ((in_dtype != SPLITKV_BF16 && in_dtype != SPLITKV_FP32) ||
+      (out_dtype != SPLITKV_BF16 && out_dtype != SPLITKV_FP32))
+    return SPLITKV_ERR_UNSUPPORTED;
+  if (rows == 0) return SPLITKV_OK;
+  if (o_parts == nullptr || lse_parts == nullptr || o == nullptr || lse == nullptr)
+    return SPLITKV_ERR_INVALID_ARG;
+  if ((rows * (d / 8) + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  return hip_status(launch_merge(P, rows, d, o_parts, in_dtype, lse_parts, o, out_dtype, lse,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
+                     const splitkv_local* loc, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse, float* delta, float* dq,
+                     void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_attn_common(an, hd, loc);
+  if (st != SPLITKV_OK) return st;
+  const int64_t n_keys = (int64_t)loc->n_chunks * loc->chunk_len;
+  const int64_t Q = an->n_blocks * (int64_t)an->block_size;
+  if (Q > 0 && (q == nullptr || dout == nullptr || lse == nullptr || delta == nullptr ||
+                dq == nullptr))
+    return SPLITKV_ERR_INVALID_ARG;
+  if (n_keys > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return SPLITKV_ERR_INVALID_ARG;
+  const BwdWorkspace ws = bwd_workspace_layout(an->n_blocks, an->block_size, hd->hq, hd->hkv);
+  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total))
+    return SPLITKV_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  int2* block_range = reinterpret_cast<int2*>(base + ws.block_range);
+  int2* chunk_range = reinterpret_cast<int2*>(base + ws.chunk_range);
+  hipError_t e = launch_block_ranges(an->s, an->a, an->n_blocks, loc->chunk_start, loc->n_chunks,
+                                     loc->chunk_len, block_range, s);
+  if (e != hipSuccess) return SPLITKV_ERR_HIP;
+  return hip_status(launch_bwd(*an, *hd, n_keys, block_range, chunk_range, q, k, v, o, dout, lse,
+                               delta, dq, dk, dv, s));
+}
+
+}  // extern "C"

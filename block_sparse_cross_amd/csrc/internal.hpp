@@ -1,0 +1,51 @@
+// Host-side launchers shared between the C-ABI layer and the kernel files.
+// Every launcher assumes its arguments were validated by the caller and
+// returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "splitkv.h"
+
+namespace splitkv {
+
+constexpr int kMaxPlanRanks = 1024;
+constexpr int kMaxPlanChunks = 4096;
+
+// Workspace layout (device bytes), 256-byte aligned segments.
+struct FwdWorkspace {
+  size_t block_range;  // int2 [N]
+  size_t total;
+};
+struct BwdWorkspace {
+  size_t block_range;  // int2 [N]
+  size_t chunk_range;  // int2 [ceil(Q*G / 32)]
+  size_t total;
+};
+FwdWorkspace fwd_workspace_layout(int64_t n_blocks);
+BwdWorkspace bwd_workspace_layout(int64_t n_blocks, int32_t block_size, int32_t hq, int32_t hkv);
+
+hipError_t launch_plan(const int64_t* s, const int64_t* a, int64_t n_blocks, int32_t B,
+                       int64_t m, int32_t P, int32_t J, int64_t* cost, int32_t* owner,
+                       int32_t* rank_chunks, int64_t* rank_load, hipStream_t stream);
+
+hipError_t launch_block_ranges(const int64_t* s, const int64_t* a, int64_t n_blocks,
+                               const int64_t* chunk_start, int32_t n_chunks, int64_t m,
+                               int2* block_range, hipStream_t stream);
+
+hipError_t launch_fwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
+                      const int2* block_range, const void* q, const void* k, const void* v,
+                      void* o, int o_dtype, float* lse, hipStream_t stream);
+
+hipError_t launch_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts, int in_dtype,
+                        const float* lse_parts, void* o, int out_dtype, float* lse,
+                        hipStream_t stream);
+
+hipError_t launch_bwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
+                      const int2* block_range, int2* chunk_range, const void* q, const void* k,
+                      const void* v, const void* o, const void* dout, const float* lse,
+                      float* delta, float* dq, void* dk, void* dv, hipStream_t stream);
+
+}  // namespace splitkv

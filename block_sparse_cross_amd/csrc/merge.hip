@@ -1,0 +1,133 @@
+// Exact LSE merge of P partials (Eq. 4 of "Split-KV: Efficient Context
+// Parallelism for Training Diffusion Drafters", §4.1):
+//   lse = log sum_p exp(lse_p),   o = sum_p exp(lse_p - lse) o_p.
+//
+// Bandwidth-bound: every byte of the P partial outputs is read once. One
+// thread owns 8 consecutive output elements of one row and streams the P
+// partials with 16-byte (bf16) or 2x16-byte (fp32) loads; the d/8 threads of a
+// row are adjacent, so each partial's row segment is read fully coalesced.
+// The lse_p of a row are read by all its threads (cache broadcast).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace splitkv {
+
+namespace {
+
+constexpr int kMergeThreads = 256;
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+  __device__ __forceinline__ static void load(const bf16_t* p, float* x) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store(bf16_t* p, const float* x) {
+    uint4 u;
+    u.x = pack_bf16x2(x[0], x[1]);
+    u.y = pack_bf16x2(x[2], x[3]);
+    u.z = pack_bf16x2(x[4], x[5]);
+    u.w = pack_bf16x2(x[6], x[7]);
+    *reinterpret_cast<uint4*>(p) = u;
+  }
+};
+template <> struct Vec8<float> {
+  __device__ __forceinline__ static void load(const float* p, float* x) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+};
+
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(kMergeThreads)
+lse_merge_kernel(int P, int64_t rows, int d, const Tin* __restrict__ o_parts,
+                 const float* __restrict__ lse_parts, Tout* __restrict__ o,
+                 float* __restrict__ lse) {
+  const int segs = d / 8;
+  const int64_t unit = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (unit >= rows * segs) return;
+  const int64_t row = unit / segs;
+  const int seg = (int)(unit % segs);
+
+  float mx = -INFINITY;
+  for (int p = 0; p < P; ++p) mx = fmaxf(mx, lse_parts[(int64_t)p * rows + row]);
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  Tout* orow = o + row * d + seg * 8;
+  if (mx == -INFINITY) {  // every partial empty
+    Vec8<Tout>::store(orow, acc);
+    if (seg == 0) lse[row] = -INFINITY;
+    return;
+  }
+  // Unnormalised sum with weights exp(lse_p - max); empty partials weigh 0.
+  float wsum = 0.f;
+  const Tin* src = o_parts + row * d + seg * 8;
+  const int64_t pstride = rows * (int64_t)d;
+  int p = 0;
+  for (; p + 4 <= P; p += 4) {
+    float x[4][8], w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      Vec8<Tin>::load(src + (int64_t)(p + u) * pstride, x[u]);
+      w[u] = __expf(lse_parts[(int64_t)(p + u) * rows + row] - mx);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      wsum += w[u];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[u], x[u][e], acc[e]);
+    }
+  }
+  for (; p < P; ++p) {
+    float x[8];
+    Vec8<Tin>::load(src + (int64_t)p * pstride, x);
+    float w = __expf(lse_parts[(int64_t)p * rows + row] - mx);
+    wsum += w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+  }
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  Vec8<Tout>::store(orow, acc);
+  if (seg == 0) lse[row] = mx + __logf(wsum);
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_merge_t(int32_t P, int64_t rows, int32_t d, const void* o_parts,
+                          const float* lse_parts, void* o, float* lse, hipStream_t stream) {
+  const int64_t units = rows * (d / 8);
+  const int64_t grid = (units + kMergeThreads - 1) / kMergeThreads;
+  hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout>), dim3((unsigned)grid), dim3(kMergeThreads),
+                     0, stream, P, rows, d, static_cast<const Tin*>(o_parts), lse_parts,
+                     static_cast<Tout*>(o), lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts, int in_dtype,
+                        const float* lse_parts, void* o, int out_dtype, float* lse,
+                        hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (in_dtype == SPLITKV_BF16 && out_dtype == SPLITKV_BF16)
+    return launch_merge_t<bf16_t, bf16_t>(P, rows, d, o_parts, lse_parts, o, lse, stream);
+  if (in_dtype == SPLITKV_BF16 && out_dtype == SPLITKV_FP32)
+    return launch_merge_t<bf16_t, float>(P, rows, d, o_parts, lse_parts, o, lse, stream);
+  if (in_dtype == SPLITKV_FP32 && out_dtype == SPLITKV_BF16)
+    return launch_merge_t<float, bf16_t>(P, rows, d, o_parts, lse_parts, o, lse, stream);
+  return launch_merge_t<float, float>(P, rows, d, o_parts, lse_parts, o, lse, stream);
+}
+
+}  // namespace splitkv

@@ -1,0 +1,146 @@
+/*
+ * splitkv.h -- C ABI of the Split-KV per-device hot path for MI355X (gfx950).
+ *
+ * Method: "Split-KV: Efficient Context Parallelism for Training Diffusion
+ * Drafters" (arXiv 2611.05926v1). One device (rank p) holds the globally
+ * gathered draft queries q (all N blocks of B rows) and J local context chunks
+ * of m positions each. Block i's rows attend the context window [s_i, a_i) of
+ * their own sample (§3.1, Figure 1), restricted here to the local chunks.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless stated otherwise; the caller owns all
+ *     memory. The library allocates nothing and keeps no state between calls.
+ *   - Scalars and struct fields are validated on the host before anything is
+ *     enqueued; on any error nothing is enqueued and a negative status returns.
+ *     Device-resident contents (anchors, chunk starts) are not validated: the
+ *     kernels stay in bounds for any contents, results are then unspecified.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising. Kernel launch failures return
+ *     SPLITKV_ERR_HIP.
+ *   - Tensors are dense row-major. Query rows are block-major: row r belongs to
+ *     block r / B. Query tensors are [Q, hq, d] with Q = N*B; key/value tensors
+ *     are [J*m, hkv, d], the local chunks in ascending chunk_start order. Query
+ *     head h reads key/value head h / (hq / hkv).
+ *   - LSE values are natural logarithms. A (row, head) with no live key gets
+ *     lse = -inf and o = 0.
+ *   - Supported: d in {64, 128}; hq % hkv == 0; q/k/v dtype bf16 (matrix-core
+ *     path) or fp32; J*m < 2^31; N*B*hq < 2^31.
+ */
+#ifndef SPLITKV_H
+#define SPLITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPLITKV_OK = 0,
+    SPLITKV_ERR_INVALID_ARG = -1, /* a scalar, a size or a required pointer is wrong */
+    SPLITKV_ERR_UNSUPPORTED = -2, /* valid but not implemented (d, dtype, limits)      */
+    SPLITKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required       */
+    SPLITKV_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed        */
+} splitkv_status;
+
+typedef enum { SPLITKV_BF16 = 0, SPLITKV_FP32 = 1 } splitkv_dtype;
+
+typedef enum {
+    SPLITKV_OP_PLAN = 0,
+    SPLITKV_OP_FWD = 1,
+    SPLITKV_OP_BWD = 2,
+    SPLITKV_OP_MERGE = 3
+} splitkv_op;
+
+/* Global anchor metadata A = {(s_i, a_i)} (§4.2: every rank holds it).
+ * s, a: device int64 [n_blocks]; block i's window is [s[i], a[i]). */
+typedef struct {
+    const int64_t* s;
+    const int64_t* a;
+    int64_t n_blocks;    /* N */
+    int32_t block_size;  /* B (16 in the paper's runs) */
+} splitkv_anchors;
+
+/* Head layout (Table 2: n_q, n_kv, d_h) and the input dtype of q, k, v, do. */
+typedef struct {
+    int32_t hq;
+    int32_t hkv;
+    int32_t d;
+    int32_t dtype;       /* splitkv_dtype */
+    float scale;         /* softmax scale of Eq. 3, normally 1/sqrt(d) */
+} splitkv_heads;
+
+/* The rank's local context chunks (§4.2 global chunking: chunk j covers
+ * [lambda_j, lambda_j + m)). chunk_start: device int64 [n_chunks], strictly
+ * ascending with chunk_start[j+1] >= chunk_start[j] + m (a plan's bundle,
+ * times m, satisfies this). */
+typedef struct {
+    const int64_t* chunk_start;
+    int32_t n_chunks;    /* J */
+    int64_t chunk_len;   /* m */
+} splitkv_local;
+
+/* Bytes of device workspace an entry point needs (0 if none). `op` is a
+ * splitkv_op; arguments it does not use may be NULL. */
+size_t splitkv_workspace_bytes(int op, const splitkv_anchors* an, const splitkv_heads* hd,
+                               const splitkv_local* loc);
+
+/* Chunk pricing (Eq. 6) and cost-aware LPT (§4.2).
+ *   cost[j]  = B * sum_i ( min(a_i, j*m + m) - max(s_i, j*m) )^+, j < P*J   (int64)
+ *   Chunks are taken by cost, highest first (equal costs: lower j first); each
+ *   goes to the least-loaded rank holding fewer than J chunks (equal loads:
+ *   lower rank first).
+ * Outputs (device): chunk_cost int64 [P*J], chunk_owner int32 [P*J],
+ *   rank_chunks int32 [P][J] (each rank's chunks ascending), rank_load int64 [P]
+ *   (= C_p, the context work of rank p).
+ * Requires P*J*m == S, P <= 1024, P*J <= 4096. Integer only: the result is
+ * unique and reproducible bit for bit. */
+int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int32_t J,
+                 int64_t* chunk_cost, int32_t* chunk_owner, int32_t* rank_chunks,
+                 int64_t* rank_load, void* stream);
+
+/* Local partial attention, Eq. 3: for every query row r (block i) and head h,
+ * over the local keys whose global position lies in [s_i, a_i):
+ *   lse_p = log sum_x exp(scale <q, k_x>),  o_p = sum_x exp(scale <q, k_x> - lse_p) v_x.
+ * q [Q, hq, d], k, v [J*m, hkv, d] in hd->dtype; o_part [Q, hq, d] in o_dtype
+ * (bf16 or fp32); lse_part fp32 [Q, hq]. Both outputs are fully overwritten.
+ * workspace: splitkv_workspace_bytes(SPLITKV_OP_FWD, ...) bytes. */
+int splitkv_attn_fwd(const splitkv_anchors* an, const splitkv_heads* hd,
+                     const splitkv_local* loc, const void* q, const void* k, const void* v,
+                     void* o_part, int o_dtype, float* lse_part,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Exact merge of P partials, Eq. 4, row by row (rows = Q*hq):
+ *   lse = log sum_p exp(lse_p),  o = sum_p exp(lse_p - lse) o_p.
+ * Partials with lse_p = -inf contribute nothing; a row whose partials are all
+ * empty gets (o = 0, lse = -inf).
+ * o_parts [P][rows][d] in in_dtype, lse_parts fp32 [P][rows]; o [rows][d] in
+ * out_dtype, lse fp32 [rows]. P >= 1. d % 8 == 0. */
+int splitkv_lse_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts, int in_dtype,
+                      const float* lse_parts, void* o, int out_dtype, float* lse, void* stream);
+
+/* Backward of the local partial, Algorithm 1 (MERGE_BWD then AttnBwd_p), with
+ * the GLOBAL (merged) lse and Delta = <do, o>:
+ *   P = exp(scale <q, k_x> - lse[r,h]);  dv_x += P do;  ds = P (<do, v_x> - Delta[r,h]);
+ *   dq_r += scale ds k_x;  dk_x += scale ds q_r   (dk, dv summed over the q heads of a kv head).
+ * o: merged output [Q, hq, d] (hd->dtype). If o != NULL, Delta is computed and
+ *   written to `delta` (fp32 [Q, hq]); if o == NULL, `delta` must hold Delta.
+ * dout [Q, hq, d] (hd->dtype); lse fp32 [Q, hq] (rows with -inf contribute 0).
+ * dq: fp32 [Q, hq, d], ACCUMULATED (+=) so that P emulated ranks sum into one
+ *   buffer (the reduce-scatter of Algorithm 1); the caller zeroes it first.
+ * dk, dv: [J*m, hkv, d] in hd->dtype, overwritten (local to the rank).
+ * workspace: splitkv_workspace_bytes(SPLITKV_OP_BWD, ...) bytes. */
+int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
+                     const splitkv_local* loc, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse, float* delta,
+                     float* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* splitkv_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPLITKV_H */
