@@ -1,0 +1,246 @@
+"""Benchmark of the Split-KV per-device hot path on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic micro-batch:
+  plan (chunk costs + LPT) -> partial attention forward of every emulated rank
+  -> LSE merge of the P partials -> backward of every emulated rank (Delta
+  computed once from the merged output, dq accumulated over ranks).
+The rank-local K/V buffers are materialised once before timing (in the real
+system that is the per-step all-to-all, outside this path).
+
+Prints one JSON line. `value` = mask-live attention FLOPs (forward 4*d*Hq per
+live query-key pair, backward 10*d*Hq) of all ranks per second of step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="weak8")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=600,
+                    help="query rows in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_cross_amd import binding, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    w = inputs.WORKLOADS[args.workload]
+    seed = args.seed
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    # ---------------------------------------------------------------- setup
+    t_setup = time.time()
+    s, a = inputs.workload_anchors(w, seed)
+    sd, ad = to_dev(s), to_dev(a)
+    q = to_dev(inputs.gen_q(w, seed))
+    do = to_dev(inputs.gen_do(w, seed))
+    plan_out = binding.splitkv_plan(sd, ad, w.B, w.S, w.m, w.P, w.J)
+    torch.cuda.synchronize()
+    cost = plan_out[0].cpu().numpy()
+    bundles = plan_out[2].cpu().numpy()
+    load = plan_out[3].cpu().numpy()
+    locs = []
+    for p in range(w.P):
+        ids = bundles[p]
+        k = to_dev(inputs.gen_local_kv(w, seed, ids, "k"))
+        v = to_dev(inputs.gen_local_kv(w, seed, ids, "v"))
+        locs.append((to_dev(ids.astype(np.int64) * w.m), k, v))
+    Q, hq, d = w.Q, w.hq, w.d
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    o_parts = torch.empty((w.P, Q, hq, d), dtype=tdt, device=dev)
+    l_parts = torch.empty((w.P, Q, hq), dtype=torch.float32, device=dev)
+    o = torch.empty((Q, hq, d), dtype=tdt, device=dev)
+    lse = torch.empty((Q, hq), dtype=torch.float32, device=dev)
+    dq = torch.empty((Q, hq, d), dtype=torch.float32, device=dev)
+    delta = torch.empty((Q, hq), dtype=torch.float32, device=dev)
+    dks = [torch.empty_like(k) for _, k, _ in locs]
+    dvs = [torch.empty_like(v) for _, _, v in locs]
+    an = binding.make_anchors(sd, ad, w.B)
+    hd = binding.make_heads(hq, w.hkv, d, tdt)
+    ws_bytes = max(binding.splitkv_workspace_bytes(binding.SPLITKV_OP_FWD, an, hd, None),
+                   binding.splitkv_workspace_bytes(binding.SPLITKV_OP_BWD, an, hd, None))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    n_ev = 5
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record()
+        mark(0)
+        binding.splitkv_plan(sd, ad, w.B, w.S, w.m, w.P, w.J, out=plan_out)
+        mark(1)
+        for p, (cs, k, v) in enumerate(locs):
+            binding.splitkv_attn_fwd(sd, ad, w.B, cs, w.m, q, k, v,
+                                     out=(o_parts[p], l_parts[p]), workspace=ws)
+        mark(2)
+        binding.splitkv_lse_merge(o_parts, l_parts, out=(o, lse))
+        mark(3)
+        dq.zero_()
+        for p, (cs, k, v) in enumerate(locs):
+            binding.splitkv_attn_bwd(sd, ad, w.B, cs, w.m, q, k, v, o if p == 0 else None, do,
+                                     lse, dq, delta=delta, out=(dks[p], dvs[p]), workspace=ws)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[ev() for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    phase = np.zeros(4)
+    for e in events:
+        for j in range(4):
+            phase[j] += e[j].elapsed_time(e[j + 1])
+    phase /= args.steps                      # ms per step: plan, fwd (P calls), merge, bwd (P calls)
+    ms_step = wall * 1e3 / args.steps
+
+    pairs = int(cost.sum())                  # sum over ranks of live (row, key) pairs per head
+    fwd_flops = 4.0 * d * hq * pairs
+    bwd_flops = 10.0 * d * hq * pairs
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    fwd_tflops = fwd_flops / (phase[1] * 1e-3) / 1e12
+    bwd_tflops = bwd_flops / (phase[3] * 1e-3) / 1e12
+    e_in = 2 if tdt == torch.bfloat16 else 4
+    rows = Q * hq
+    merge_bytes = w.P * rows * (d * e_in + 4) + rows * (d * e_in + 4)
+    merge_gbs = merge_bytes / (phase[2] * 1e-3) / 1e9
+    dominant = "bwd" if phase[3] >= phase[1] else "fwd"
+    ach = bwd_tflops if dominant == "bwd" else fwd_tflops
+
+    result = {
+        "metric": "mask-live attn fwd+bwd TFLOP/s (% MFMA peak) + LSE-merge GB/s, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if tdt == torch.bfloat16 else "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: b=%d x L=%d context (S=%d), %d anchors/sample x B=%d (Q=%d), "
+                        "Hq/Hkv/d=%d/%d/%d, m=%d, P=%d ranks x J=%d chunks, all ranks "
+                        "emulated on one GPU" % (w.name, w.b, w.L, w.S, w.A, w.B, Q, hq,
+                                                 w.hkv, d, w.m, w.P, w.J),
+            "step": "plan + fwd(all ranks) + merge + bwd(all ranks)",
+            "live_pairs_per_head": pairs,
+        },
+        "fwd_tflops": round(fwd_tflops, 2),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "fwd_frac_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "bwd_frac_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "merge_gbs": round(merge_gbs, 1),
+        "merge_frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4),
+        "plan_us": round(phase[0] * 1e3, 1),
+        "phase_ms": {"plan": round(phase[0], 4), "fwd_all_ranks": round(phase[1], 4),
+                     "merge": round(phase[2], 4), "bwd_all_ranks": round(phase[3], 4)},
+        "rank_load_max_over_mean": round(float(load.max() / load.mean()), 5),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bwd_bf16_kernel" if dominant == "bwd" else "attn_fwd_bf16_kernel",
+            "achieved": round(ach, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "setup_s": round(setup_s, 1),
+    }
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, seed, s, a, bundles, load, q, locs, args)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, seed, s, a, bundles, load, q, locs, args):
+    """The oracle (fp64 C, OpenMP) timed on this host on a bounded sample of the
+    same workload: Eq. 3 partial attention for a few query rows (all heads)
+    against the max-loaded rank's local keys, FLOPs counted like the GPU's."""
+    import oracle
+    from block_sparse_cross_amd import inputs
+
+    oracle.lib()
+    r = int(np.argmax(load))
+    ids = bundles[r]
+    pos = oracle.local_key_positions(ids, w.m)
+    k = inputs.as_f32(inputs.gen_local_kv(w, seed, ids, "k")).astype(np.float64)
+    v = inputs.as_f32(inputs.gen_local_kv(w, seed, ids, "v")).astype(np.float64)
+    g = np.random.default_rng(seed + 12345)
+    rows = np.sort(g.choice(w.Q, size=min(args.cpu_rows, w.Q), replace=False))
+    qs = inputs.as_f32(inputs.gen_q(w, seed, blocks=rows // w.B)).reshape(
+        len(rows), w.B, w.hq, w.d)[np.arange(len(rows)), rows % w.B].astype(np.float64)
+    blk = rows // w.B
+    live = int(sum(((pos >= s[i]) & (pos < a[i])).sum() for i in blk))  # pairs per head
+    t0 = time.perf_counter()
+    oracle.partial_attn(rows, w.B, s, a, qs, pos, k, v, w.d ** -0.5)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * w.hq * live
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "fp64 partial attention (Eq. 3) of %d query rows x %d heads against "
+                      "rank %d's %d local keys (%d live pairs per head)"
+                      % (len(rows), w.hq, r, len(pos), live)}
+
+
+if __name__ == "__main__":
+    main()
