@@ -1,0 +1,151 @@
+"""Full-size parity on sampled outputs, in the launch configuration bench.py
+times (same binding calls, the plan's critical-path rank r* = argmax load).
+
+For each workload the GPU runs the whole rank share; the oracle recomputes a
+sample of outputs one by one: forward o_p / lse_p for sampled rows (all
+heads), dq for sampled rows, dk / dv for sampled keys (all kv heads), merged
+o / lse for sampled rows against the unsplit attention over the whole context.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_cross_amd import binding, inputs
+from tests.helpers import assert_close_bf16, assert_lse, to_dev, to_f64, vals64
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0
+
+
+class Share:
+    """One workload's r* share on the GPU (+ host copies of what the oracle reads)."""
+
+    def __init__(self, name):
+        w = self.w = inputs.WORKLOADS[name]
+        print("[full] building %s: S=%d Q=%d P=%d J=%d" % (name, w.S, w.Q, w.P, w.J), flush=True)
+        self.s, self.a = inputs.workload_anchors(w, SEED)
+        self.sd, self.ad = to_dev(self.s), to_dev(self.a)
+        cost, owner, bundles, load = [t.cpu().numpy() for t in binding.splitkv_plan(
+            self.sd, self.ad, w.B, w.S, w.m, w.P, w.J)]
+        c_o, ow_o, b_o, l_o = oracle.plan(self.s, self.a, w.B, w.S, w.m, w.P, w.J)
+        assert (cost == c_o).all() and (bundles == b_o).all() and (load == l_o).all()
+        self.bundles, self.load = bundles, load
+        self.r = int(np.argmax(load))
+        self.ids = bundles[self.r]
+        self.pos = oracle.local_key_positions(self.ids, w.m)
+        self.q = inputs.gen_q(w, SEED)
+        self.k = inputs.gen_local_kv(w, SEED, self.ids, "k")
+        self.v = inputs.gen_local_kv(w, SEED, self.ids, "v")
+        self.qd, self.kd, self.vd = to_dev(self.q), to_dev(self.k), to_dev(self.v)
+        self.cs = to_dev(self.ids.astype(np.int64) * w.m)
+        g = np.random.default_rng(99)
+        self.rows = np.unique(np.concatenate([[0, w.Q - 1], g.choice(w.Q, 8, replace=False)]))
+
+    def fwd(self):
+        o, l = binding.splitkv_attn_fwd(self.sd, self.ad, self.w.B, self.cs, self.w.m, self.qd,
+                                        self.kd, self.vd)
+        torch.cuda.synchronize()
+        return o, l
+
+    def oracle_fwd(self, rows):
+        w = self.w
+        return oracle.partial_attn(rows, w.B, self.s, self.a, vals64(self.q[rows]), self.pos,
+                                   vals64(self.k), vals64(self.v), w.d ** -0.5)
+
+
+_cache = {}
+
+
+def share(name):
+    if name not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        _cache[name] = Share(name)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", ["weak8", "strong8", "qs4", "qs32", "weak64"])
+def test_fwd_full_size_sampled_rows(name):
+    sh = share(name)
+    o, l = sh.fwd()
+    o_ref, l_ref = sh.oracle_fwd(sh.rows)
+    assert_lse(to_f64(l)[sh.rows], l_ref)
+    assert_close_bf16(to_f64(o)[sh.rows], o_ref, "%s o_p" % name)
+    # property at any size: lse is -inf exactly where a row has no live local key
+    got_l = to_f64(l)
+    blk = np.arange(sh.w.Q) // sh.w.B
+    lo = np.searchsorted(sh.pos, sh.s[blk], side="left")
+    hi = np.searchsorted(sh.pos, sh.a[blk], side="left")
+    empty = hi <= lo
+    assert (np.isneginf(got_l).all(axis=1) == empty).all()
+    assert np.isfinite(got_l[~empty]).all()
+
+
+@pytest.mark.parametrize("name", ["strong8", "qs32", "weak64"])
+def test_bwd_full_size_sampled(name):
+    sh = share(name)
+    w = sh.w
+    o_syn = inputs.gen_o_like(w, SEED, w.Q)
+    lse_syn = inputs.gen_lse_like(w.Q, w.hq, SEED, center=10.0)
+    do = inputs.gen_do(w, SEED)
+    dq = torch.zeros((w.Q, w.hq, w.d), dtype=torch.float32, device="cuda")
+    dk, dv, delta = binding.splitkv_attn_bwd(sh.sd, sh.ad, w.B, sh.cs, w.m, sh.qd, sh.kd, sh.vd,
+                                             to_dev(o_syn), to_dev(do), to_dev(lse_syn), dq)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    dq_rows = np.unique(np.concatenate([[w.Q - 1], g.choice(w.Q, 2, replace=False)]))
+    # keys: both ends of the buffer, a block's last live key, random ones
+    i = int(g.integers(0, w.N))
+    last_live = int(np.searchsorted(sh.pos, sh.a[i]) - 1)
+    keys = np.unique(np.clip(np.concatenate([[0, len(sh.pos) - 1, last_live, last_live + 1],
+                                             g.choice(len(sh.pos), 10, replace=False)]),
+                             0, len(sh.pos) - 1))
+    dl = oracle.delta(vals64(o_syn), vals64(do))
+    np.testing.assert_allclose(to_f64(delta)[dq_rows], dl[dq_rows], rtol=1e-3, atol=1e-6)
+    dq_ref, dk_ref, dv_ref = oracle.attn_bwd(w.B, sh.s, sh.a, vals64(sh.q), vals64(do),
+                                             lse_syn.astype(np.float64), dl, sh.pos,
+                                             vals64(sh.k), vals64(sh.v), w.d ** -0.5, dq_rows,
+                                             keys)
+    assert_close_bf16(to_f64(dq)[dq_rows], dq_ref, "%s dq" % name)
+    assert_close_bf16(to_f64(dk)[keys], dk_ref, "%s dk" % name)
+    assert_close_bf16(to_f64(dv)[keys], dv_ref, "%s dv" % name)
+
+
+def test_weak8_all_ranks_merge_equals_unsplit():
+    """All 8 emulated ranks of the weak-scaling share, merged on the GPU, equal
+    the oracle's unsplit attention over the whole 128k context (sampled rows)."""
+    sh = share("weak8")
+    w = sh.w
+    parts_o, parts_l = [], []
+    for p in range(w.P):
+        ids = sh.bundles[p]
+        k = to_dev(inputs.gen_local_kv(w, SEED, ids, "k"))
+        v = to_dev(inputs.gen_local_kv(w, SEED, ids, "v"))
+        o, l = binding.splitkv_attn_fwd(sh.sd, sh.ad, w.B, to_dev(ids.astype(np.int64) * w.m),
+                                        w.m, sh.qd, k, v)
+        parts_o.append(o)
+        parts_l.append(l)
+    om, lm = binding.splitkv_lse_merge(torch.stack(parts_o), torch.stack(parts_l))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 17, 40])      # first blocks: the shortest windows
+    kg = inputs.gen_kv_rows(w, SEED, "k", 0, w.S)
+    vg = inputs.gen_kv_rows(w, SEED, "v", 0, w.S)
+    o_ref, l_ref = oracle.partial_attn(rows, w.B, sh.s, sh.a, vals64(sh.q[rows]),
+                                       np.arange(w.S), vals64(kg), vals64(vg), w.d ** -0.5)
+    assert_lse(to_f64(lm)[rows], l_ref)
+    assert_close_bf16(to_f64(om)[rows], o_ref, "merged o")
+
+
+def test_merge_full_size_weak64_shape():
+    """Merge at the P=64 shape (64 partials of 8192 x 32 rows, d=128, bf16)."""
+    P, rows, d = 64, 8192 * 32, 128
+    o_parts, lse_parts = inputs.gen_partials(P, rows, d, seed=64, dtype="bf16")
+    om, lm = binding.splitkv_lse_merge(to_dev(o_parts), to_dev(lse_parts))
+    torch.cuda.synchronize()
+    g = np.random.default_rng(1)
+    sel = np.unique(np.concatenate([[0, 16, rows - 1], g.choice(rows, 200, replace=False)]))
+    o_ref, l_ref = oracle.merge(vals64(o_parts[:, sel]), lse_parts[:, sel].astype(np.float64))
+    assert_lse(to_f64(lm)[sel], l_ref, tol=1e-5)
+    assert_close_bf16(to_f64(om)[sel], o_ref, "merge")
