@@ -43,7 +43,8 @@ int check_heads(const splitkv_heads* hd) {
   if (hd == nullptr) return SPLITKV_ERR_INVALID_ARG;
   if (hd->hq < 1 || hd->hkv < 1 || hd->d < 1) return SPLITKV_ERR_INVALID_ARG;
   if (hd->hq % hd->hkv != 0) return SPLITKV_ERR_INVALID_ARG;
-  if (!(hd->scale == hd->scale)) return SPLITKV_ERR_INVALID_ARG;  // NaN
+  // positive and finite (NaN fails the first test)
+  if (!(hd->scale > 0.f) || hd->scale > 3.0e38f) return SPLITKV_ERR_INVALID_ARG;
   if (hd->dtype != SPLITKV_BF16 && hd->dtype != SPLITKV_FP32) return SPLITKV_ERR_UNSUPPORTED;
   if (hd->d != 64 && hd->d != 128) return SPLITKV_ERR_UNSUPPORTED;
   return SPLITKV_OK;

@@ -10,17 +10,26 @@
 // consecutive vectors of one kv head; each of its 4 waves owns 32 of them.
 // Because the local buffer is sorted by global position, every block reaches
 // one contiguous local key interval [lo, hi); the workgroup walks only the
-// 64-key tiles of the union of its vectors' intervals, and masks per lane.
+// 64-key tiles of the union of its vectors' intervals.
 //
-// Matrix-core layout (v_mfma_f32_32x32x16_bf16, gfx950). Scores are computed
-// transposed, S^T = K Q^T, so that a lane's 16 accumulator values all belong
-// to its own query vector (lane % 32); softmax statistics are per lane, with
-// one exchange between the two half-waves holding the two key halves. The
-// output is also accumulated transposed, O^T = V^T P^T, so the P tile feeds
-// the second product straight from registers and rescaling is per lane. V is
-// staged transposed in LDS ([d][key]) so that both products read 16-byte (or
-// 2x8-byte) fragments. Softmax runs in fp32 in the log2 domain (scale * log2 e
-// folded into one multiply of the fp32 scores); LSE is returned in natural log.
+// Pipeline. K and V tiles are copied global -> LDS with asynchronous 16-byte
+// direct loads (no VGPR staging), double-buffered: the copy of tile t+1 is in
+// flight while tile t is computed, with one barrier per tile. Both tiles stay
+// row-major in LDS with XOR-swizzled 16-byte slots.
+//
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16). Scores are computed
+// transposed, S^T = K Q^T, so a lane's 16 accumulator values all belong to its
+// own query vector (lane % 32) and softmax statistics are per lane, with one
+// exchange between the two half-waves holding the two key halves. The output
+// is accumulated transposed, O^T = V^T P^T: P feeds the product straight from
+// registers, and the V^T fragments come from the row-major V tile through the
+// transposing LDS read (ds_read_b64_tr_b16).
+//
+// Softmax: fp32, log2 domain (scale * log2 e folded into one FMA with the
+// running max); the per-key mask is applied only on tiles that cut some
+// vector's interval; the running max is raised (and O, l rescaled) only when a
+// new score exceeds it by more than 8 (so unnormalised weights stay <= 2^8).
+// LSE is returned in natural log.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -28,15 +37,11 @@ namespace splitkv {
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kFwdThreads = 256;  // 4 waves
 constexpr int kVecPerWave = 32;
 constexpr int kVecPerWG = 128;
 constexpr int kKT = 64;           // keys per tile
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kRescaleSlack = 8.f;
 
 // Per block: local key interval [lo, hi) = [#local keys before s_i, #local
 // keys before a_i). Empty windows give lo == hi.
@@ -56,14 +61,6 @@ __global__ void block_range_kernel(const int64_t* __restrict__ s, const int64_t*
   out[i] = make_int2((int)lo, (int)hi);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
-}
-
 template <typename Tout> struct Store4;
 template <> struct Store4<float> {
   __device__ __forceinline__ static void run(float* p, float a, float b, float c, float d) {
@@ -73,27 +70,50 @@ template <> struct Store4<float> {
 template <> struct Store4<bf16_t> {
   __device__ __forceinline__ static void run(bf16_t* p, float a, float b, float c, float d) {
     u32x2 u;
-    u.x = pack2(a, b);
-    u.y = pack2(c, d);
+    u.x = pack_bf16x2_hw(a, b);
+    u.y = pack_bf16x2_hw(c, d);
     *reinterpret_cast<u32x2*>(p) = u;
   }
 };
 
+// Issue the asynchronous copy of one 64-row tile of k or v (kv head g) into
+// LDS. Row r of the tile is local key k0 + r (clamped to the last key: rows
+// past the end are finite filler that the masks never use). Slot `phys` of a
+// row receives logical slot phys ^ swz(row).
+template <int D, bool kTr>
+__device__ __forceinline__ void issue_tile(const bf16_t* __restrict__ src, int hkv, int g, int k0,
+                                           int n_keys, bf16_t* tile, int tid) {
+  constexpr int NS = D / 8;
+  constexpr int PASSES = kKT * NS / kFwdThreads;
+  const int wave = tid >> 6;
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int u = pass * kFwdThreads + tid;
+    const int row = u / NS, phys = u % NS;
+    const int logical = phys ^ (kTr ? swz_tr<NS>(row) : swz_rows<NS>(row));
+    const int key = min(k0 + row, n_keys - 1);
+    const bf16_t* gp = src + ((int64_t)key * hkv + g) * D + logical * 8;
+    async_copy16(gp, tile + (pass * kFwdThreads + wave * 64) * 8);
+  }
+}
+
 template <int D, typename Tout>
-__global__ void __launch_bounds__(kFwdThreads)
+__global__ void __launch_bounds__(kFwdThreads, 2)
 attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const bf16_t* __restrict__ v, Tout* __restrict__ o, float* __restrict__ lse,
                      const int2* __restrict__ block_range, int64_t n_vec, int G, int hq, int hkv,
                      int B, int n_keys, float scale_log2) {
-  constexpr int KS = D + 8;    // K tile row stride (elements): conflict-free 16-byte reads
-  constexpr int VS = kKT + 4;  // V^T tile row stride: conflict-free 8-byte reads
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kKT * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VS];
+  constexpr int NS = D / 8;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][kKT * D];
   __shared__ int wave_lo[4], wave_hi[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int g = blockIdx.y;
-  const int64_t vec = (int64_t)blockIdx.x * kVecPerWG + wave * kVecPerWave + (lane & 31);
+  // kv head fastest across workgroup ids: consecutive ids land on different
+  // XCDs, so each XCD keeps serving the same kv head's keys from its L2.
+  const int g = blockIdx.x % hkv;
+  const int64_t vgroup = blockIdx.x / hkv;
+  const int64_t vec = vgroup * kVecPerWG + wave * kVecPerWave + (lane & 31);
   const bool valid = vec < n_vec;
   int64_t row = 0;
   int hh = 0, qlo = 0, qhi = 0;
@@ -104,15 +124,18 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     qlo = r.x;
     qhi = r.y;
   }
+  const bool live_lane = valid && qlo < qhi;
   const int64_t head_off = (row * hq + (int64_t)g * G + hh) * D;
 
-  // Key range of this wave and of the workgroup (union of non-empty ranges).
-  int wlo = wave_min_i(qlo < qhi ? qlo : 0x7fffffff);
-  int whi = wave_max_i(qlo < qhi ? qhi : -1);
+  // Key interval union of this wave / workgroup, and the interval every lane
+  // of the wave covers (tiles inside it need no per-key mask).
+  const int wlo = wave_min_i(live_lane ? qlo : 0x7fffffff);
+  const int whi = wave_max_i(live_lane ? qhi : -1);
+  const int wall_lo = wave_max_i(live_lane ? qlo : 0x7fffffff);
+  const int wall_hi = wave_min_i(live_lane ? qhi : -1);
   if (lane == 0) { wave_lo[wave] = wlo; wave_hi[wave] = whi; }
 
-  // Query fragment (B operand of S^T = K Q^T): lane holds d-slices
-  // [16 ks + 8 half, +8) of its own vector.
+  // Query fragment (B operand of S^T = K Q^T): d-slices [16 ks + 8 half, +8).
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -132,104 +155,103 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int k0 = lo; k0 < hi; k0 += kKT) {
-    // ---- stage K (row-major) and V (transposed) tiles in LDS ----
-#pragma unroll
-    for (int c = tid; c < kKT * (D / 8); c += kFwdThreads) {
-      const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int kg = k0 + key;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (kg < n_keys) val = *reinterpret_cast<const u32x4*>(k + ((int64_t)kg * hkv + g) * D + col);
-      *reinterpret_cast<u32x4*>(&Ks[key * KS + col]) = val;
-    }
-#pragma unroll
-    for (int c = tid; c < (kKT / 4) * (D / 8); c += kFwdThreads) {
-      const int col = (c % (D / 8)) * 8, kq = (c / (D / 8)) * 4;
-      u32x4 r[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kg = k0 + kq + u;
-        r[u] = u32x4{0u, 0u, 0u, 0u};
-        if (kg < n_keys) r[u] = *reinterpret_cast<const u32x4*>(v + ((int64_t)kg * hkv + g) * D + col);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, sh = (e & 1) * 16;
-        u32x2 t;
-        t.x = ((r[0][w] >> sh) & 0xffffu) | (((r[1][w] >> sh) & 0xffffu) << 16);
-        t.y = ((r[2][w] >> sh) & 0xffffu) | (((r[3][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(&Vt[(col + e) * VS + kq]) = t;
-      }
-    }
+  if (lo < hi) {
+    issue_tile<D, false>(k, hkv, g, lo, n_keys, Ks[0], tid);
+    issue_tile<D, true>(v, hkv, g, lo, n_keys, Vs[0], tid);
+  }
+  int buf = 0;
+  for (int k0 = lo; k0 < hi; k0 += kKT, buf ^= 1) {
+    wait_async();
     __syncthreads();
+    if (k0 + kKT < hi) {  // prefetch the next tile into the other buffer
+      issue_tile<D, false>(k, hkv, g, k0 + kKT, n_keys, Ks[buf ^ 1], tid);
+      issue_tile<D, true>(v, hkv, g, k0 + kKT, n_keys, Vs[buf ^ 1], tid);
+    }
+    if (!(k0 < whi && k0 + kKT > wlo)) continue;  // nothing live for this wave
+    const bf16_t* Kt = Ks[buf];
+    const bf16_t* Vt = Vs[buf];
 
-    if (k0 < whi && k0 + kKT > wlo) {
-      // ---- S^T = K Q^T for two 32-key halves ----
-      f32x16 sacc[2];
+    // ---- S^T = K Q^T for two 32-key halves ----
+    f32x16 sacc[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+      const int krow = mt * 32 + (lane & 31);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[(mt * 32 + (lane & 31)) * KS + ks * 16 + half * 8]);
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
-        }
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int slot = (2 * ks + half) ^ swz_rows<NS>(krow);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&Kt[krow * D + slot * 8]);
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
       }
-      // ---- mask, online softmax (log2 domain) ----
-      float mloc = -INFINITY;
+    }
+    // ---- mask (boundary tiles only), running max ----
+    const bool need_mask = k0 < wall_lo || k0 + kKT > wall_hi;
+    float mloc = -INFINITY;
+    if (need_mask) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          float x = sacc[mt][r] * scale_log2;
-          x = (key >= qlo && key < qhi) ? x : -INFINITY;
+          const float x = (key >= qlo && key < qhi) ? sacc[mt][r] : -INFINITY;
           sacc[mt][r] = x;
           mloc = fmaxf(mloc, x);
         }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
+    } else {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[mt][r] - m_use);
-          sacc[mt][r] = p;
-          psum += p;
-        }
-      l_run = l_run * alpha + psum;
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mt][r]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
+    // ---- lazy rescale: raise the running max only when exceeded by > 8 ----
+    if (__any(mloc > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-
-      // ---- O^T += V^T P^T, four 16-key steps ----
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          u32x4 pu;
-          pu.x = pack2(sacc[mt][8 * h2 + 0], sacc[mt][8 * h2 + 1]);
-          pu.y = pack2(sacc[mt][8 * h2 + 2], sacc[mt][8 * h2 + 3]);
-          pu.z = pack2(sacc[mt][8 * h2 + 4], sacc[mt][8 * h2 + 5]);
-          pu.w = pack2(sacc[mt][8 * h2 + 6], sacc[mt][8 * h2 + 7]);
-          const bf16x8 pb = as_bf16x8(pu);
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const bf16_t* vr = &Vt[(dt * 32 + (lane & 31)) * VS + mt * 32 + 16 * h2 + 4 * half];
-            const u32x2 x0 = *reinterpret_cast<const u32x2*>(vr);
-            const u32x2 x1 = *reinterpret_cast<const u32x2*>(vr + 8);
-            const u32x4 au = {x0.x, x0.y, x1.x, x1.y};
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(au), pb, oacc[dt], 0, 0, 0);
-          }
-        }
     }
-    __syncthreads();
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sacc[mt][r], scale_log2, neg_m));
+        sacc[mt][r] = p;
+        psum += p;
+      }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T, four 16-key steps ----
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        u32x4 pu;
+        pu.x = pack_bf16x2_hw(sacc[mt][8 * h2 + 0], sacc[mt][8 * h2 + 1]);
+        pu.y = pack_bf16x2_hw(sacc[mt][8 * h2 + 2], sacc[mt][8 * h2 + 3]);
+        pu.z = pack_bf16x2_hw(sacc[mt][8 * h2 + 4], sacc[mt][8 * h2 + 5]);
+        pu.w = pack_bf16x2_hw(sacc[mt][8 * h2 + 6], sacc[mt][8 * h2 + 7]);
+        const bf16x8 pb = as_bf16x8(pu);
+        // keys of this step held by the lane: base + 4 half + {0..3}, +8
+        const int s16 = lane & 15;
+        const int vrow = mt * 32 + 16 * h2 + 4 * half + (s16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+          const int slot = dcol >> 3, off = dcol & 7;
+          const u32x2 x0 = read_tr4(&Vt[vrow * D + ((slot ^ swz_tr<NS>(vrow)) * 8) + off]);
+          const u32x2 x1 = read_tr4(&Vt[(vrow + 8) * D + ((slot ^ swz_tr<NS>(vrow + 8)) * 8) + off]);
+          const u32x4 au = {x0.x, x0.y, x1.x, x1.y};
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(au), pb, oacc[dt], 0, 0, 0);
+        }
+      }
   }
 
   // ---- epilogue: normalise, store o_p and lse_p ----
@@ -296,12 +318,12 @@ hipError_t launch_fwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
   if (hd.dtype == SPLITKV_BF16) {
     const int G = hd.hq / hd.hkv;
     const int64_t n_vec = Q * G;
-    const dim3 grid((unsigned)((n_vec + kVecPerWG - 1) / kVecPerWG), (unsigned)hd.hkv);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, Tout>), grid, dim3(kFwdThreads), 0, stream,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), static_cast<Tout*>(o), lse, block_range,
-                       n_vec, G, hd.hq, hd.hkv, an.block_size, (int)n_keys,
-                       hd.scale * kLog2e);
+    const int64_t n_groups = (n_vec + kVecPerWG - 1) / kVecPerWG;
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, Tout>), dim3((unsigned)(n_groups * hd.hkv)),
+                       dim3(kFwdThreads), 0, stream, static_cast<const bf16_t*>(q),
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                       static_cast<Tout*>(o), lse, block_range, n_vec, G, hd.hq, hd.hkv,
+                       an.block_size, (int)n_keys, hd.scale * kLog2e);
   } else {
     const int64_t n = Q * hd.hq;
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, Tout>), dim3((unsigned)((n + 127) / 128)),

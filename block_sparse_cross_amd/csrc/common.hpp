@@ -62,6 +62,57 @@ __device__ __forceinline__ int wave_max_i(int x) {
   return x;
 }
 
+// ---------------------------------------------------------------------------
+// LDS staging primitives (gfx950).
+//
+// async_copy16: one 16-byte global -> LDS copy per lane that bypasses VGPRs
+// (global_load_lds_dwordx4). The LDS destination of a wave is contiguous:
+// lane l writes bytes [base + 16 l, base + 16 l + 16), with `base` uniform
+// across the wave; each lane picks its own global source. Completion is
+// tracked by vmcnt: wait_async() then a barrier makes the data visible.
+//
+// read_tr4: ds_read_b64_tr_b16. Within each 16-lane group, lane i receives
+// element (i % 4) of the 8-byte words addressed by lanes i/4, i/4 + 4,
+// i/4 + 8 and i/4 + 12 (in that order). If lane s of the group addresses
+// row r0 + s/4, column c0 + 4 (s % 4) of a row-major bf16 tile, lane i gets
+// column c0 + i of rows r0 .. r0 + 3: a transposed 4-element fragment.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void async_copy16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_async() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ u32x2 read_tr4(const bf16_t* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// XOR swizzles of the 16-byte slots of a row-major [row][D] bf16 tile
+// (NS = D / 8 slots per row). Rows read 16 bytes at a time by 32 different
+// rows (row-major MFMA operands) use slot ^ (row mod NS); rows read through
+// read_tr4 (4 consecutive rows x 2 slots per 16-lane group) use
+// slot ^ 4 (row mod 4). Both keep a wave's reads free of bank conflicts for
+// D = 128.
+template <int NS> __device__ __forceinline__ int swz_rows(int row) { return row & (NS - 1); }
+template <int NS> __device__ __forceinline__ int swz_tr(int row) { return (4 * (row & 3)) & (NS - 1); }
+
 // Local (per-rank) key range of one block. The local buffer holds the rank's
 // chunks in ascending global position, so the keys a window [s, a) reaches
 // form one contiguous local interval [lo, hi): lo counts local keys before s,

@@ -68,7 +68,7 @@ typedef struct {
     int32_t hkv;
     int32_t d;
     int32_t dtype;       /* splitkv_dtype */
-    float scale;         /* softmax scale of Eq. 3, normally 1/sqrt(d) */
+    float scale;         /* softmax scale of Eq. 3, normally 1/sqrt(d); finite, > 0 */
 } splitkv_heads;
 
 /* The rank's local context chunks (§4.2 global chunking: chunk j covers
