@@ -20,9 +20,11 @@ FwdWorkspace fwd_workspace_layout(int64_t n_blocks) {
 BwdWorkspace bwd_workspace_layout(int64_t n_blocks, int32_t block_size, int32_t hq, int32_t hkv) {
   BwdWorkspace w;
   w.block_range = 0;
-  w.chunk_range = align256((size_t)n_blocks * sizeof(int2));
+  w.meta = align256((size_t)n_blocks * sizeof(int2));
+  const int64_t n_rh = n_blocks * block_size * hq;
+  w.chunk_range = w.meta + align256((size_t)(n_rh + 1) * sizeof(float4));
   const int64_t n_vec = n_blocks * block_size * (hq / hkv);
-  w.total = w.chunk_range + align256((size_t)((n_vec + 31) / 32) * sizeof(int2));
+  w.total = w.chunk_range + align256((size_t)((n_vec + 31) / 32) * sizeof(int4));
   return w;
 }
 
@@ -170,12 +172,12 @@ int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   int2* block_range = reinterpret_cast<int2*>(base + ws.block_range);
-  int2* chunk_range = reinterpret_cast<int2*>(base + ws.chunk_range);
   hipError_t e = launch_block_ranges(an->s, an->a, an->n_blocks, loc->chunk_start, loc->n_chunks,
                                      loc->chunk_len, block_range, s);
   if (e != hipSuccess) return SPLITKV_ERR_HIP;
-  return hip_status(launch_bwd(*an, *hd, n_keys, block_range, chunk_range, q, k, v, o, dout, lse,
-                               delta, dq, dk, dv, s));
+  return hip_status(launch_bwd(*an, *hd, n_keys, block_range, base + ws.meta,
+                               base + ws.chunk_range, q, k, v, o, dout, lse, delta, dq, dk, dv,
+                               s));
 }
 
 }  // extern "C"

@@ -7,13 +7,24 @@
 // dk and dv stay local to the rank; dq is accumulated (+=) so that the P
 // emulated ranks of one device sum into one buffer.
 //
-// bf16 path: a workgroup owns 128 local keys of one kv head (32 per wave) and
-// walks the 32-vector query chunks whose key intervals reach those keys. Per
-// chunk each wave forms S = Q K^T and dP = dO V^T with v_mfma_f32_32x32x16_bf16
-// so that a lane owns one key and 16 query vectors, then accumulates
-// dV^T += dO^T P and dK^T += Q^T dS in registers (Q^T, dO^T staged transposed
-// in LDS). dS goes through LDS so that dQ = dS K (K^T staged once in LDS) is
-// formed per 32-wide d slice and added to dq with fp32 atomics.
+// bf16 path, three kernels:
+//  1. bwd_prep_kernel: per (row, head) Delta (from o and do, or given) and a
+//     16-byte record {lse * log2 e, Delta, lo, hi} with the row's local key
+//     interval; lse = -inf becomes +inf so that P = exp2(. - inf) = 0.
+//  2. chunk_range_kernel: per 32-vector query chunk, the union of its
+//     intervals and the interval that every vector of the chunk covers.
+//  3. attn_bwd_bf16_kernel: a workgroup owns 128 local keys of one kv head (32
+//     per wave; K and V fragments in registers, K also row-major in LDS) and
+//     walks the query chunks whose union reaches those keys. Q, dO and the
+//     records of the next chunk are copied global -> LDS asynchronously
+//     (double-buffered, row-major, XOR-swizzled) while the current chunk is
+//     computed. Per chunk, with v_mfma_f32_32x32x16_bf16: S = Q K^T and
+//     dP = dO V^T so that a lane owns one key and 16 vectors;
+//     dV^T += dO^T P and dK^T += Q^T dS in registers, the Q^T and dO^T
+//     fragments read by the transposing LDS read; dS^T goes to LDS and
+//     dQ = dS K is formed per 32-wide d slice (both operands through
+//     transposing reads) and added to dq with fp32 atomics. Chunks whose
+//     vectors all cover a wave's 32 keys skip the per-key mask.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -21,25 +32,12 @@ namespace splitkv {
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kBwdThreads = 256;  // 4 waves
 constexpr int kBwdKeys = 128;     // keys per workgroup, 32 per wave
 constexpr int kQC = 32;           // query vectors per chunk
+constexpr int kListCap = 2048;    // chunk indices buffered per scan
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
-}
-__device__ __forceinline__ bf16_t to_bf16(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-
-// Delta[r, h] = <do[r, h], o[r, h]>, one thread per (row, head).
+// Delta[r, h] = <do[r, h], o[r, h]>, one thread per (row, head). fp32 path.
 template <int D, typename T>
 __global__ void __launch_bounds__(256)
 delta_kernel(const T* __restrict__ o, const T* __restrict__ dout, float* __restrict__ delta,
@@ -52,52 +50,100 @@ delta_kernel(const T* __restrict__ o, const T* __restrict__ dout, float* __restr
   delta[t] = acc;
 }
 
-// Key interval of each 32-vector query chunk: union of its rows' block ranges.
+// bf16 path: D/8 lanes per (row, head), 16-byte loads, shuffle reduction.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+                const float* __restrict__ lse, float* __restrict__ delta,
+                const int2* __restrict__ block_range, float4* __restrict__ meta, int64_t n_rh,
+                int hq, int B) {
+  constexpr int L = D / 8;  // lanes per item (8 or 16), a divisor of 64
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t item = gt / L;
+  const int part = (int)(gt % L);
+  const bool ok = item < n_rh;
+  float acc = 0.f;
+  if (ok && o != nullptr) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + item * D + part * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + item * D + part * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
+      acc = fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(b[w] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int off = L / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (!ok || part != 0) return;
+  float dl;
+  if (o != nullptr) {
+    dl = acc;
+    delta[item] = dl;
+  } else {
+    dl = delta[item];
+  }
+  const float l = lse[item];
+  const int2 r = block_range[(item / hq) / B];
+  meta[item] = make_float4(l == -INFINITY ? INFINITY : l * kLog2e, dl, __int_as_float(r.x),
+                           __int_as_float(r.y));
+  // record n_rh: a dead vector (P = 0, empty interval) for chunk padding
+  if (item == 0) meta[n_rh] = make_float4(INFINITY, 0.f, __int_as_float(0), __int_as_float(0));
+}
+
+// Per 32-vector chunk c: {min lo, max hi} over its non-empty vectors (union),
+// {max lo, min hi} over all 32 slots (what every vector covers; vectors past
+// the end count as empty).
 __global__ void chunk_range_kernel(const int2* __restrict__ block_range, int64_t n_vec, int G,
-                                   int B, int64_t n_qc, int2* __restrict__ out) {
+                                   int B, int64_t n_qc, int4* __restrict__ out) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n_qc) return;
-  const int64_t v0 = c * kQC, v1 = min(v0 + kQC, n_vec);
-  int lo = 0x7fffffff, hi = -1;
-  for (int64_t row = v0 / G; row <= (v1 - 1) / G; ++row) {
-    const int2 r = block_range[row / B];
-    if (r.x < r.y) { lo = min(lo, r.x); hi = max(hi, r.y); }
+  int ulo = 0x7fffffff, uhi = -1, clo = -1, chi = 0x7fffffff;
+  for (int t = 0; t < kQC; ++t) {
+    const int64_t vec = c * kQC + t;
+    int2 r = make_int2(0, 0);
+    if (vec < n_vec) r = block_range[(vec / G) / B];
+    if (r.x < r.y) { ulo = min(ulo, r.x); uhi = max(uhi, r.y); }
+    clo = max(clo, r.x);
+    chi = min(chi, r.y);
   }
-  out[c] = hi < 0 ? make_int2(0, 0) : make_int2(lo, hi);
+  out[c] = uhi < 0 ? make_int4(0, 0, 0, 0) : make_int4(ulo, uhi, clo, chi);
 }
 
 template <int D>
-__global__ void __launch_bounds__(kBwdThreads)
+__global__ void __launch_bounds__(kBwdThreads, 1)
 attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                     const float* __restrict__ lse, const float* __restrict__ delta,
-                     float* __restrict__ dq, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
-                     const int2* __restrict__ block_range, const int2* __restrict__ chunk_range,
-                     int64_t n_vec, int64_t n_qc, int G, int hq, int hkv, int B, int n_keys,
-                     float scale, float scale_log2) {
-  constexpr int QS = D + 8;          // [vec][d] tiles
-  constexpr int TS = kQC + 4;        // [d][vec] tiles
-  constexpr int SS = kBwdKeys + 8;   // dS [vec][key]
-  constexpr int KTS = kBwdKeys + 8;  // K^T [d][key]
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[kQC * QS];
-  __shared__ __attribute__((aligned(16))) bf16_t dOs[kQC * QS];
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) bf16_t dOt[D * TS];
-  __shared__ __attribute__((aligned(16))) bf16_t dSs[kQC * SS];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[D * KTS];
-  __shared__ float lse_s[kQC], dlt_s[kQC];
-  __shared__ int lo_s[kQC], hi_s[kQC];
-  __shared__ long long dq_off[kQC];
-  __shared__ int list[kBwdThreads];
+                     const float4* __restrict__ meta, float* __restrict__ dq,
+                     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+                     const int4* __restrict__ chunk_range, int64_t n_vec, int64_t n_qc, int G,
+                     int hq, int hkv, int n_keys, float scale, float scale_log2) {
+  constexpr int NS = D / 8;
+  constexpr int DST = kQC + 4;  // dS^T row stride (elements)
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][kQC * D];
+  __shared__ __attribute__((aligned(16))) bf16_t dOs[2][kQC * D];
+  __shared__ __attribute__((aligned(16))) float4 Ms[2][kQC];
+  __shared__ long long dq_off[2][kQC];
+  __shared__ __attribute__((aligned(16))) bf16_t Kl[kBwdKeys * D];
+  __shared__ __attribute__((aligned(16))) bf16_t dSt[kBwdKeys * DST];
+  __shared__ int list[kListCap];
   __shared__ int wave_cnt[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int g = blockIdx.y;
-  const int k0 = blockIdx.x * kBwdKeys;
+  const int g = blockIdx.x % hkv;  // kv head fastest: one kv head per XCD
+  const int k0 = (blockIdx.x / hkv) * kBwdKeys;
   const int kend = min(k0 + kBwdKeys, n_keys);
   const int kw0 = k0 + wave * 32;
   const int mykey = kw0 + (lane & 31);
 
+  // K row-major in LDS (B operand of dQ), asynchronously.
+#pragma unroll
+  for (int pass = 0; pass < kBwdKeys * NS / kBwdThreads; ++pass) {
+    const int u = pass * kBwdThreads + tid;
+    const int row = u / NS, phys = u % NS;
+    const int key = min(k0 + row, n_keys - 1);
+    async_copy16(k + ((int64_t)key * hkv + g) * D + (phys ^ swz_both<NS>(row)) * 8,
+                 Kl + (pass * kBwdThreads + wave * 64) * 8);
+  }
   // K, V fragments of this wave's 32 keys (B operands: lane = key, 8 d values).
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
@@ -111,25 +157,6 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     kf[ks] = as_bf16x8(a);
     vf[ks] = as_bf16x8(b);
   }
-  // K^T of the workgroup's 128 keys in LDS (B operand of dQ = dS K).
-  for (int c = tid; c < (kBwdKeys / 4) * (D / 8); c += kBwdThreads) {
-    const int col = (c % (D / 8)) * 8, kq = (c / (D / 8)) * 4;
-    u32x4 r[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kg = k0 + kq + u;
-      r[u] = u32x4{0u, 0u, 0u, 0u};
-      if (kg < n_keys) r[u] = *reinterpret_cast<const u32x4*>(k + ((int64_t)kg * hkv + g) * D + col);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      u32x2 t;
-      t.x = ((r[0][w] >> sh) & 0xffffu) | (((r[1][w] >> sh) & 0xffffu) << 16);
-      t.y = ((r[2][w] >> sh) & 0xffffu) | (((r[3][w] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<u32x2*>(&Kt[(col + e) * KTS + kq]) = t;
-    }
-  }
 
   f32x16 dvt[D / 32], dkt[D / 32];
 #pragma unroll
@@ -137,128 +164,116 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dvt[dt][r] = 0.f; dkt[dt][r] = 0.f; }
 
-  for (int64_t base = 0; base < n_qc; base += kBwdThreads) {
-    // ---- collect the query chunks that reach this workgroup's keys ----
-    const int64_t c = base + tid;
-    bool live = false;
-    if (c < n_qc) {
-      const int2 cr = chunk_range[c];
-      live = cr.x < cr.y && cr.x < kend && cr.y > k0;
+  // Stage chunk c (32 vectors) into buffer b: Q, dO rows and records by async
+  // copies; dq row offsets by plain LDS stores.
+  auto issue_chunk = [&](int64_t c, int b) {
+    const int64_t vec0 = c * kQC;
+#pragma unroll
+    for (int pass = 0; pass < 2 * kQC * NS / kBwdThreads; ++pass) {
+      const int u = pass * kBwdThreads + tid;      // over [tensor][row][slot]
+      const int tsel = u / (kQC * NS);
+      const int uu = u % (kQC * NS);
+      const int row = uu / NS, phys = uu % NS;
+      const int64_t vec = min(vec0 + row, n_vec - 1);
+      const int64_t idx = (vec / G) * hq + (int64_t)g * G + vec % G;
+      const bf16_t* src = (tsel ? dout : q) + idx * D + (phys ^ swz_both<NS>(row)) * 8;
+      bf16_t* dst = (tsel ? dOs[b] : Qs[b]) + (uu - lane) * 8;
+      async_copy16(src, dst);
     }
-    const unsigned long long bal = __ballot(live);
-    if (lane == 0) wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) { off += (w < wave) ? wave_cnt[w] : 0; total += wave_cnt[w]; }
-    if (live) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = (int)(c - base);
-    __syncthreads();
+    if (wave == 3 && lane < kQC) {
+      const int64_t vec = vec0 + lane;
+      const int64_t rec = vec < n_vec ? (vec / G) * hq + (int64_t)g * G + vec % G : n_vec * hq / G;
+      async_copy16(meta + rec, &Ms[b][0]);
+    }
+    if (tid < kQC) {
+      const int64_t vec = vec0 + tid;
+      dq_off[b][tid] = vec < n_vec ? ((vec / G) * hq + (int64_t)g * G + vec % G) * D : -1;
+    }
+  };
 
-    for (int it = 0; it < total; ++it) {
-      const int64_t vec0 = (base + list[it]) * kQC;
-      // ---- stage Q, dO (row-major and transposed), lse, Delta, ranges ----
-      {
-        const int tsel = tid / 128;                     // 0: q, 1: do
-        const int t = tid % 128;
-        const int col = (t % (D / 8)) * 8, vq = (t / (D / 8)) * 4;
-        if (vq < kQC) {
-          const bf16_t* src = tsel ? dout : q;
-          bf16_t* nat = tsel ? dOs : Qs;
-          bf16_t* tr = tsel ? dOt : Qt;
-          u32x4 r[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int64_t vec = vec0 + vq + u;
-            r[u] = u32x4{0u, 0u, 0u, 0u};
-            if (vec < n_vec) {
-              const int64_t row = vec / G;
-              const int hh = (int)(vec % G);
-              r[u] = *reinterpret_cast<const u32x4*>(src + (row * hq + (int64_t)g * G + hh) * D + col);
-            }
-            *reinterpret_cast<u32x4*>(&nat[(vq + u) * QS + col]) = r[u];
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1, sh = (e & 1) * 16;
-            u32x2 tt;
-            tt.x = ((r[0][w] >> sh) & 0xffffu) | (((r[1][w] >> sh) & 0xffffu) << 16);
-            tt.y = ((r[2][w] >> sh) & 0xffffu) | (((r[3][w] >> sh) & 0xffffu) << 16);
-            *reinterpret_cast<u32x2*>(&tr[(col + e) * TS + vq]) = tt;
-          }
-        }
-        if (tid < kQC) {
-          const int64_t vec = vec0 + tid;
-          float l2 = -INFINITY, dl = 0.f;
-          int lo = 0, hi = 0;
-          long long doff = -1;
-          if (vec < n_vec) {
-            const int64_t row = vec / G;
-            const int hh = (int)(vec % G);
-            const int64_t idx = row * hq + (int64_t)g * G + hh;
-            const float l = lse[idx];
-            if (l != -INFINITY) {
-              const int2 rg = block_range[row / B];
-              lo = rg.x;
-              hi = rg.y;
-              l2 = l * kLog2e;
-            }
-            dl = delta[idx];
-            doff = idx * D;
-          }
-          lse_s[tid] = l2;
-          dlt_s[tid] = dl;
-          lo_s[tid] = lo;
-          hi_s[tid] = hi;
-          dq_off[tid] = doff;
-        }
+  for (int64_t scan = 0; scan < n_qc;) {
+    // ---- collect (in order) the chunks whose union reaches this workgroup ----
+    int n = 0;
+    while (scan < n_qc && n + kBwdThreads <= kListCap) {
+      const int64_t c = scan + tid;
+      bool live = false;
+      if (c < n_qc) {
+        const int4 cr = chunk_range[c];
+        live = cr.x < cr.y && cr.x < kend && cr.y > k0;
       }
+      const unsigned long long bal = __ballot(live);
+      if (lane == 0) wave_cnt[wave] = __popcll(bal);
       __syncthreads();
-
-      // ---- per wave: S, dP, P, dS; dV^T, dK^T updates; dS to LDS ----
-      int wlo = 0x7fffffff, whi = -1;
+      int off = n, total = 0;
 #pragma unroll
-      for (int t = 0; t < kQC; ++t)
-        if (lo_s[t] < hi_s[t]) { wlo = min(wlo, lo_s[t]); whi = max(whi, hi_s[t]); }
-      const bool active = kw0 < whi && kw0 + 32 > wlo && kw0 < n_keys;
+      for (int w = 0; w < 4; ++w) { off += (w < wave) ? wave_cnt[w] : 0; total += wave_cnt[w]; }
+      if (live) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = (int)c;
+      n += total;
+      scan += kBwdThreads;
+      __syncthreads();
+    }
+    if (n > 0) issue_chunk(list[0], 0);
+
+    for (int it = 0; it < n; ++it) {
+      const int b = it & 1;
+      wait_async();
+      __syncthreads();
+      if (it + 1 < n) issue_chunk(list[it + 1], b ^ 1);
+      const int4 cr = chunk_range[list[it]];
+      const bool active = cr.x < kw0 + 32 && cr.y > kw0;
+      const bool need_mask = !(cr.z <= kw0 && cr.w >= kw0 + 32);
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
       if (active) {
+        const bf16_t* Qb = Qs[b];
+        const bf16_t* Db = dOs[b];
+        // ---- S = Q K^T, dP = dO V^T (lane = key, 16 vectors per lane) ----
+        const int qrow = lane & 31;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const u32x4 aq = *reinterpret_cast<const u32x4*>(&Qs[(lane & 31) * QS + ks * 16 + half * 8]);
-          const u32x4 ad = *reinterpret_cast<const u32x4*>(&dOs[(lane & 31) * QS + ks * 16 + half * 8]);
+          const int slot = (2 * ks + half) ^ swz_both<NS>(qrow);
+          const u32x4 aq = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
+          const u32x4 ad = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), kf[ks], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), vf[ks], pacc, 0, 0, 0);
         }
+        // ---- P = exp2(s c - lse2), dS = P (dP - Delta) ----
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qv = 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool ok = mykey >= lo_s[qv] && mykey < hi_s[qv];
-          const float p = ok ? fast_exp2(sacc[r] * scale_log2 - lse_s[qv]) : 0.f;
-          sacc[r] = p;
-          pacc[r] = p * (pacc[r] - dlt_s[qv]);
-        }
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * jj + i;
+            const float4 mt = Ms[b][8 * jj + 4 * half + i];
+            float p = fast_exp2(fmaf(sacc[r], scale_log2, -mt.x));
+            if (need_mask) {
+              const int lo = __float_as_int(mt.z), hi = __float_as_int(mt.w);
+              p = (mykey >= lo && mykey < hi) ? p : 0.f;
+            }
+            sacc[r] = p;
+            pacc[r] = p * (pacc[r] - mt.y);
+          }
+        // ---- dV^T += dO^T P, dK^T += Q^T dS ----
+        const int s16 = lane & 15;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           u32x4 pu, su;
-          pu.x = pack2(sacc[8 * h2 + 0], sacc[8 * h2 + 1]);
-          pu.y = pack2(sacc[8 * h2 + 2], sacc[8 * h2 + 3]);
-          pu.z = pack2(sacc[8 * h2 + 4], sacc[8 * h2 + 5]);
-          pu.w = pack2(sacc[8 * h2 + 6], sacc[8 * h2 + 7]);
-          su.x = pack2(pacc[8 * h2 + 0], pacc[8 * h2 + 1]);
-          su.y = pack2(pacc[8 * h2 + 2], pacc[8 * h2 + 3]);
-          su.z = pack2(pacc[8 * h2 + 4], pacc[8 * h2 + 5]);
-          su.w = pack2(pacc[8 * h2 + 6], pacc[8 * h2 + 7]);
+          pu.x = pack_bf16x2_hw(sacc[8 * h2 + 0], sacc[8 * h2 + 1]);
+          pu.y = pack_bf16x2_hw(sacc[8 * h2 + 2], sacc[8 * h2 + 3]);
+          pu.z = pack_bf16x2_hw(sacc[8 * h2 + 4], sacc[8 * h2 + 5]);
+          pu.w = pack_bf16x2_hw(sacc[8 * h2 + 6], sacc[8 * h2 + 7]);
+          su.x = pack_bf16x2_hw(pacc[8 * h2 + 0], pacc[8 * h2 + 1]);
+          su.y = pack_bf16x2_hw(pacc[8 * h2 + 2], pacc[8 * h2 + 3]);
+          su.z = pack_bf16x2_hw(pacc[8 * h2 + 4], pacc[8 * h2 + 5]);
+          su.w = pack_bf16x2_hw(pacc[8 * h2 + 6], pacc[8 * h2 + 7]);
+          const int vr = 16 * h2 + 4 * half + (s16 >> 2);
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
-            const int rowd = (dt * 32 + (lane & 31));
-            const bf16_t* dr = &dOt[rowd * TS + 16 * h2 + 4 * half];
-            const bf16_t* qr = &Qt[rowd * TS + 16 * h2 + 4 * half];
-            const u32x2 d0 = *reinterpret_cast<const u32x2*>(dr);
-            const u32x2 d1 = *reinterpret_cast<const u32x2*>(dr + 8);
-            const u32x2 q0 = *reinterpret_cast<const u32x2*>(qr);
-            const u32x2 q1 = *reinterpret_cast<const u32x2*>(qr + 8);
+            const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+            const int o0 = vr * D + (((dcol >> 3) ^ swz_both<NS>(vr)) * 8) + (dcol & 7);
+            const int o1 = (vr + 8) * D + (((dcol >> 3) ^ swz_both<NS>(vr + 8)) * 8) + (dcol & 7);
+            const u32x2 d0 = read_tr4(&Db[o0]), d1 = read_tr4(&Db[o1]);
+            const u32x2 q0 = read_tr4(&Qb[o0]), q1 = read_tr4(&Qb[o1]);
             const u32x4 ad = {d0.x, d0.y, d1.x, d1.y};
             const u32x4 aq = {q0.x, q0.y, q1.x, q1.y};
             dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), as_bf16x8(pu), dvt[dt], 0, 0, 0);
@@ -266,42 +281,54 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           }
         }
       }
-      // dS (bf16) into LDS as [vec][key]; inactive waves write zeros.
+      // dS^T (bf16) into LDS as [key][vec]; inactive waves write zeros.
+      {
+        const int kk = wave * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qv = 8 * (r >> 2) + 4 * half + (r & 3);
-        dSs[qv * SS + wave * 32 + (lane & 31)] = to_bf16(pacc[r]);
+        for (int jj = 0; jj < 4; ++jj) {
+          u32x2 w2;
+          w2.x = pack_bf16x2_hw(pacc[4 * jj], pacc[4 * jj + 1]);
+          w2.y = pack_bf16x2_hw(pacc[4 * jj + 2], pacc[4 * jj + 3]);
+          *reinterpret_cast<u32x2*>(&dSt[kk * DST + 8 * jj + 4 * half]) = w2;
+        }
       }
       __syncthreads();
 
       // ---- dQ = dS K for one 32-wide d slice per wave, atomically added ----
       {
-        constexpr int NDT = D / 32;                  // d slices
-        constexpr int KSPLIT = 4 / NDT;              // waves sharing a slice
+        constexpr int NDT = D / 32;               // d slices
+        constexpr int KSPLIT = 4 / NDT;           // waves sharing a slice
         constexpr int KSTEPS = kBwdKeys / 16 / KSPLIT;
         const int dt = wave % NDT, kpart = wave / NDT;
+        const int s16 = lane & 15;
+        const int qcol = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+        const int dcol = dt * 32 + qcol;
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          const int kb = (kpart * KSTEPS + kk) * 16 + half * 8;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(&dSs[(lane & 31) * SS + kb]);
-          const u32x4 b = *reinterpret_cast<const u32x4*>(&Kt[(dt * 32 + (lane & 31)) * KTS + kb]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
+          const int kr = (kpart * KSTEPS + kk) * 16 + 8 * half + (s16 >> 2);
+          const u32x2 a0 = read_tr4(&dSt[kr * DST + qcol]);
+          const u32x2 a1 = read_tr4(&dSt[(kr + 4) * DST + qcol]);
+          const u32x2 b0 = read_tr4(&Kl[kr * D + (((dcol >> 3) ^ swz_both<NS>(kr)) * 8) + (dcol & 7)]);
+          const u32x2 b1 = read_tr4(&Kl[(kr + 4) * D + (((dcol >> 3) ^ swz_both<NS>(kr + 4)) * 8) + (dcol & 7)]);
+          const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
+          const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bb), acc, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qv = 8 * (r >> 2) + 4 * half + (r & 3);
-          const long long doff = dq_off[qv];
+          const long long doff = dq_off[b][qv];
           if (doff >= 0) atomicAdd(dq + doff + dt * 32 + (lane & 31), acc[r] * scale);
         }
       }
-      __syncthreads();
     }
   }
 
   // ---- write dK = scale * dK^T, dV = dV^T for this wave's keys ----
+  wait_async();  // no copy into this workgroup's LDS may outlive it
   if (mykey < n_keys) {
     bf16_t* dkp = dk + ((int64_t)mykey * hkv + g) * D;
     bf16_t* dvp = dv + ((int64_t)mykey * hkv + g) * D;
@@ -311,10 +338,10 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       for (int jj = 0; jj < 4; ++jj) {
         const int d0 = dt * 32 + 8 * jj + 4 * half;
         u32x2 a, b;
-        a.x = pack2(dkt[dt][4 * jj] * scale, dkt[dt][4 * jj + 1] * scale);
-        a.y = pack2(dkt[dt][4 * jj + 2] * scale, dkt[dt][4 * jj + 3] * scale);
-        b.x = pack2(dvt[dt][4 * jj], dvt[dt][4 * jj + 1]);
-        b.y = pack2(dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
+        a.x = pack_bf16x2_hw(dkt[dt][4 * jj] * scale, dkt[dt][4 * jj + 1] * scale);
+        a.y = pack_bf16x2_hw(dkt[dt][4 * jj + 2] * scale, dkt[dt][4 * jj + 3] * scale);
+        b.x = pack_bf16x2_hw(dvt[dt][4 * jj], dvt[dt][4 * jj + 1]);
+        b.y = pack_bf16x2_hw(dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
         *reinterpret_cast<u32x2*>(dkp + d0) = a;
         *reinterpret_cast<u32x2*>(dvp + d0) = b;
       }
@@ -406,52 +433,53 @@ bwd_dkdv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
 template <int D>
 hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
-                        const int2* block_range, int2* chunk_range, const void* q,
+                        const int2* block_range, void* meta_ws, void* chunk_ws, const void* q,
                         const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, float* delta, float* dq, void* dk, void* dv,
                         hipStream_t stream) {
   const int64_t Q = an.n_blocks * an.block_size;
   const int64_t n_rh = Q * hd.hq;
-  if (o != nullptr && n_rh > 0) {
-    const unsigned grid = (unsigned)((n_rh + 255) / 256);
-    if (hd.dtype == SPLITKV_BF16)
-      hipLaunchKernelGGL((delta_kernel<D, bf16_t>), dim3(grid), dim3(256), 0, stream,
-                         static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), delta,
-                         n_rh);
-    else
-      hipLaunchKernelGGL((delta_kernel<D, float>), dim3(grid), dim3(256), 0, stream,
-                         static_cast<const float*>(o), static_cast<const float*>(dout), delta,
-                         n_rh);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
+  hipError_t err;
   if (hd.dtype == SPLITKV_BF16) {
     const int G = hd.hq / hd.hkv;
     const int64_t n_vec = Q * G;
     const int64_t n_qc = (n_vec + kQC - 1) / kQC;
-    if (n_qc > 0) {
+    float4* meta = static_cast<float4*>(meta_ws);
+    int4* chunk_range = static_cast<int4*>(chunk_ws);
+    if (n_rh > 0) {
+      const int64_t threads = n_rh * (D / 8);
+      hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                         0, stream, static_cast<const bf16_t*>(o),
+                         static_cast<const bf16_t*>(dout), lse, delta, block_range, meta, n_rh,
+                         hd.hq, an.block_size);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
       hipLaunchKernelGGL(chunk_range_kernel, dim3((unsigned)((n_qc + 255) / 256)), dim3(256), 0,
                          stream, block_range, n_vec, G, an.block_size, n_qc, chunk_range);
-      hipError_t err = hipGetLastError();
-      if (err != hipSuccess) return err;
+      if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (n_keys == 0) return hipSuccess;
-    const dim3 grid((unsigned)((n_keys + kBwdKeys - 1) / kBwdKeys), (unsigned)hd.hkv);
-    hipLaunchKernelGGL((attn_bwd_bf16_kernel<D>), grid, dim3(kBwdThreads), 0, stream,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse,
-                       delta, dq, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),
-                       block_range, chunk_range, n_vec, n_qc, G, hd.hq, hd.hkv, an.block_size,
+    const int64_t n_tiles = (n_keys + kBwdKeys - 1) / kBwdKeys;
+    hipLaunchKernelGGL((attn_bwd_bf16_kernel<D>), dim3((unsigned)(n_tiles * hd.hkv)),
+                       dim3(kBwdThreads), 0, stream, static_cast<const bf16_t*>(q),
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                       static_cast<const bf16_t*>(dout), meta, dq, static_cast<bf16_t*>(dk),
+                       static_cast<bf16_t*>(dv), chunk_range, n_vec, n_qc, G, hd.hq, hd.hkv,
                        (int)n_keys, hd.scale, hd.scale * kLog2e);
     return hipGetLastError();
   }
-  if (n_rh > 0)
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), dim3((unsigned)((n_rh + 127) / 128)), dim3(128), 0,
-                     stream, static_cast<const float*>(q), static_cast<const float*>(k),
-                     static_cast<const float*>(v), static_cast<const float*>(dout), lse, delta,
-                     dq, block_range, Q, hd.hq, hd.hkv, an.block_size, hd.scale);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (o != nullptr && n_rh > 0) {
+    hipLaunchKernelGGL((delta_kernel<D, float>), dim3((unsigned)((n_rh + 255) / 256)), dim3(256),
+                       0, stream, static_cast<const float*>(o), static_cast<const float*>(dout),
+                       delta, n_rh);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (n_rh > 0) {
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), dim3((unsigned)((n_rh + 127) / 128)), dim3(128),
+                       0, stream, static_cast<const float*>(q), static_cast<const float*>(k),
+                       static_cast<const float*>(v), static_cast<const float*>(dout), lse, delta,
+                       dq, block_range, Q, hd.hq, hd.hkv, an.block_size, hd.scale);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   const int64_t n_kg = n_keys * hd.hkv;
   if (n_kg == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3((unsigned)((n_kg + 127) / 128)), dim3(128),
@@ -465,14 +493,15 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
 }  // namespace
 
 hipError_t launch_bwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
-                      const int2* block_range, int2* chunk_range, const void* q, const void* k,
-                      const void* v, const void* o, const void* dout, const float* lse,
-                      float* delta, float* dq, void* dk, void* dv, hipStream_t stream) {
+                      const int2* block_range, void* meta, void* chunk_range, const void* q,
+                      const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, float* delta, float* dq, void* dk, void* dv,
+                      hipStream_t stream) {
   if (hd.d == 128)
-    return launch_bwd_t<128>(an, hd, n_keys, block_range, chunk_range, q, k, v, o, dout, lse,
-                             delta, dq, dk, dv, stream);
-  return launch_bwd_t<64>(an, hd, n_keys, block_range, chunk_range, q, k, v, o, dout, lse, delta,
-                          dq, dk, dv, stream);
+    return launch_bwd_t<128>(an, hd, n_keys, block_range, meta, chunk_range, q, k, v, o, dout,
+                             lse, delta, dq, dk, dv, stream);
+  return launch_bwd_t<64>(an, hd, n_keys, block_range, meta, chunk_range, q, k, v, o, dout, lse,
+                          delta, dq, dk, dv, stream);
 }
 
 }  // namespace splitkv

@@ -112,6 +112,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // D = 128.
 template <int NS> __device__ __forceinline__ int swz_rows(int row) { return row & (NS - 1); }
 template <int NS> __device__ __forceinline__ int swz_tr(int row) { return (4 * (row & 3)) & (NS - 1); }
+// One swizzle for tiles read both ways: 16 consecutive rows take 16 distinct
+// values (row-major reads) and 4 consecutive rows take 4 distinct 4-slot
+// blocks (transposing reads).
+template <int NS> __device__ __forceinline__ int swz_both(int row) {
+  return (((row & 3) << 2) | ((row >> 2) & 3)) & (NS - 1);
+}
 
 // Local (per-rank) key range of one block. The local buffer holds the rank's
 // chunks in ascending global position, so the keys a window [s, a) reaches

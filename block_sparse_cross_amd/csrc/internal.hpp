@@ -21,7 +21,8 @@ struct FwdWorkspace {
 };
 struct BwdWorkspace {
   size_t block_range;  // int2 [N]
-  size_t chunk_range;  // int2 [ceil(Q*G / 32)]
+  size_t meta;         // float4 [Q*hq + 1]: lse*log2e, Delta, lo, hi per (row, head)
+  size_t chunk_range;  // int4 [ceil(Q*G / 32)]
   size_t total;
 };
 FwdWorkspace fwd_workspace_layout(int64_t n_blocks);
@@ -44,8 +45,9 @@ hipError_t launch_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts,
                         hipStream_t stream);
 
 hipError_t launch_bwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
-                      const int2* block_range, int2* chunk_range, const void* q, const void* k,
-                      const void* v, const void* o, const void* dout, const float* lse,
-                      float* delta, float* dq, void* dk, void* dv, hipStream_t stream);
+                      const int2* block_range, void* meta, void* chunk_range, const void* q,
+                      const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, float* delta, float* dq, void* dk, void* dv,
+                      hipStream_t stream);
 
 }  // namespace splitkv
