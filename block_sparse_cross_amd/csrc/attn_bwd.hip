@@ -35,7 +35,7 @@ namespace {
 constexpr int kBwdThreads = 256;  // 4 waves
 constexpr int kBwdKeys = 128;     // keys per workgroup, 32 per wave
 constexpr int kQC = 32;           // query vectors per chunk
-constexpr int kListCap = 2048;    // chunk indices buffered per scan
+constexpr int kListCap = 1024;    // chunk indices buffered per scan
 
 // Delta[r, h] = <do[r, h], o[r, h]>, one thread per (row, head). fp32 path.
 template <int D, typename T>
@@ -119,13 +119,21 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      int hq, int hkv, int n_keys, float scale, float scale_log2) {
   constexpr int NS = D / 8;
   constexpr int DST = kQC + 4;  // dS^T row stride (elements)
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][kQC * D];
-  __shared__ __attribute__((aligned(16))) bf16_t dOs[2][kQC * D];
-  __shared__ __attribute__((aligned(16))) float4 Ms[2][kQC];
-  __shared__ long long dq_off[2][kQC];
+  // Double buffers as distinct arrays: the chunk loop is unrolled by two so
+  // the compiler can tell the next chunk's asynchronous LDS writes from the
+  // current chunk's reads (and does not wait for the copies to land).
+  __shared__ __attribute__((aligned(16))) bf16_t Qs0[kQC * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Qs1[kQC * D];
+  __shared__ __attribute__((aligned(16))) bf16_t dOs0[kQC * D];
+  __shared__ __attribute__((aligned(16))) bf16_t dOs1[kQC * D];
+  __shared__ __attribute__((aligned(16))) float4 Ms0[kQC];
+  __shared__ __attribute__((aligned(16))) float4 Ms1[kQC];
+  __shared__ __attribute__((aligned(16))) bf16_t dSt0[kBwdKeys * DST];
+  __shared__ __attribute__((aligned(16))) bf16_t dSt1[kBwdKeys * DST];
+  __shared__ long long dq_off[3][kQC];
   __shared__ __attribute__((aligned(16))) bf16_t Kl[kBwdKeys * D];
-  __shared__ __attribute__((aligned(16))) bf16_t dSt[kBwdKeys * DST];
   __shared__ int list[kListCap];
+  __shared__ int4 lrange[kListCap];
   __shared__ int wave_cnt[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
@@ -134,6 +142,7 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int kend = min(k0 + kBwdKeys, n_keys);
   const int kw0 = k0 + wave * 32;
   const int mykey = kw0 + (lane & 31);
+  const int s16 = lane & 15;
 
   // K row-major in LDS (B operand of dQ), asynchronously.
 #pragma unroll
@@ -164,9 +173,9 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dvt[dt][r] = 0.f; dkt[dt][r] = 0.f; }
 
-  // Stage chunk c (32 vectors) into buffer b: Q, dO rows and records by async
-  // copies; dq row offsets by plain LDS stores.
-  auto issue_chunk = [&](int64_t c, int b) {
+  // Stage chunk c (32 vectors): Q, dO rows and records by asynchronous copies,
+  // dq row offsets by plain LDS stores.
+  auto issue_chunk = [&](int64_t c, bf16_t* Qd, bf16_t* Dd, float4* Md, long long* offd) {
     const int64_t vec0 = c * kQC;
 #pragma unroll
     for (int pass = 0; pass < 2 * kQC * NS / kBwdThreads; ++pass) {
@@ -177,17 +186,115 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const int64_t vec = min(vec0 + row, n_vec - 1);
       const int64_t idx = (vec / G) * hq + (int64_t)g * G + vec % G;
       const bf16_t* src = (tsel ? dout : q) + idx * D + (phys ^ swz_both<NS>(row)) * 8;
-      bf16_t* dst = (tsel ? dOs[b] : Qs[b]) + (uu - lane) * 8;
-      async_copy16(src, dst);
+      async_copy16(src, (tsel ? Dd : Qd) + (uu - lane) * 8);
     }
     if (wave == 3 && lane < kQC) {
       const int64_t vec = vec0 + lane;
       const int64_t rec = vec < n_vec ? (vec / G) * hq + (int64_t)g * G + vec % G : n_vec * hq / G;
-      async_copy16(meta + rec, &Ms[b][0]);
+      async_copy16(meta + rec, Md);
     }
     if (tid < kQC) {
       const int64_t vec = vec0 + tid;
-      dq_off[b][tid] = vec < n_vec ? ((vec / G) * hq + (int64_t)g * G + vec % G) * D : -1;
+      offd[tid] = vec < n_vec ? ((vec / G) * hq + (int64_t)g * G + vec % G) * D : -1;
+    }
+  };
+
+  // dQ = dS K for one 32-wide d slice per wave (both operands through the
+  // transposing read), added to dq with fp32 atomics.
+  auto dq_phase = [&](const bf16_t* dS, const long long* offs) {
+    constexpr int NDT = D / 32;               // d slices
+    constexpr int KSPLIT = 4 / NDT;           // waves sharing a slice
+    constexpr int KSTEPS = kBwdKeys / 16 / KSPLIT;
+    const int dt = wave % NDT, kpart = wave / NDT;
+    const int qcol = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    const int dcol = dt * 32 + qcol;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int kr = (kpart * KSTEPS + kk) * 16 + 8 * half + (s16 >> 2);
+      const u32x2 a0 = read_tr4(&dS[kr * DST + qcol]);
+      const u32x2 a1 = read_tr4(&dS[(kr + 4) * DST + qcol]);
+      const u32x2 b0 = read_tr4(&Kl[kr * D + (((dcol >> 3) ^ swz_both<NS>(kr)) * 8) + (dcol & 7)]);
+      const u32x2 b1 = read_tr4(&Kl[(kr + 4) * D + (((dcol >> 3) ^ swz_both<NS>(kr + 4)) * 8) + (dcol & 7)]);
+      const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
+      const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bb), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const long long doff = offs[8 * (r >> 2) + 4 * half + (r & 3)];
+      if (doff >= 0) atomicAdd(dq + doff + dt * 32 + (lane & 31), acc[r] * scale);
+    }
+  };
+
+  // S = Q K^T and dP = dO V^T (lane = key, 16 vectors per lane), P, dS,
+  // dV^T += dO^T P, dK^T += Q^T dS; dS^T (bf16) into LDS as [key][vec].
+  auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float4* Mb,
+                           bf16_t* dSout) {
+    const bool active = cr.x < kw0 + 32 && cr.y > kw0;
+    const bool need_mask = !(cr.z <= kw0 && cr.w >= kw0 + 32);
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+    if (active) {
+      const int qrow = lane & 31;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int slot = (2 * ks + half) ^ swz_both<NS>(qrow);
+        const u32x4 aq = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
+        const u32x4 ad = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), kf[ks], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), vf[ks], pacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * jj + i;
+          const float4 mt = Mb[8 * jj + 4 * half + i];
+          float p = fast_exp2(fmaf(sacc[r], scale_log2, -mt.x));
+          if (need_mask) {
+            const int lo = __float_as_int(mt.z), hi = __float_as_int(mt.w);
+            p = (mykey >= lo && mykey < hi) ? p : 0.f;
+          }
+          sacc[r] = p;
+          pacc[r] = p * (pacc[r] - mt.y);
+        }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        u32x4 pu, su;
+        pu.x = pack_bf16x2_hw(sacc[8 * h2 + 0], sacc[8 * h2 + 1]);
+        pu.y = pack_bf16x2_hw(sacc[8 * h2 + 2], sacc[8 * h2 + 3]);
+        pu.z = pack_bf16x2_hw(sacc[8 * h2 + 4], sacc[8 * h2 + 5]);
+        pu.w = pack_bf16x2_hw(sacc[8 * h2 + 6], sacc[8 * h2 + 7]);
+        su.x = pack_bf16x2_hw(pacc[8 * h2 + 0], pacc[8 * h2 + 1]);
+        su.y = pack_bf16x2_hw(pacc[8 * h2 + 2], pacc[8 * h2 + 3]);
+        su.z = pack_bf16x2_hw(pacc[8 * h2 + 4], pacc[8 * h2 + 5]);
+        su.w = pack_bf16x2_hw(pacc[8 * h2 + 6], pacc[8 * h2 + 7]);
+        const int vr = 16 * h2 + 4 * half + (s16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+          const int o0 = vr * D + (((dcol >> 3) ^ swz_both<NS>(vr)) * 8) + (dcol & 7);
+          const int o1 = (vr + 8) * D + (((dcol >> 3) ^ swz_both<NS>(vr + 8)) * 8) + (dcol & 7);
+          const u32x2 d0 = read_tr4(&Db[o0]), d1 = read_tr4(&Db[o1]);
+          const u32x2 q0 = read_tr4(&Qb[o0]), q1 = read_tr4(&Qb[o1]);
+          const u32x4 ad = {d0.x, d0.y, d1.x, d1.y};
+          const u32x4 aq = {q0.x, q0.y, q1.x, q1.y};
+          dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), as_bf16x8(pu), dvt[dt], 0, 0, 0);
+          dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), as_bf16x8(su), dkt[dt], 0, 0, 0);
+        }
+      }
+    }
+    const int kk = wave * 32 + (lane & 31);  // inactive waves write zeros
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x2 w2;
+      w2.x = pack_bf16x2_hw(pacc[4 * jj], pacc[4 * jj + 1]);
+      w2.y = pack_bf16x2_hw(pacc[4 * jj + 2], pacc[4 * jj + 3]);
+      *reinterpret_cast<u32x2*>(&dSout[kk * DST + 8 * jj + 4 * half]) = w2;
     }
   };
 
@@ -196,9 +303,10 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     int n = 0;
     while (scan < n_qc && n + kBwdThreads <= kListCap) {
       const int64_t c = scan + tid;
+      int4 cr = make_int4(0, 0, 0, 0);
       bool live = false;
       if (c < n_qc) {
-        const int4 cr = chunk_range[c];
+        cr = chunk_range[c];
         live = cr.x < cr.y && cr.x < kend && cr.y > k0;
       }
       const unsigned long long bal = __ballot(live);
@@ -207,124 +315,37 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       int off = n, total = 0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) { off += (w < wave) ? wave_cnt[w] : 0; total += wave_cnt[w]; }
-      if (live) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = (int)c;
+      if (live) {
+        const int slot = off + __popcll(bal & ((1ull << lane) - 1ull));
+        list[slot] = (int)c;
+        lrange[slot] = cr;
+      }
       n += total;
       scan += kBwdThreads;
       __syncthreads();
     }
-    if (n > 0) issue_chunk(list[0], 0);
 
-    for (int it = 0; it < n; ++it) {
-      const int b = it & 1;
+    // ---- software pipeline over the list: per chunk `it`, one barrier; dQ of
+    // chunk it-1 (its dS^T in the other buffer), copies of chunk it+1, then
+    // the compute of chunk it ----
+    auto step = [&](int it, const bf16_t* Qb, const bf16_t* Db, const float4* Mb, bf16_t* dSb,
+                    const bf16_t* dSprev, bf16_t* Qn, bf16_t* Dn, float4* Mn) {
       wait_async();
       __syncthreads();
-      if (it + 1 < n) issue_chunk(list[it + 1], b ^ 1);
-      const int4 cr = chunk_range[list[it]];
-      const bool active = cr.x < kw0 + 32 && cr.y > kw0;
-      const bool need_mask = !(cr.z <= kw0 && cr.w >= kw0 + 32);
-      f32x16 sacc, pacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
-      if (active) {
-        const bf16_t* Qb = Qs[b];
-        const bf16_t* Db = dOs[b];
-        // ---- S = Q K^T, dP = dO V^T (lane = key, 16 vectors per lane) ----
-        const int qrow = lane & 31;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const int slot = (2 * ks + half) ^ swz_both<NS>(qrow);
-          const u32x4 aq = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
-          const u32x4 ad = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), kf[ks], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), vf[ks], pacc, 0, 0, 0);
-        }
-        // ---- P = exp2(s c - lse2), dS = P (dP - Delta) ----
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * jj + i;
-            const float4 mt = Ms[b][8 * jj + 4 * half + i];
-            float p = fast_exp2(fmaf(sacc[r], scale_log2, -mt.x));
-            if (need_mask) {
-              const int lo = __float_as_int(mt.z), hi = __float_as_int(mt.w);
-              p = (mykey >= lo && mykey < hi) ? p : 0.f;
-            }
-            sacc[r] = p;
-            pacc[r] = p * (pacc[r] - mt.y);
-          }
-        // ---- dV^T += dO^T P, dK^T += Q^T dS ----
-        const int s16 = lane & 15;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          u32x4 pu, su;
-          pu.x = pack_bf16x2_hw(sacc[8 * h2 + 0], sacc[8 * h2 + 1]);
-          pu.y = pack_bf16x2_hw(sacc[8 * h2 + 2], sacc[8 * h2 + 3]);
-          pu.z = pack_bf16x2_hw(sacc[8 * h2 + 4], sacc[8 * h2 + 5]);
-          pu.w = pack_bf16x2_hw(sacc[8 * h2 + 6], sacc[8 * h2 + 7]);
-          su.x = pack_bf16x2_hw(pacc[8 * h2 + 0], pacc[8 * h2 + 1]);
-          su.y = pack_bf16x2_hw(pacc[8 * h2 + 2], pacc[8 * h2 + 3]);
-          su.z = pack_bf16x2_hw(pacc[8 * h2 + 4], pacc[8 * h2 + 5]);
-          su.w = pack_bf16x2_hw(pacc[8 * h2 + 6], pacc[8 * h2 + 7]);
-          const int vr = 16 * h2 + 4 * half + (s16 >> 2);
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-            const int o0 = vr * D + (((dcol >> 3) ^ swz_both<NS>(vr)) * 8) + (dcol & 7);
-            const int o1 = (vr + 8) * D + (((dcol >> 3) ^ swz_both<NS>(vr + 8)) * 8) + (dcol & 7);
-            const u32x2 d0 = read_tr4(&Db[o0]), d1 = read_tr4(&Db[o1]);
-            const u32x2 q0 = read_tr4(&Qb[o0]), q1 = read_tr4(&Qb[o1]);
-            const u32x4 ad = {d0.x, d0.y, d1.x, d1.y};
-            const u32x4 aq = {q0.x, q0.y, q1.x, q1.y};
-            dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), as_bf16x8(pu), dvt[dt], 0, 0, 0);
-            dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), as_bf16x8(su), dkt[dt], 0, 0, 0);
-          }
-        }
-      }
-      // dS^T (bf16) into LDS as [key][vec]; inactive waves write zeros.
-      {
-        const int kk = wave * 32 + (lane & 31);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          u32x2 w2;
-          w2.x = pack_bf16x2_hw(pacc[4 * jj], pacc[4 * jj + 1]);
-          w2.y = pack_bf16x2_hw(pacc[4 * jj + 2], pacc[4 * jj + 3]);
-          *reinterpret_cast<u32x2*>(&dSt[kk * DST + 8 * jj + 4 * half]) = w2;
-        }
-      }
-      __syncthreads();
-
-      // ---- dQ = dS K for one 32-wide d slice per wave, atomically added ----
-      {
-        constexpr int NDT = D / 32;               // d slices
-        constexpr int KSPLIT = 4 / NDT;           // waves sharing a slice
-        constexpr int KSTEPS = kBwdKeys / 16 / KSPLIT;
-        const int dt = wave % NDT, kpart = wave / NDT;
-        const int s16 = lane & 15;
-        const int qcol = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-        const int dcol = dt * 32 + qcol;
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const int kr = (kpart * KSTEPS + kk) * 16 + 8 * half + (s16 >> 2);
-          const u32x2 a0 = read_tr4(&dSt[kr * DST + qcol]);
-          const u32x2 a1 = read_tr4(&dSt[(kr + 4) * DST + qcol]);
-          const u32x2 b0 = read_tr4(&Kl[kr * D + (((dcol >> 3) ^ swz_both<NS>(kr)) * 8) + (dcol & 7)]);
-          const u32x2 b1 = read_tr4(&Kl[(kr + 4) * D + (((dcol >> 3) ^ swz_both<NS>(kr + 4)) * 8) + (dcol & 7)]);
-          const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
-          const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bb), acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qv = 8 * (r >> 2) + 4 * half + (r & 3);
-          const long long doff = dq_off[b][qv];
-          if (doff >= 0) atomicAdd(dq + doff + dt * 32 + (lane & 31), acc[r] * scale);
-        }
-      }
+      if (it > 0) dq_phase(dSprev, dq_off[(it - 1) % 3]);
+      if (it + 1 < n) issue_chunk(list[it + 1], Qn, Dn, Mn, dq_off[(it + 1) % 3]);
+      compute_phase(lrange[it], Qb, Db, Mb, dSb);
+    };
+    if (n > 0) issue_chunk(list[0], Qs0, dOs0, Ms0, dq_off[0]);
+    for (int it = 0; it < n; it += 2) {
+      step(it, Qs0, dOs0, Ms0, dSt0, dSt1, Qs1, dOs1, Ms1);
+      if (it + 1 < n) step(it + 1, Qs1, dOs1, Ms1, dSt1, dSt0, Qs0, dOs0, Ms0);
     }
+    if (n > 0) {
+      __syncthreads();
+      dq_phase((n - 1) & 1 ? dSt1 : dSt0, dq_off[(n - 1) % 3]);
+    }
+    __syncthreads();  // the list and dS^T buffers are reused by the next scan
   }
 
   // ---- write dK = scale * dK^T, dV = dV^T for this wave's keys ----

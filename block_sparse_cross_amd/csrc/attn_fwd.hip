@@ -104,8 +104,11 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const int2* __restrict__ block_range, int64_t n_vec, int G, int hq, int hkv,
                      int B, int n_keys, float scale_log2) {
   constexpr int NS = D / 8;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kKT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][kKT * D];
+  // two buffer pairs, as distinct arrays (see tile_step)
+  __shared__ __attribute__((aligned(16))) bf16_t K0[kKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t V0[kKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t K1[kKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t V1[kKT * D];
   __shared__ int wave_lo[4], wave_hi[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
@@ -155,36 +158,34 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (lo < hi) {
-    issue_tile<D, false>(k, hkv, g, lo, n_keys, Ks[0], tid);
-    issue_tile<D, true>(v, hkv, g, lo, n_keys, Vs[0], tid);
-  }
-  int buf = 0;
-  for (int k0 = lo; k0 < hi; k0 += kKT, buf ^= 1) {
+  // One tile: wait for its copy, start the copy of the next tile into the
+  // other buffer pair, compute. The buffer pairs are distinct LDS arrays and
+  // the loop below is unrolled by two, so the compiler can tell the copy's LDS
+  // writes from this tile's reads and does not wait for the copy to land.
+  auto tile_step = [&](int k0, const bf16_t* Kt, const bf16_t* Vt, bf16_t* Kn, bf16_t* Vn) {
     wait_async();
     __syncthreads();
-    if (k0 + kKT < hi) {  // prefetch the next tile into the other buffer
-      issue_tile<D, false>(k, hkv, g, k0 + kKT, n_keys, Ks[buf ^ 1], tid);
-      issue_tile<D, true>(v, hkv, g, k0 + kKT, n_keys, Vs[buf ^ 1], tid);
+    if (k0 + kKT < hi) {
+      issue_tile<D, false>(k, hkv, g, k0 + kKT, n_keys, Kn, tid);
+      issue_tile<D, true>(v, hkv, g, k0 + kKT, n_keys, Vn, tid);
     }
-    if (!(k0 < whi && k0 + kKT > wlo)) continue;  // nothing live for this wave
-    const bf16_t* Kt = Ks[buf];
-    const bf16_t* Vt = Vs[buf];
+    if (!(k0 < whi && k0 + kKT > wlo)) return;  // nothing live for this wave
 
     // ---- S^T = K Q^T for two 32-key halves ----
     f32x16 sacc[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
-      const int krow = mt * 32 + (lane & 31);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {  // two independent accumulation chains
+        const int krow = mt * 32 + (lane & 31);
         const int slot = (2 * ks + half) ^ swz_rows<NS>(krow);
         const u32x4 a = *reinterpret_cast<const u32x4*>(&Kt[krow * D + slot * 8]);
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
       }
-    }
     // ---- mask (boundary tiles only), running max ----
     const bool need_mask = k0 < wall_lo || k0 + kKT > wall_hi;
     float mloc = -INFINITY;
@@ -252,6 +253,15 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(au), pb, oacc[dt], 0, 0, 0);
         }
       }
+  };
+
+  if (lo < hi) {
+    issue_tile<D, false>(k, hkv, g, lo, n_keys, K0, tid);
+    issue_tile<D, true>(v, hkv, g, lo, n_keys, V0, tid);
+  }
+  for (int k0 = lo; k0 < hi; k0 += 2 * kKT) {
+    tile_step(k0, K0, V0, K1, V1);
+    if (k0 + kKT < hi) tile_step(k0 + kKT, K1, V1, K0, V0);
   }
 
   // ---- epilogue: normalise, store o_p and lse_p ----
