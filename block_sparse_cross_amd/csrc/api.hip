@@ -21,10 +21,11 @@ BwdWorkspace bwd_workspace_layout(int64_t n_blocks, int32_t block_size, int32_t 
   BwdWorkspace w;
   w.block_range = 0;
   w.meta = align256((size_t)n_blocks * sizeof(int2));
-  const int64_t n_rh = n_blocks * block_size * hq;
-  w.chunk_range = w.meta + align256((size_t)(n_rh + 1) * sizeof(float4));
   const int64_t n_vec = n_blocks * block_size * (hq / hkv);
-  w.total = w.chunk_range + align256((size_t)((n_vec + 31) / 32) * sizeof(int4));
+  const int64_t n_qc = (n_vec + 31) / 32;
+  // 4 fp32 fields x 32 vectors per (kv head, query chunk)
+  w.chunk_range = w.meta + align256((size_t)hkv * n_qc * 4 * 32 * sizeof(float));
+  w.total = w.chunk_range + align256((size_t)n_qc * sizeof(int4));
   return w;
 }
 

@@ -13,7 +13,7 @@
 //     interval; lse = -inf becomes +inf so that P = exp2(. - inf) = 0.
 //  2. chunk_range_kernel: per 32-vector query chunk, the union of its
 //     intervals and the interval that every vector of the chunk covers.
-//  3. attn_bwd_bf16_kernel: a workgroup owns 128 local keys of one kv head (32
+//  3. attn_bwd_dkdv_kernel: a workgroup owns 128 local keys of one kv head (32
 //     per wave; K and V fragments in registers, K also row-major in LDS) and
 //     walks the query chunks whose union reaches those keys. Q, dO and the
 //     records of the next chunk are copied global -> LDS asynchronously
@@ -50,20 +50,36 @@ delta_kernel(const T* __restrict__ o, const T* __restrict__ dout, float* __restr
   delta[t] = acc;
 }
 
-// bf16 path: D/8 lanes per (row, head), 16-byte loads, shuffle reduction.
+// bf16 path: one record slot per (kv head g, 32-vector chunk c, t < 32); D/8
+// lanes per slot (16-byte loads, shuffle reduction). The records are laid out
+// as [g][c][field][t] with fields {lse * log2 e, Delta, lo, hi}, so that one
+// 512-byte copy stages a chunk's records as four 32-wide arrays. Slots past
+// the last vector are dead (lse = +inf: P = 0; empty interval).
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
                 const float* __restrict__ lse, float* __restrict__ delta,
-                const int2* __restrict__ block_range, float4* __restrict__ meta, int64_t n_rh,
-                int hq, int B) {
-  constexpr int L = D / 8;  // lanes per item (8 or 16), a divisor of 64
+                const int2* __restrict__ block_range, float* __restrict__ meta, int64_t n_vec,
+                int64_t n_qc, int G, int gshift, int hq, int hkv, int B) {
+  constexpr int L = D / 8;  // lanes per slot (8 or 16), a divisor of 64
   const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t item = gt / L;
+  const int64_t slot = gt / L;
   const int part = (int)(gt % L);
-  const bool ok = item < n_rh;
+  const int64_t n_slots = (int64_t)hkv * n_qc * kQC;
+  const bool ok = slot < n_slots;
+  int64_t item = -1;
+  uint32_t rw = 0;
+  if (ok) {
+    const int64_t gc = slot / kQC;
+    const int g = (int)(gc / n_qc);
+    const uint32_t vec = (uint32_t)((gc % n_qc) * kQC + slot % kQC);
+    if (vec < n_vec) {
+      rw = gshift >= 0 ? vec >> gshift : vec / (uint32_t)G;
+      item = (int64_t)rw * hq + g * G + (vec - rw * G);
+    }
+  }
   float acc = 0.f;
-  if (ok && o != nullptr) {
+  if (item >= 0 && o != nullptr) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(o + item * D + part * 8);
     const u32x4 b = *reinterpret_cast<const u32x4*>(dout + item * D + part * 8);
 #pragma unroll
@@ -75,6 +91,14 @@ bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
 #pragma unroll
   for (int off = L / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (!ok || part != 0) return;
+  float* rec = meta + (slot / kQC) * (4 * kQC) + slot % kQC;
+  if (item < 0) {
+    rec[0] = INFINITY;
+    rec[kQC] = 0.f;
+    rec[2 * kQC] = __int_as_float(0);
+    rec[3 * kQC] = __int_as_float(0);
+    return;
+  }
   float dl;
   if (o != nullptr) {
     dl = acc;
@@ -83,11 +107,11 @@ bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
     dl = delta[item];
   }
   const float l = lse[item];
-  const int2 r = block_range[(item / hq) / B];
-  meta[item] = make_float4(l == -INFINITY ? INFINITY : l * kLog2e, dl, __int_as_float(r.x),
-                           __int_as_float(r.y));
-  // record n_rh: a dead vector (P = 0, empty interval) for chunk padding
-  if (item == 0) meta[n_rh] = make_float4(INFINITY, 0.f, __int_as_float(0), __int_as_float(0));
+  const int2 r = block_range[rw / B];
+  rec[0] = l == -INFINITY ? INFINITY : l * kLog2e;
+  rec[kQC] = dl;
+  rec[2 * kQC] = __int_as_float(r.x);
+  rec[3 * kQC] = __int_as_float(r.y);
 }
 
 // Per 32-vector chunk c: {min lo, max hi} over its non-empty vectors (union),
@@ -111,14 +135,14 @@ __global__ void chunk_range_kernel(const int2* __restrict__ block_range, int64_t
 
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads, 1)
-attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                     const float4* __restrict__ meta, float* __restrict__ dq,
-                     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
-                     const int4* __restrict__ chunk_range, int64_t n_vec, int64_t n_qc, int G,
-                     int hq, int hkv, int n_keys, float scale, float scale_log2) {
+                     const float* __restrict__ meta, bf16_t* __restrict__ dk,
+                     bf16_t* __restrict__ dv, const int4* __restrict__ chunk_range,
+                     int64_t n_vec, int64_t n_qc, int G, int gshift, int hq, int hkv,
+                     int n_keys, float scale, float scale_log2) {
   constexpr int NS = D / 8;
-  constexpr int DST = kQC + 4;  // dS^T row stride (elements)
+  constexpr int NW = kBwdThreads / 64;
   // Double buffers as distinct arrays: the chunk loop is unrolled by two so
   // the compiler can tell the next chunk's asynchronous LDS writes from the
   // current chunk's reads (and does not wait for the copies to land).
@@ -126,34 +150,23 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16_t Qs1[kQC * D];
   __shared__ __attribute__((aligned(16))) bf16_t dOs0[kQC * D];
   __shared__ __attribute__((aligned(16))) bf16_t dOs1[kQC * D];
-  __shared__ __attribute__((aligned(16))) float4 Ms0[kQC];
-  __shared__ __attribute__((aligned(16))) float4 Ms1[kQC];
-  __shared__ __attribute__((aligned(16))) bf16_t dSt0[kBwdKeys * DST];
-  __shared__ __attribute__((aligned(16))) bf16_t dSt1[kBwdKeys * DST];
-  __shared__ long long dq_off[3][kQC];
-  __shared__ __attribute__((aligned(16))) bf16_t Kl[kBwdKeys * D];
+  __shared__ __attribute__((aligned(16))) float Ms0[4 * kQC];
+  __shared__ __attribute__((aligned(16))) float Ms1[4 * kQC];
   __shared__ int list[kListCap];
   __shared__ int4 lrange[kListCap];
-  __shared__ int wave_cnt[4];
+  __shared__ int wave_cnt[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int g = blockIdx.x % hkv;  // kv head fastest: one kv head per XCD
   const int k0 = (blockIdx.x / hkv) * kBwdKeys;
   const int kend = min(k0 + kBwdKeys, n_keys);
   const int kw0 = k0 + wave * 32;
-  const int mykey = kw0 + (lane & 31);
+  const int krow = wave * 32 + (lane & 31);  // this lane's key row in Kl
+  const int mykey = k0 + krow;
   const int s16 = lane & 15;
 
-  // K row-major in LDS (B operand of dQ), asynchronously.
-#pragma unroll
-  for (int pass = 0; pass < kBwdKeys * NS / kBwdThreads; ++pass) {
-    const int u = pass * kBwdThreads + tid;
-    const int row = u / NS, phys = u % NS;
-    const int key = min(k0 + row, n_keys - 1);
-    async_copy16(k + ((int64_t)key * hkv + g) * D + (phys ^ swz_both<NS>(row)) * 8,
-                 Kl + (pass * kBwdThreads + wave * 64) * 8);
-  }
-  // K, V fragments of this wave's 32 keys (B operands: lane = key, 8 d values).
+  // K, V fragments of this wave's 32 keys (B operands of S and dP: lane = key,
+  // 8 d values).
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -173,9 +186,10 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dvt[dt][r] = 0.f; dkt[dt][r] = 0.f; }
 
-  // Stage chunk c (32 vectors): Q, dO rows and records by asynchronous copies,
-  // dq row offsets by plain LDS stores.
-  auto issue_chunk = [&](int64_t c, bf16_t* Qd, bf16_t* Dd, float4* Md, long long* offd) {
+  // Stage chunk c (32 vectors): Q, dO rows and the records by asynchronous
+  // copies. Vectors past the end reuse the last vector's rows (their records
+  // are dead, so they add exact zeros).
+  auto issue_chunk = [&](int64_t c, bf16_t* Qd, bf16_t* Dd, float* Md) {
     const int64_t vec0 = c * kQC;
 #pragma unroll
     for (int pass = 0; pass < 2 * kQC * NS / kBwdThreads; ++pass) {
@@ -183,56 +197,19 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const int tsel = u / (kQC * NS);
       const int uu = u % (kQC * NS);
       const int row = uu / NS, phys = uu % NS;
-      const int64_t vec = min(vec0 + row, n_vec - 1);
-      const int64_t idx = (vec / G) * hq + (int64_t)g * G + vec % G;
+      const uint32_t vec = (uint32_t)min(vec0 + row, n_vec - 1);
+      const uint32_t rw = gshift >= 0 ? vec >> gshift : vec / (uint32_t)G;
+      const int64_t idx = (int64_t)rw * hq + g * G + (vec - rw * G);
       const bf16_t* src = (tsel ? dout : q) + idx * D + (phys ^ swz_both<NS>(row)) * 8;
       async_copy16(src, (tsel ? Dd : Qd) + (uu - lane) * 8);
     }
-    if (wave == 3 && lane < kQC) {
-      const int64_t vec = vec0 + lane;
-      const int64_t rec = vec < n_vec ? (vec / G) * hq + (int64_t)g * G + vec % G : n_vec * hq / G;
-      async_copy16(meta + rec, Md);
-    }
-    if (tid < kQC) {
-      const int64_t vec = vec0 + tid;
-      offd[tid] = vec < n_vec ? ((vec / G) * hq + (int64_t)g * G + vec % G) * D : -1;
-    }
-  };
-
-  // dQ = dS K for one 32-wide d slice per wave (both operands through the
-  // transposing read), added to dq with fp32 atomics.
-  auto dq_phase = [&](const bf16_t* dS, const long long* offs) {
-    constexpr int NDT = D / 32;               // d slices
-    constexpr int KSPLIT = 4 / NDT;           // waves sharing a slice
-    constexpr int KSTEPS = kBwdKeys / 16 / KSPLIT;
-    const int dt = wave % NDT, kpart = wave / NDT;
-    const int qcol = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-    const int dcol = dt * 32 + qcol;
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int kr = (kpart * KSTEPS + kk) * 16 + 8 * half + (s16 >> 2);
-      const u32x2 a0 = read_tr4(&dS[kr * DST + qcol]);
-      const u32x2 a1 = read_tr4(&dS[(kr + 4) * DST + qcol]);
-      const u32x2 b0 = read_tr4(&Kl[kr * D + (((dcol >> 3) ^ swz_both<NS>(kr)) * 8) + (dcol & 7)]);
-      const u32x2 b1 = read_tr4(&Kl[(kr + 4) * D + (((dcol >> 3) ^ swz_both<NS>(kr + 4)) * 8) + (dcol & 7)]);
-      const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
-      const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bb), acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const long long doff = offs[8 * (r >> 2) + 4 * half + (r & 3)];
-      if (doff >= 0) atomicAdd(dq + doff + dt * 32 + (lane & 31), acc[r] * scale);
-    }
+    if (wave == NW - 1 && lane < kQC)
+      async_copy16(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
   };
 
   // S = Q K^T and dP = dO V^T (lane = key, 16 vectors per lane), P, dS,
-  // dV^T += dO^T P, dK^T += Q^T dS; dS^T (bf16) into LDS as [key][vec].
-  auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float4* Mb,
-                           bf16_t* dSout) {
+  // dV^T += dO^T P, dK^T += Q^T dS.
+  auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
     const bool active = cr.x < kw0 + 32 && cr.y > kw0;
     const bool need_mask = !(cr.z <= kw0 && cr.w >= kw0 + 32);
     f32x16 sacc, pacc;
@@ -249,19 +226,29 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), vf[ks], pacc, 0, 0, 0);
       }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 4; ++jj) {
+        const int q0 = 8 * jj + 4 * half;
+        const float4 l2 = *reinterpret_cast<const float4*>(&Mb[q0]);
+        const float4 dl = *reinterpret_cast<const float4*>(&Mb[kQC + q0]);
+        const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
+        const float dla[4] = {dl.x, dl.y, dl.z, dl.w};
+        float pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = fast_exp2(fmaf(sacc[4 * jj + i], scale_log2, -l2a[i]));
+        if (need_mask) {
+          const int4 lo = *reinterpret_cast<const int4*>(&Mb[2 * kQC + q0]);
+          const int4 hi = *reinterpret_cast<const int4*>(&Mb[3 * kQC + q0]);
+          pk[0] = (mykey >= lo.x && mykey < hi.x) ? pk[0] : 0.f;
+          pk[1] = (mykey >= lo.y && mykey < hi.y) ? pk[1] : 0.f;
+          pk[2] = (mykey >= lo.z && mykey < hi.z) ? pk[2] : 0.f;
+          pk[3] = (mykey >= lo.w && mykey < hi.w) ? pk[3] : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 4 * jj + i;
-          const float4 mt = Mb[8 * jj + 4 * half + i];
-          float p = fast_exp2(fmaf(sacc[r], scale_log2, -mt.x));
-          if (need_mask) {
-            const int lo = __float_as_int(mt.z), hi = __float_as_int(mt.w);
-            p = (mykey >= lo && mykey < hi) ? p : 0.f;
-          }
-          sacc[r] = p;
-          pacc[r] = p * (pacc[r] - mt.y);
+          sacc[4 * jj + i] = pk[i];
+          pacc[4 * jj + i] = pk[i] * (pacc[4 * jj + i] - dla[i]);
         }
+      }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         u32x4 pu, su;
@@ -288,14 +275,6 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
       }
     }
-    const int kk = wave * 32 + (lane & 31);  // inactive waves write zeros
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      u32x2 w2;
-      w2.x = pack_bf16x2_hw(pacc[4 * jj], pacc[4 * jj + 1]);
-      w2.y = pack_bf16x2_hw(pacc[4 * jj + 2], pacc[4 * jj + 3]);
-      *reinterpret_cast<u32x2*>(&dSout[kk * DST + 8 * jj + 4 * half]) = w2;
-    }
   };
 
   for (int64_t scan = 0; scan < n_qc;) {
@@ -314,7 +293,7 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       __syncthreads();
       int off = n, total = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) { off += (w < wave) ? wave_cnt[w] : 0; total += wave_cnt[w]; }
+      for (int w = 0; w < NW; ++w) { off += (w < wave) ? wave_cnt[w] : 0; total += wave_cnt[w]; }
       if (live) {
         const int slot = off + __popcll(bal & ((1ull << lane) - 1ull));
         list[slot] = (int)c;
@@ -325,27 +304,25 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       __syncthreads();
     }
 
-    // ---- software pipeline over the list: per chunk `it`, one barrier; dQ of
-    // chunk it-1 (its dS^T in the other buffer), copies of chunk it+1, then
-    // the compute of chunk it ----
-    auto step = [&](int it, const bf16_t* Qb, const bf16_t* Db, const float4* Mb, bf16_t* dSb,
-                    const bf16_t* dSprev, bf16_t* Qn, bf16_t* Dn, float4* Mn) {
+    // ---- software pipeline over the list: per chunk `it`, one barrier, the
+    // copies of chunk it+1, then the compute of chunk it ----
+    // Workgroups start at different points of their lists so that the key
+    // tiles of one kv head do not all read the same query rows at once.
+    const int rot = n > 0 ? (int)((blockIdx.x / hkv) * 97u % (unsigned)n) : 0;
+    auto at = [&](int it) { const int j = it + rot; return j >= n ? j - n : j; };
+    auto step = [&](int it, const bf16_t* Qb, const bf16_t* Db, const float* Mb, bf16_t* Qn,
+                    bf16_t* Dn, float* Mn) {
       wait_async();
       __syncthreads();
-      if (it > 0) dq_phase(dSprev, dq_off[(it - 1) % 3]);
-      if (it + 1 < n) issue_chunk(list[it + 1], Qn, Dn, Mn, dq_off[(it + 1) % 3]);
-      compute_phase(lrange[it], Qb, Db, Mb, dSb);
+      if (it + 1 < n) issue_chunk(list[at(it + 1)], Qn, Dn, Mn);
+      compute_phase(lrange[at(it)], Qb, Db, Mb);
     };
-    if (n > 0) issue_chunk(list[0], Qs0, dOs0, Ms0, dq_off[0]);
+    if (n > 0) issue_chunk(list[at(0)], Qs0, dOs0, Ms0);
     for (int it = 0; it < n; it += 2) {
-      step(it, Qs0, dOs0, Ms0, dSt0, dSt1, Qs1, dOs1, Ms1);
-      if (it + 1 < n) step(it + 1, Qs1, dOs1, Ms1, dSt1, dSt0, Qs0, dOs0, Ms0);
+      step(it, Qs0, dOs0, Ms0, Qs1, dOs1, Ms1);
+      if (it + 1 < n) step(it + 1, Qs1, dOs1, Ms1, Qs0, dOs0, Ms0);
     }
-    if (n > 0) {
-      __syncthreads();
-      dq_phase((n - 1) & 1 ? dSt1 : dSt0, dq_off[(n - 1) % 3]);
-    }
-    __syncthreads();  // the list and dS^T buffers are reused by the next scan
+    __syncthreads();  // the list and the buffers are reused by the next scan
   }
 
   // ---- write dK = scale * dK^T, dV = dV^T for this wave's keys ----
@@ -365,6 +342,166 @@ attn_bwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         b.y = pack_bf16x2_hw(dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
         *reinterpret_cast<u32x2*>(dkp + d0) = a;
         *reinterpret_cast<u32x2*>(dvp + d0) = b;
+      }
+  }
+}
+
+// dQ, query-outer (no atomics): a workgroup takes 128 consecutive query
+// vectors of one kv head (32 per wave, lane % 32 = the lane's vector) and
+// walks the 64-key tiles of their key intervals, like the forward kernel. With
+// the global lse the weights need no running statistics:
+//   S^T = K Q^T, dP^T = V dO^T, dS^T = P (dP - Delta), dQ^T += K^T dS^T,
+// the K^T fragments coming from the row-major K tile through the transposing
+// read. dq += scale * dQ once at the end (each (row, head) has one owner).
+constexpr int kDqThreads = 256;
+constexpr int kDqVecPerWG = 128;
+constexpr int kDqKT = 64;
+
+template <int D>
+__global__ void __launch_bounds__(kDqThreads, 2)
+attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                   const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                   const float* __restrict__ lse, const float* __restrict__ delta,
+                   float* __restrict__ dq, const int2* __restrict__ block_range, int64_t n_vec,
+                   int G, int hq, int hkv, int B, int n_keys, float scale, float scale_log2) {
+  constexpr int NS = D / 8;
+  __shared__ __attribute__((aligned(16))) bf16_t K0[kDqKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t V0[kDqKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t K1[kDqKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t V1[kDqKT * D];
+  __shared__ int wave_lo[4], wave_hi[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int s16 = lane & 15;
+  const int g = blockIdx.x % hkv;
+  const int64_t vec = (int64_t)(blockIdx.x / hkv) * kDqVecPerWG + wave * 32 + (lane & 31);
+  const bool valid = vec < n_vec;
+  int64_t row = 0;
+  int hh = 0, qlo = 0, qhi = 0;
+  float lse2 = INFINITY, dl = 0.f;
+  if (valid) {
+    row = vec / G;
+    hh = (int)(vec % G);
+    const int64_t idx = row * hq + (int64_t)g * G + hh;
+    const float l = lse[idx];
+    if (l != -INFINITY) {
+      const int2 r = block_range[row / B];
+      qlo = r.x;
+      qhi = r.y;
+      lse2 = l * kLog2e;
+    }
+    dl = delta[idx];
+  }
+  const bool live_lane = valid && qlo < qhi;
+  const int64_t head_off = (row * hq + (int64_t)g * G + hh) * D;
+  const int wlo = wave_min_i(live_lane ? qlo : 0x7fffffff);
+  const int whi = wave_max_i(live_lane ? qhi : -1);
+  const int wall_lo = wave_max_i(live_lane ? qlo : 0x7fffffff);
+  const int wall_hi = wave_min_i(live_lane ? qhi : -1);
+  if (lane == 0) { wave_lo[wave] = wlo; wave_hi[wave] = whi; }
+
+  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T).
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (valid) {
+      a = *reinterpret_cast<const u32x4*>(q + head_off + ks * 16 + half * 8);
+      b = *reinterpret_cast<const u32x4*>(dout + head_off + ks * 16 + half * 8);
+    }
+    qf[ks] = as_bf16x8(a);
+    df[ks] = as_bf16x8(b);
+  }
+  __syncthreads();
+  int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) { lo = min(lo, wave_lo[w]); hi = max(hi, wave_hi[w]); }
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.f;
+
+  auto tile_step = [&](int k0, const bf16_t* Kt, const bf16_t* Vt, bf16_t* Kn, bf16_t* Vn) {
+    wait_async();
+    __syncthreads();
+    if (k0 + kDqKT < hi) {
+      issue_rows_async<D, kDqKT, kDqThreads, kSwzBoth>(k, hkv, g, k0 + kDqKT, n_keys, Kn, tid);
+      issue_rows_async<D, kDqKT, kDqThreads, kSwzRows>(v, hkv, g, k0 + kDqKT, n_keys, Vn, tid);
+    }
+    if (!(k0 < whi && k0 + kDqKT > wlo)) return;
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sacc[mt][r] = 0.f; pacc[mt][r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int kr = mt * 32 + (lane & 31);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&Kt[kr * D + (((2 * ks + half) ^ swz_both<NS>(kr)) * 8)]);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&Vt[kr * D + (((2 * ks + half) ^ swz_rows<NS>(kr)) * 8)]);
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
+        pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b), df[ks], pacc[mt], 0, 0, 0);
+      }
+    const bool need_mask = k0 < wall_lo || k0 + kDqKT > wall_hi;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(sacc[mt][r], scale_log2, -lse2));
+        if (need_mask) {
+          const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          p = (key >= qlo && key < qhi) ? p : 0.f;
+        }
+        sacc[mt][r] = p * (pacc[mt][r] - dl);
+      }
+    // dQ^T += K^T dS^T, four 16-key steps
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        u32x4 su;
+        su.x = pack_bf16x2_hw(sacc[mt][8 * h2 + 0], sacc[mt][8 * h2 + 1]);
+        su.y = pack_bf16x2_hw(sacc[mt][8 * h2 + 2], sacc[mt][8 * h2 + 3]);
+        su.z = pack_bf16x2_hw(sacc[mt][8 * h2 + 4], sacc[mt][8 * h2 + 5]);
+        su.w = pack_bf16x2_hw(sacc[mt][8 * h2 + 6], sacc[mt][8 * h2 + 7]);
+        const int kr = mt * 32 + 16 * h2 + 4 * half + (s16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+          const u32x2 x0 = read_tr4(&Kt[kr * D + (((dcol >> 3) ^ swz_both<NS>(kr)) * 8) + (dcol & 7)]);
+          const u32x2 x1 = read_tr4(&Kt[(kr + 8) * D + (((dcol >> 3) ^ swz_both<NS>(kr + 8)) * 8) + (dcol & 7)]);
+          const u32x4 au = {x0.x, x0.y, x1.x, x1.y};
+          dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(au), as_bf16x8(su), dqacc[dt], 0, 0, 0);
+        }
+      }
+  };
+
+  if (lo < hi) {
+    issue_rows_async<D, kDqKT, kDqThreads, kSwzBoth>(k, hkv, g, lo, n_keys, K0, tid);
+    issue_rows_async<D, kDqKT, kDqThreads, kSwzRows>(v, hkv, g, lo, n_keys, V0, tid);
+  }
+  for (int k0 = lo; k0 < hi; k0 += 2 * kDqKT) {
+    tile_step(k0, K0, V0, K1, V1);
+    if (k0 + kDqKT < hi) tile_step(k0 + kDqKT, K1, V1, K0, V0);
+  }
+
+  if (live_lane) {
+    float* dp = dq + head_off;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = dt * 32 + 8 * jj + 4 * half;
+        float4 cur = *reinterpret_cast<float4*>(dp + d0);
+        cur.x = fmaf(dqacc[dt][4 * jj], scale, cur.x);
+        cur.y = fmaf(dqacc[dt][4 * jj + 1], scale, cur.y);
+        cur.z = fmaf(dqacc[dt][4 * jj + 2], scale, cur.z);
+        cur.w = fmaf(dqacc[dt][4 * jj + 3], scale, cur.w);
+        *reinterpret_cast<float4*>(dp + d0) = cur;
       }
   }
 }
@@ -465,14 +602,15 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
     const int G = hd.hq / hd.hkv;
     const int64_t n_vec = Q * G;
     const int64_t n_qc = (n_vec + kQC - 1) / kQC;
-    float4* meta = static_cast<float4*>(meta_ws);
+    float* meta = static_cast<float*>(meta_ws);
+    const int gshift = (G & (G - 1)) == 0 ? __builtin_ctz(G) : -1;
     int4* chunk_range = static_cast<int4*>(chunk_ws);
     if (n_rh > 0) {
-      const int64_t threads = n_rh * (D / 8);
+      const int64_t threads = (int64_t)hd.hkv * n_qc * kQC * (D / 8);
       hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
                          0, stream, static_cast<const bf16_t*>(o),
-                         static_cast<const bf16_t*>(dout), lse, delta, block_range, meta, n_rh,
-                         hd.hq, an.block_size);
+                         static_cast<const bf16_t*>(dout), lse, delta, block_range, meta, n_vec,
+                         n_qc, G, gshift, hd.hq, hd.hkv, an.block_size);
       if ((err = hipGetLastError()) != hipSuccess) return err;
       hipLaunchKernelGGL(chunk_range_kernel, dim3((unsigned)((n_qc + 255) / 256)), dim3(256), 0,
                          stream, block_range, n_vec, G, an.block_size, n_qc, chunk_range);
@@ -480,12 +618,20 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
     }
     if (n_keys == 0) return hipSuccess;
     const int64_t n_tiles = (n_keys + kBwdKeys - 1) / kBwdKeys;
-    hipLaunchKernelGGL((attn_bwd_bf16_kernel<D>), dim3((unsigned)(n_tiles * hd.hkv)),
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)(n_tiles * hd.hkv)),
                        dim3(kBwdThreads), 0, stream, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-                       static_cast<const bf16_t*>(dout), meta, dq, static_cast<bf16_t*>(dk),
-                       static_cast<bf16_t*>(dv), chunk_range, n_vec, n_qc, G, hd.hq, hd.hkv,
-                       (int)n_keys, hd.scale, hd.scale * kLog2e);
+                       static_cast<const bf16_t*>(dout), meta, static_cast<bf16_t*>(dk),
+                       static_cast<bf16_t*>(dv), chunk_range, n_vec, n_qc, G, gshift, hd.hq,
+                       hd.hkv, (int)n_keys, hd.scale, hd.scale * kLog2e);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (n_rh == 0) return hipSuccess;
+    const int64_t n_groups = (n_vec + kDqVecPerWG - 1) / kDqVecPerWG;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((unsigned)(n_groups * hd.hkv)),
+                       dim3(kDqThreads), 0, stream, static_cast<const bf16_t*>(q),
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                       static_cast<const bf16_t*>(dout), lse, delta, dq, block_range, n_vec, G,
+                       hd.hq, hd.hkv, an.block_size, (int)n_keys, hd.scale, hd.scale * kLog2e);
     return hipGetLastError();
   }
   if (o != nullptr && n_rh > 0) {

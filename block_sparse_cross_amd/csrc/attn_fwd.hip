@@ -76,27 +76,6 @@ template <> struct Store4<bf16_t> {
   }
 };
 
-// Issue the asynchronous copy of one 64-row tile of k or v (kv head g) into
-// LDS. Row r of the tile is local key k0 + r (clamped to the last key: rows
-// past the end are finite filler that the masks never use). Slot `phys` of a
-// row receives logical slot phys ^ swz(row).
-template <int D, bool kTr>
-__device__ __forceinline__ void issue_tile(const bf16_t* __restrict__ src, int hkv, int g, int k0,
-                                           int n_keys, bf16_t* tile, int tid) {
-  constexpr int NS = D / 8;
-  constexpr int PASSES = kKT * NS / kFwdThreads;
-  const int wave = tid >> 6;
-#pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
-    const int u = pass * kFwdThreads + tid;
-    const int row = u / NS, phys = u % NS;
-    const int logical = phys ^ (kTr ? swz_tr<NS>(row) : swz_rows<NS>(row));
-    const int key = min(k0 + row, n_keys - 1);
-    const bf16_t* gp = src + ((int64_t)key * hkv + g) * D + logical * 8;
-    async_copy16(gp, tile + (pass * kFwdThreads + wave * 64) * 8);
-  }
-}
-
 template <int D, typename Tout>
 __global__ void __launch_bounds__(kFwdThreads, 2)
 attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -166,8 +145,8 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     wait_async();
     __syncthreads();
     if (k0 + kKT < hi) {
-      issue_tile<D, false>(k, hkv, g, k0 + kKT, n_keys, Kn, tid);
-      issue_tile<D, true>(v, hkv, g, k0 + kKT, n_keys, Vn, tid);
+      issue_rows_async<D, kKT, kFwdThreads, kSwzRows>(k, hkv, g, k0 + kKT, n_keys, Kn, tid);
+      issue_rows_async<D, kKT, kFwdThreads, kSwzTr>(v, hkv, g, k0 + kKT, n_keys, Vn, tid);
     }
     if (!(k0 < whi && k0 + kKT > wlo)) return;  // nothing live for this wave
 
@@ -256,8 +235,8 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   };
 
   if (lo < hi) {
-    issue_tile<D, false>(k, hkv, g, lo, n_keys, K0, tid);
-    issue_tile<D, true>(v, hkv, g, lo, n_keys, V0, tid);
+    issue_rows_async<D, kKT, kFwdThreads, kSwzRows>(k, hkv, g, lo, n_keys, K0, tid);
+    issue_rows_async<D, kKT, kFwdThreads, kSwzTr>(v, hkv, g, lo, n_keys, V0, tid);
   }
   for (int k0 = lo; k0 < hi; k0 += 2 * kKT) {
     tile_step(k0, K0, V0, K1, V1);

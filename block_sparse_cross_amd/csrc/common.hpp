@@ -119,6 +119,32 @@ template <int NS> __device__ __forceinline__ int swz_both(int row) {
   return (((row & 3) << 2) | ((row >> 2) & 3)) & (NS - 1);
 }
 
+enum SwzKind { kSwzRows = 0, kSwzTr = 1, kSwzBoth = 2 };
+template <int NS, int KIND> __device__ __forceinline__ int swz(int row) {
+  return KIND == kSwzRows ? swz_rows<NS>(row) : (KIND == kSwzTr ? swz_tr<NS>(row) : swz_both<NS>(row));
+}
+
+// Asynchronous copy of ROWS consecutive local key rows k0 .. k0 + ROWS - 1 of
+// kv head g (D bf16 each; rows past the end repeat the last key: finite
+// filler that the masks never use) into a row-major LDS tile whose 16-byte
+// slots are permuted by the swizzle KIND. All THREADS threads take part.
+template <int D, int ROWS, int THREADS, int KIND>
+__device__ __forceinline__ void issue_rows_async(const bf16_t* __restrict__ src, int hkv, int g,
+                                                 int k0, int n_keys, bf16_t* tile, int tid) {
+  constexpr int NS = D / 8;
+  constexpr int PASSES = ROWS * NS / THREADS;
+  static_assert(PASSES * THREADS == ROWS * NS, "tile must split evenly over the threads");
+  const int wave = tid >> 6;
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int u = pass * THREADS + tid;
+    const int row = u / NS, phys = u % NS;
+    const int key = min(k0 + row, n_keys - 1);
+    async_copy16(src + ((int64_t)key * hkv + g) * D + (phys ^ swz<NS, KIND>(row)) * 8,
+                 tile + (pass * THREADS + wave * 64) * 8);
+  }
+}
+
 // Local (per-rank) key range of one block. The local buffer holds the rank's
 // chunks in ascending global position, so the keys a window [s, a) reaches
 // form one contiguous local interval [lo, hi): lo counts local keys before s,

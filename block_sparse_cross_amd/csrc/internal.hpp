@@ -21,8 +21,8 @@ struct FwdWorkspace {
 };
 struct BwdWorkspace {
   size_t block_range;  // int2 [N]
-  size_t meta;         // float4 [Q*hq + 1]: lse*log2e, Delta, lo, hi per (row, head)
-  size_t chunk_range;  // int4 [ceil(Q*G / 32)]
+  size_t meta;         // fp32 [hkv][n_qc][4][32]: lse*log2e, Delta, lo, hi per vector
+  size_t chunk_range;  // int4 [n_qc], n_qc = ceil(Q*G / 32)
   size_t total;
 };
 FwdWorkspace fwd_workspace_layout(int64_t n_blocks);

@@ -221,6 +221,7 @@ BWD_CASES = [
     dict(d=64),
     dict(hq=4, hkv=4),
     dict(hq=16, hkv=2, B=5, m=50),
+    dict(hq=6, hkv=2, B=5, m=50),                        # GQA group of 3
     dict(B=1, A=40, hq=2, hkv=1),
     dict(J=12, n_chunks=12, m=16),
     dict(scale_vals=1.0),
