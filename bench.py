@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--workload", default="weak8")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=600,
+    ap.add_argument("--cpu-rows", type=int, default=1200,
                     help="query rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -188,7 +188,10 @@ def main():
         "rank_load_max_over_mean": round(float(load.max() / load.mean()), 5),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_bwd_bf16_kernel" if dominant == "bwd" else "attn_fwd_bf16_kernel",
+            "kernel": ("splitkv_attn_bwd (attn_bwd_dkdv_kernel + attn_bwd_dq_kernel)"
+                       if dominant == "bwd" else "splitkv_attn_fwd (attn_fwd_bf16_kernel)"),
+            "per_launch": "one emulated rank's call; achieved = the phase's mask-live FLOPs "
+                          "over its measured time (= per-launch FLOPs / mean launch time)",
             "achieved": round(ach, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
