@@ -22,9 +22,9 @@ BwdWorkspace bwd_workspace_layout(int64_t n_blocks, int32_t block_size, int32_t 
   w.block_range = 0;
   w.meta = align256((size_t)n_blocks * sizeof(int2));
   const int64_t n_vec = n_blocks * block_size * (hq / hkv);
-  const int64_t n_qc = (n_vec + 31) / 32;
-  // 4 fp32 fields x 32 vectors per (kv head, query chunk)
-  w.chunk_range = w.meta + align256((size_t)hkv * n_qc * 4 * 32 * sizeof(float));
+  const int64_t n_qc = (n_vec + kBwdChunk - 1) / kBwdChunk;
+  // 4 fp32 fields per vector, per (kv head, query chunk)
+  w.chunk_range = w.meta + align256((size_t)hkv * n_qc * 4 * kBwdChunk * sizeof(float));
   w.total = w.chunk_range + align256((size_t)n_qc * sizeof(int4));
   return w;
 }

@@ -34,7 +34,7 @@ namespace {
 
 constexpr int kBwdThreads = 256;  // 4 waves
 constexpr int kBwdKeys = 128;     // keys per workgroup, 32 per wave
-constexpr int kQC = 32;           // query vectors per chunk
+constexpr int kQC = kBwdChunk;    // query vectors per chunk (dK/dV kernel)
 constexpr int kListCap = 1024;    // chunk indices buffered per scan
 
 // Delta[r, h] = <do[r, h], o[r, h]>, one thread per (row, head). fp32 path.
@@ -186,7 +186,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dvt[dt][r] = 0.f; dkt[dt][r] = 0.f; }
 
-  // Stage chunk c (32 vectors): Q, dO rows and the records by asynchronous
+  // Stage chunk c (kQC vectors): Q, dO rows and the records by asynchronous
   // copies. Vectors past the end reuse the last vector's rows (their records
   // are dead, so they add exact zeros).
   auto issue_chunk = [&](int64_t c, bf16_t* Qd, bf16_t* Dd, float* Md) {
@@ -208,33 +208,42 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   };
 
   // S = Q K^T and dP = dO V^T (lane = key, 16 vectors per lane), P, dS,
-  // dV^T += dO^T P, dK^T += Q^T dS.
+  // dV^T += dO^T P, dK^T += Q^T dS, for the chunk's 32-vector halves. The
+  // products of all halves are issued before the elementwise work, so one
+  // half's softmax overlaps the other half's matrix-core work.
+  constexpr int NH = kQC / 32;
   auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
     const bool active = cr.x < kw0 + 32 && cr.y > kw0;
+    if (!active) return;
     const bool need_mask = !(cr.z <= kw0 && cr.w >= kw0 + 32);
-    f32x16 sacc, pacc;
+    f32x16 sacc[NH], pacc[NH];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
-    if (active) {
-      const int qrow = lane & 31;
+    for (int hv = 0; hv < NH; ++hv)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+      for (int r = 0; r < 16; ++r) { sacc[hv][r] = 0.f; pacc[hv][r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int hv = 0; hv < NH; ++hv) {
+        const int qrow = hv * 32 + (lane & 31);
         const int slot = (2 * ks + half) ^ swz_both<NS>(qrow);
         const u32x4 aq = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
         const u32x4 ad = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), kf[ks], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), vf[ks], pacc, 0, 0, 0);
+        sacc[hv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), kf[ks], sacc[hv], 0, 0, 0);
+        pacc[hv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), vf[ks], pacc[hv], 0, 0, 0);
       }
 #pragma unroll
+    for (int hv = 0; hv < NH; ++hv) {
+#pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int q0 = 8 * jj + 4 * half;
+        const int q0 = hv * 32 + 8 * jj + 4 * half;
         const float4 l2 = *reinterpret_cast<const float4*>(&Mb[q0]);
         const float4 dl = *reinterpret_cast<const float4*>(&Mb[kQC + q0]);
         const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
         const float dla[4] = {dl.x, dl.y, dl.z, dl.w};
         float pk[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = fast_exp2(fmaf(sacc[4 * jj + i], scale_log2, -l2a[i]));
+        for (int i = 0; i < 4; ++i) pk[i] = fast_exp2(fmaf(sacc[hv][4 * jj + i], scale_log2, -l2a[i]));
         if (need_mask) {
           const int4 lo = *reinterpret_cast<const int4*>(&Mb[2 * kQC + q0]);
           const int4 hi = *reinterpret_cast<const int4*>(&Mb[3 * kQC + q0]);
@@ -245,22 +254,22 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sacc[4 * jj + i] = pk[i];
-          pacc[4 * jj + i] = pk[i] * (pacc[4 * jj + i] - dla[i]);
+          sacc[hv][4 * jj + i] = pk[i];
+          pacc[hv][4 * jj + i] = pk[i] * (pacc[hv][4 * jj + i] - dla[i]);
         }
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         u32x4 pu, su;
-        pu.x = pack_bf16x2_hw(sacc[8 * h2 + 0], sacc[8 * h2 + 1]);
-        pu.y = pack_bf16x2_hw(sacc[8 * h2 + 2], sacc[8 * h2 + 3]);
-        pu.z = pack_bf16x2_hw(sacc[8 * h2 + 4], sacc[8 * h2 + 5]);
-        pu.w = pack_bf16x2_hw(sacc[8 * h2 + 6], sacc[8 * h2 + 7]);
-        su.x = pack_bf16x2_hw(pacc[8 * h2 + 0], pacc[8 * h2 + 1]);
-        su.y = pack_bf16x2_hw(pacc[8 * h2 + 2], pacc[8 * h2 + 3]);
-        su.z = pack_bf16x2_hw(pacc[8 * h2 + 4], pacc[8 * h2 + 5]);
-        su.w = pack_bf16x2_hw(pacc[8 * h2 + 6], pacc[8 * h2 + 7]);
-        const int vr = 16 * h2 + 4 * half + (s16 >> 2);
+        pu.x = pack_bf16x2_hw(sacc[hv][8 * h2 + 0], sacc[hv][8 * h2 + 1]);
+        pu.y = pack_bf16x2_hw(sacc[hv][8 * h2 + 2], sacc[hv][8 * h2 + 3]);
+        pu.z = pack_bf16x2_hw(sacc[hv][8 * h2 + 4], sacc[hv][8 * h2 + 5]);
+        pu.w = pack_bf16x2_hw(sacc[hv][8 * h2 + 6], sacc[hv][8 * h2 + 7]);
+        su.x = pack_bf16x2_hw(pacc[hv][8 * h2 + 0], pacc[hv][8 * h2 + 1]);
+        su.y = pack_bf16x2_hw(pacc[hv][8 * h2 + 2], pacc[hv][8 * h2 + 3]);
+        su.z = pack_bf16x2_hw(pacc[hv][8 * h2 + 4], pacc[hv][8 * h2 + 5]);
+        su.w = pack_bf16x2_hw(pacc[hv][8 * h2 + 6], pacc[hv][8 * h2 + 7]);
+        const int vr = hv * 32 + 16 * h2 + 4 * half + (s16 >> 2);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
@@ -305,11 +314,10 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
 
     // ---- software pipeline over the list: per chunk `it`, one barrier, the
-    // copies of chunk it+1, then the compute of chunk it ----
-    // Workgroups start at different points of their lists so that the key
-    // tiles of one kv head do not all read the same query rows at once.
-    const int rot = n > 0 ? (int)((blockIdx.x / hkv) * 97u % (unsigned)n) : 0;
-    auto at = [&](int it) { const int j = it + rot; return j >= n ? j - n : j; };
+    // copies of chunk it+1, then the compute of chunk it. Workgroups of one kv
+    // head (one XCD) walk their lists in the same ascending order, so the
+    // query chunks they share are read from that XCD's L2. ----
+    auto at = [](int it) { return it; };
     auto step = [&](int it, const bf16_t* Qb, const bf16_t* Db, const float* Mb, bf16_t* Qn,
                     bf16_t* Dn, float* Mn) {
       wait_async();

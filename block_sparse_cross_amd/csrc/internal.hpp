@@ -13,6 +13,7 @@ namespace splitkv {
 
 constexpr int kMaxPlanRanks = 1024;
 constexpr int kMaxPlanChunks = 4096;
+constexpr int kBwdChunk = 64;  // query vectors per chunk of the dK/dV kernel
 
 // Workspace layout (device bytes), 256-byte aligned segments.
 struct FwdWorkspace {
@@ -21,8 +22,8 @@ struct FwdWorkspace {
 };
 struct BwdWorkspace {
   size_t block_range;  // int2 [N]
-  size_t meta;         // fp32 [hkv][n_qc][4][32]: lse*log2e, Delta, lo, hi per vector
-  size_t chunk_range;  // int4 [n_qc], n_qc = ceil(Q*G / 32)
+  size_t meta;         // fp32 [hkv][n_qc][4][kBwdChunk]: lse*log2e, Delta, lo, hi
+  size_t chunk_range;  // int4 [n_qc], n_qc = ceil(Q*G / kBwdChunk)
   size_t total;
 };
 FwdWorkspace fwd_workspace_layout(int64_t n_blocks);
