@@ -7,24 +7,26 @@
 // dk and dv stay local to the rank; dq is accumulated (+=) so that the P
 // emulated ranks of one device sum into one buffer.
 //
-// bf16 path, three kernels:
-//  1. bwd_prep_kernel: per (row, head) Delta (from o and do, or given) and a
-//     16-byte record {lse * log2 e, Delta, lo, hi} with the row's local key
-//     interval; lse = -inf becomes +inf so that P = exp2(. - inf) = 0.
-//  2. chunk_range_kernel: per 32-vector query chunk, the union of its
+// bf16 path, four kernels:
+//  1. bwd_prep_kernel: Delta (from o and do, or given) and, per query vector,
+//     a record {lse * log2 e, Delta, lo, hi} with the row's local key interval
+//     (lse = -inf becomes +inf so that P = exp2(. - inf) = 0), laid out per
+//     (kv head, 64-vector chunk) as four 64-wide arrays.
+//  2. chunk_range_kernel: per 64-vector query chunk, the union of its
 //     intervals and the interval that every vector of the chunk covers.
 //  3. attn_bwd_dkdv_kernel: a workgroup owns 128 local keys of one kv head (32
-//     per wave; K and V fragments in registers, K also row-major in LDS) and
-//     walks the query chunks whose union reaches those keys. Q, dO and the
+//     per wave; K and V fragments and the dK, dV accumulators in registers)
+//     and walks the query chunks whose union reaches those keys. Q, dO and the
 //     records of the next chunk are copied global -> LDS asynchronously
 //     (double-buffered, row-major, XOR-swizzled) while the current chunk is
-//     computed. Per chunk, with v_mfma_f32_32x32x16_bf16: S = Q K^T and
-//     dP = dO V^T so that a lane owns one key and 16 vectors;
-//     dV^T += dO^T P and dK^T += Q^T dS in registers, the Q^T and dO^T
-//     fragments read by the transposing LDS read; dS^T goes to LDS and
-//     dQ = dS K is formed per 32-wide d slice (both operands through
-//     transposing reads) and added to dq with fp32 atomics. Chunks whose
-//     vectors all cover a wave's 32 keys skip the per-key mask.
+//     computed. Per 32-vector half of a chunk, with v_mfma_f32_32x32x16_bf16:
+//     S = Q K^T and dP = dO V^T so that a lane owns one key and 16 vectors;
+//     dV^T += dO^T P and dK^T += Q^T dS, the Q^T and dO^T fragments read by
+//     the transposing LDS read. Chunks whose vectors all cover a wave's 32
+//     keys skip the per-key mask.
+//  4. attn_bwd_dq_kernel: query-outer like the forward; recomputes S and dP
+//     per key tile and accumulates dQ^T += K^T dS^T in registers, so dq needs
+//     no atomics and is deterministic.
 #include "common.hpp"
 #include "internal.hpp"
 
