@@ -27,6 +27,8 @@
 //  4. attn_bwd_dq_kernel: query-outer like the forward; recomputes S and dP
 //     per key tile and accumulates dQ^T += K^T dS^T in registers, so dq needs
 //     no atomics and is deterministic.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -191,8 +193,39 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // Stage chunk c (kQC vectors): Q, dO rows and the records by asynchronous
   // copies. Vectors past the end reuse the last vector's rows (their records
   // are dead, so they add exact zeros).
+  //
+  // Fast path (G a power of two dividing kQC, chunk inside the buffer): a
+  // chunk is kQC / G whole rows times G heads, so vector vec0 + r sits at
+  // element ((vec0 / G + r / G) hq + g G + r % G) D. With r = RPP p + t (t the
+  // lane's row within pass p, RPP = rows per pass) the offset splits into a
+  // per-lane part fixed for the kernel and a part uniform per pass.
+  constexpr int RPP = kBwdThreads / NS;         // vector rows per copy pass
+  constexpr int QPASSES = kQC * NS / kBwdThreads;  // passes per tensor
+  const bool fast_chunks = gshift >= 0 && gshift <= 6 && (kQC % G) == 0;
+  uint32_t lane_off = 0;
+  {
+    const int t = tid / NS, phys = tid % NS;
+    const int tg = fast_chunks ? (t >> gshift) : 0, th = fast_chunks ? (t & (G - 1)) : 0;
+    lane_off = (uint32_t)(((int64_t)tg * hq + th) * D * 2 + ((phys ^ swz_both<NS>(t)) * 16));
+  }
+  const int lds_wave = __builtin_amdgcn_readfirstlane(wave * 64 * 8);
   auto issue_chunk = [&](int64_t c, bf16_t* Qd, bf16_t* Dd, float* Md) {
     const int64_t vec0 = c * kQC;
+    if (fast_chunks && vec0 + kQC <= n_vec) {
+      const int64_t first = ((vec0 >> gshift) * hq + (int64_t)g * G) * D;
+      const char* qb = reinterpret_cast<const char*>(q + first);
+      const char* db = reinterpret_cast<const char*>(dout + first);
+#pragma unroll
+      for (int pp = 0; pp < QPASSES; ++pp) {
+        const int r0 = RPP * pp;
+        const uint32_t step = (uint32_t)((((int64_t)(r0 >> gshift)) * hq + (r0 & (G - 1))) * D * 2);
+        async_copy16(qb + (lane_off + step), Qd + pp * kBwdThreads * 8 + lds_wave);
+        async_copy16(db + (lane_off + step), Dd + pp * kBwdThreads * 8 + lds_wave);
+      }
+      if (wave == NW - 1 && lane < kQC)
+        async_copy16(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
+      return;
+    }
 #pragma unroll
     for (int pass = 0; pass < 2 * kQC * NS / kBwdThreads; ++pass) {
       const int u = pass * kBwdThreads + tid;      // over [tensor][row][slot]
@@ -209,15 +242,29 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       async_copy16(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
   };
 
+  // Element offsets of this lane's transposing reads of Q and dO (rows t and
+  // t + 8 of each 16-vector step, t = 4 half + s16 / 4), per 32-column block
+  // dt; opaque so that step offsets and buffer bases become immediates.
+  int tr_off[D / 32][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int t = 4 * half + (s16 >> 2);
+    const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    tr_off[dt][0] = t * D + (((dcol >> 3) ^ swz_both<NS>(t)) * 8) + (dcol & 7);
+    tr_off[dt][1] = (t + 8) * D + (((dcol >> 3) ^ swz_both<NS>(t + 8)) * 8) + (dcol & 7);
+    asm volatile("" : "+v"(tr_off[dt][0]), "+v"(tr_off[dt][1]));
+  }
+
   // S = Q K^T and dP = dO V^T (lane = key, 16 vectors per lane), P, dS,
   // dV^T += dO^T P, dK^T += Q^T dS, for the chunk's 32-vector halves. The
   // products of all halves are issued before the elementwise work, so one
   // half's softmax overlaps the other half's matrix-core work.
   constexpr int NH = kQC / 32;
-  auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
-    const bool active = cr.x < kw0 + 32 && cr.y > kw0;
-    if (!active) return;
-    const bool need_mask = !(cr.z <= kw0 && cr.w >= kw0 + 32);
+  // MASKED: some vector's interval cuts this wave's 32 keys (per-key test);
+  // otherwise every vector of the chunk covers them all. The two variants are
+  // separate code so that the common unmasked one has no branches inside.
+  auto compute_chunk = [&](auto masked, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
+    constexpr bool MASKED = decltype(masked)::value;
     f32x16 sacc[NH], pacc[NH];
 #pragma unroll
     for (int hv = 0; hv < NH; ++hv)
@@ -246,7 +293,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         float pk[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk[i] = fast_exp2(fmaf(sacc[hv][4 * jj + i], scale_log2, -l2a[i]));
-        if (need_mask) {
+        if constexpr (MASKED) {
           const int4 lo = *reinterpret_cast<const int4*>(&Mb[2 * kQC + q0]);
           const int4 hi = *reinterpret_cast<const int4*>(&Mb[3 * kQC + q0]);
           pk[0] = (mykey >= lo.x && mykey < hi.x) ? pk[0] : 0.f;
@@ -271,12 +318,10 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         su.y = pack_bf16x2_hw(pacc[hv][8 * h2 + 2], pacc[hv][8 * h2 + 3]);
         su.z = pack_bf16x2_hw(pacc[hv][8 * h2 + 4], pacc[hv][8 * h2 + 5]);
         su.w = pack_bf16x2_hw(pacc[hv][8 * h2 + 6], pacc[hv][8 * h2 + 7]);
-        const int vr = hv * 32 + 16 * h2 + 4 * half + (s16 >> 2);
+        const int vbase = (hv * 32 + 16 * h2) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-          const int o0 = vr * D + (((dcol >> 3) ^ swz_both<NS>(vr)) * 8) + (dcol & 7);
-          const int o1 = (vr + 8) * D + (((dcol >> 3) ^ swz_both<NS>(vr + 8)) * 8) + (dcol & 7);
+          const int o0 = vbase + tr_off[dt][0], o1 = vbase + tr_off[dt][1];
           const u32x2 d0 = read_tr4(&Db[o0]), d1 = read_tr4(&Db[o1]);
           const u32x2 q0 = read_tr4(&Qb[o0]), q1 = read_tr4(&Qb[o1]);
           const u32x4 ad = {d0.x, d0.y, d1.x, d1.y};
@@ -286,6 +331,14 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
       }
     }
+  };
+  auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
+    const bool active = cr.x < kw0 + 32 && cr.y > kw0;
+    if (!active) return;
+    if (cr.z <= kw0 && cr.w >= kw0 + 32)
+      compute_chunk(std::false_type{}, Qb, Db, Mb);
+    else
+      compute_chunk(std::true_type{}, Qb, Db, Mb);
   };
 
   for (int64_t scan = 0; scan < n_qc;) {
@@ -324,10 +377,13 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                     bf16_t* Dn, float* Mn) {
       wait_async();
       __syncthreads();
-      if (it + 1 < n) issue_chunk(list[at(it + 1)], Qn, Dn, Mn);
-      compute_phase(lrange[at(it)], Qb, Db, Mb);
+      if (it + 1 < n) issue_chunk(__builtin_amdgcn_readfirstlane(list[at(it + 1)]), Qn, Dn, Mn);
+      const int4 cr = lrange[at(it)];
+      compute_phase(make_int4(__builtin_amdgcn_readfirstlane(cr.x), __builtin_amdgcn_readfirstlane(cr.y),
+                              __builtin_amdgcn_readfirstlane(cr.z), __builtin_amdgcn_readfirstlane(cr.w)),
+                    Qb, Db, Mb);
     };
-    if (n > 0) issue_chunk(list[at(0)], Qs0, dOs0, Ms0);
+    if (n > 0) issue_chunk(__builtin_amdgcn_readfirstlane(list[at(0)]), Qs0, dOs0, Ms0);
     for (int it = 0; it < n; it += 2) {
       step(it, Qs0, dOs0, Ms0, Qs1, dOs1, Ms1);
       if (it + 1 < n) step(it + 1, Qs1, dOs1, Ms1, Qs0, dOs0, Ms0);
@@ -426,6 +482,19 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   int lo = 0x7fffffff, hi = -1;
 #pragma unroll
   for (int w = 0; w < 4; ++w) { lo = min(lo, wave_lo[w]); hi = max(hi, wave_hi[w]); }
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+
+  auto issue_tile = [&](int k0, bf16_t* Kn, bf16_t* Vn) {
+    if (k0 + kDqKT <= n_keys) {
+      const int64_t first = ((int64_t)k0 * hkv + g) * D;
+      issue_tile_async<D, kDqKT, kDqThreads, kSwzBoth>(k + first, (int64_t)hkv * D, Kn, tid);
+      issue_tile_async<D, kDqKT, kDqThreads, kSwzRows>(v + first, (int64_t)hkv * D, Vn, tid);
+    } else {
+      issue_rows_async<D, kDqKT, kDqThreads, kSwzBoth>(k, hkv, g, k0, n_keys, Kn, tid);
+      issue_rows_async<D, kDqKT, kDqThreads, kSwzRows>(v, hkv, g, k0, n_keys, Vn, tid);
+    }
+  };
 
   f32x16 dqacc[D / 32];
 #pragma unroll
@@ -433,67 +502,82 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.f;
 
+  // Element offsets of this lane's transposing reads of K (rows t and t + 8
+  // of each 16-key step, t = 4 half + s16 / 4), per 32-column block dt. They
+  // are opaque to the compiler so that it adds the step's row offset and the
+  // buffer's base as immediates instead of rebuilding each address.
+  int tr_off[D / 32][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int t = 4 * half + (s16 >> 2);
+    const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    tr_off[dt][0] = t * D + (((dcol >> 3) ^ swz_both<NS>(t)) * 8) + (dcol & 7);
+    tr_off[dt][1] = (t + 8) * D + (((dcol >> 3) ^ swz_both<NS>(t + 8)) * 8) + (dcol & 7);
+    asm volatile("" : "+v"(tr_off[dt][0]), "+v"(tr_off[dt][1]));
+  }
+
   auto tile_step = [&](int k0, const bf16_t* Kt, const bf16_t* Vt, bf16_t* Kn, bf16_t* Vn) {
     wait_async();
     __syncthreads();
-    if (k0 + kDqKT < hi) {
-      issue_rows_async<D, kDqKT, kDqThreads, kSwzBoth>(k, hkv, g, k0 + kDqKT, n_keys, Kn, tid);
-      issue_rows_async<D, kDqKT, kDqThreads, kSwzRows>(v, hkv, g, k0 + kDqKT, n_keys, Vn, tid);
-    }
+    if (k0 + kDqKT < hi) issue_tile(k0 + kDqKT, Kn, Vn);
     if (!(k0 < whi && k0 + kDqKT > wlo)) return;
-    f32x16 sacc[2], pacc[2];
+    const bool tile_masked = k0 < wall_lo || k0 + kDqKT > wall_hi;
+    // The tile's two 32-key halves one after the other: S^T, dP^T (16
+    // products), the weights, dQ^T (8 products); only one half's scores are
+    // live at a time.
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      const int kr = mt * 32 + (lane & 31);
+      f32x16 sacc, pacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { sacc[mt][r] = 0.f; pacc[mt][r] = 0.f; }
+      for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int kr = mt * 32 + (lane & 31);
+      for (int ks = 0; ks < D / 16; ++ks) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&Kt[kr * D + (((2 * ks + half) ^ swz_both<NS>(kr)) * 8)]);
         const u32x4 b = *reinterpret_cast<const u32x4*>(&Vt[kr * D + (((2 * ks + half) ^ swz_rows<NS>(kr)) * 8)]);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
-        pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b), df[ks], pacc[mt], 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b), df[ks], pacc, 0, 0, 0);
       }
-    const bool need_mask = k0 < wall_lo || k0 + kDqKT > wall_hi;
+      // dS^T = P (dP - Delta); the per-key test only on tiles that cut some
+      // lane's interval (a separate copy of the loop, so the common case has
+      // no per-element branches)
+      auto weights = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(sacc[mt][r], scale_log2, -lse2));
-        if (need_mask) {
-          const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          p = (key >= qlo && key < qhi) ? p : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(sacc[r], scale_log2, -lse2));
+          if constexpr (MASKED) {
+            const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            p = (key >= qlo && key < qhi) ? p : 0.f;
+          }
+          sacc[r] = p * (pacc[r] - dl);
         }
-        sacc[mt][r] = p * (pacc[mt][r] - dl);
-      }
-    // dQ^T += K^T dS^T, four 16-key steps
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      };
+      if (tile_masked)
+        weights(std::true_type{});
+      else
+        weights(std::false_type{});
+      // dQ^T += K^T dS^T, two 16-key steps
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         u32x4 su;
-        su.x = pack_bf16x2_hw(sacc[mt][8 * h2 + 0], sacc[mt][8 * h2 + 1]);
-        su.y = pack_bf16x2_hw(sacc[mt][8 * h2 + 2], sacc[mt][8 * h2 + 3]);
-        su.z = pack_bf16x2_hw(sacc[mt][8 * h2 + 4], sacc[mt][8 * h2 + 5]);
-        su.w = pack_bf16x2_hw(sacc[mt][8 * h2 + 6], sacc[mt][8 * h2 + 7]);
-        const int kr = mt * 32 + 16 * h2 + 4 * half + (s16 >> 2);
+        su.x = pack_bf16x2_hw(sacc[8 * h2 + 0], sacc[8 * h2 + 1]);
+        su.y = pack_bf16x2_hw(sacc[8 * h2 + 2], sacc[8 * h2 + 3]);
+        su.z = pack_bf16x2_hw(sacc[8 * h2 + 4], sacc[8 * h2 + 5]);
+        su.w = pack_bf16x2_hw(sacc[8 * h2 + 6], sacc[8 * h2 + 7]);
+        const int kbase = (mt * 32 + 16 * h2) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-          const u32x2 x0 = read_tr4(&Kt[kr * D + (((dcol >> 3) ^ swz_both<NS>(kr)) * 8) + (dcol & 7)]);
-          const u32x2 x1 = read_tr4(&Kt[(kr + 8) * D + (((dcol >> 3) ^ swz_both<NS>(kr + 8)) * 8) + (dcol & 7)]);
+          const u32x2 x0 = read_tr4(&Kt[kbase + tr_off[dt][0]]);
+          const u32x2 x1 = read_tr4(&Kt[kbase + tr_off[dt][1]]);
           const u32x4 au = {x0.x, x0.y, x1.x, x1.y};
           dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(au), as_bf16x8(su), dqacc[dt], 0, 0, 0);
         }
       }
+    }
   };
 
-  if (lo < hi) {
-    issue_rows_async<D, kDqKT, kDqThreads, kSwzBoth>(k, hkv, g, lo, n_keys, K0, tid);
-    issue_rows_async<D, kDqKT, kDqThreads, kSwzRows>(v, hkv, g, lo, n_keys, V0, tid);
-  }
+  if (lo < hi) issue_tile(lo, K0, V0);
   for (int k0 = lo; k0 < hi; k0 += 2 * kDqKT) {
     tile_step(k0, K0, V0, K1, V1);
     if (k0 + kDqKT < hi) tile_step(k0 + kDqKT, K1, V1, K0, V0);

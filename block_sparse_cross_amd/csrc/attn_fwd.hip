@@ -129,6 +129,22 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   int lo = 0x7fffffff, hi = -1;
 #pragma unroll
   for (int w = 0; w < 4; ++w) { lo = min(lo, wave_lo[w]); hi = max(hi, wave_hi[w]); }
+  // the same in every lane: keep the tile loop and its addressing scalar
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+
+  // K and V tiles: rows k0 .. k0 + 63 of kv head g (row stride hkv * D); the
+  // last tile of the buffer may run past it and takes the clamped copy.
+  auto issue_tile = [&](int k0, bf16_t* Kn, bf16_t* Vn) {
+    if (k0 + kKT <= n_keys) {
+      const int64_t first = ((int64_t)k0 * hkv + g) * D;
+      issue_tile_async<D, kKT, kFwdThreads, kSwzRows, false>(k + first, (int64_t)hkv * D, Kn, tid);
+      issue_tile_async<D, kKT, kFwdThreads, kSwzTr, false>(v + first, (int64_t)hkv * D, Vn, tid);
+    } else {
+      issue_rows_async<D, kKT, kFwdThreads, kSwzRows>(k, hkv, g, k0, n_keys, Kn, tid);
+      issue_rows_async<D, kKT, kFwdThreads, kSwzTr>(v, hkv, g, k0, n_keys, Vn, tid);
+    }
+  };
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -144,10 +160,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   auto tile_step = [&](int k0, const bf16_t* Kt, const bf16_t* Vt, bf16_t* Kn, bf16_t* Vn) {
     wait_async();
     __syncthreads();
-    if (k0 + kKT < hi) {
-      issue_rows_async<D, kKT, kFwdThreads, kSwzRows>(k, hkv, g, k0 + kKT, n_keys, Kn, tid);
-      issue_rows_async<D, kKT, kFwdThreads, kSwzTr>(v, hkv, g, k0 + kKT, n_keys, Vn, tid);
-    }
+    if (k0 + kKT < hi) issue_tile(k0 + kKT, Kn, Vn);
     if (!(k0 < whi && k0 + kKT > wlo)) return;  // nothing live for this wave
 
     // ---- S^T = K Q^T for two 32-key halves ----
@@ -234,10 +247,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       }
   };
 
-  if (lo < hi) {
-    issue_rows_async<D, kKT, kFwdThreads, kSwzRows>(k, hkv, g, lo, n_keys, K0, tid);
-    issue_rows_async<D, kKT, kFwdThreads, kSwzTr>(v, hkv, g, lo, n_keys, V0, tid);
-  }
+  if (lo < hi) issue_tile(lo, K0, V0);
   for (int k0 = lo; k0 < hi; k0 += 2 * kKT) {
     tile_step(k0, K0, V0, K1, V1);
     if (k0 + kKT < hi) tile_step(k0 + kKT, K1, V1, K0, V0);

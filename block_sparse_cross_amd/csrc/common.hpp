@@ -96,10 +96,14 @@ __device__ __forceinline__ u32x2 read_tr4(const bf16_t* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Two floats -> packed bf16 pair (round to nearest even) in one
+// v_cvt_pk_bf16_f32; converting the pair as a vector keeps the compiler from
+// splitting it into two single conversions plus a shift and an or.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+  const f32x2_v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -135,14 +139,48 @@ __device__ __forceinline__ void issue_rows_async(const bf16_t* __restrict__ src,
   constexpr int PASSES = ROWS * NS / THREADS;
   static_assert(PASSES * THREADS == ROWS * NS, "tile must split evenly over the threads");
   const int wave = tid >> 6;
+  int t = tid;
+  asm volatile("" : "+v"(t));  // opaque: nothing here is hoisted out of a caller's loop
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
-    const int u = pass * THREADS + tid;
+    const int u = pass * THREADS + t;
     const int row = u / NS, phys = u % NS;
     const int key = min(k0 + row, n_keys - 1);
     async_copy16(src + ((int64_t)key * hkv + g) * D + (phys ^ swz<NS, KIND>(row)) * 8,
                  tile + (pass * THREADS + wave * 64) * 8);
   }
+}
+
+// The same copy for a tile that lies wholly inside the buffer, with the
+// addressing split into a wave-uniform part (the tile's first row and the
+// per-pass steps, scalar) and a per-lane byte offset within the tile (row r at
+// r * row_stride elements, its 16-byte slot permuted by the swizzle KIND).
+// Rows of pass p sit p * THREADS / NS rows below those of pass 0, a multiple
+// of 16, and the swizzles depend on the row modulo 16 only, so one per-lane
+// offset serves every pass. The offset is recomputed from the thread index at
+// each call (a few integer operations) rather than kept live across the tile
+// loop: under register pressure the compiler would otherwise spill it, and a
+// scratch reload waits on the same counter as the asynchronous copies.
+// Kernels with registers to spare pass RECOMPUTE = false and let the compiler
+// hoist the offsets out of the loop.
+template <int D, int ROWS, int THREADS, int KIND, bool RECOMPUTE = true>
+__device__ __forceinline__ void issue_tile_async(const bf16_t* first, int64_t row_stride,
+                                                 bf16_t* tile, int tid) {
+  constexpr int NS = D / 8;
+  constexpr int PASSES = ROWS * NS / THREADS;
+  constexpr int ROWS_PER_PASS = THREADS / NS;
+  static_assert(PASSES * THREADS == ROWS * NS, "tile must split evenly over the threads");
+  static_assert(ROWS_PER_PASS % 16 == 0, "pass step must keep the swizzle");
+  int t = tid;
+  if constexpr (RECOMPUTE) asm volatile("" : "+v"(t));  // opaque: keep the offset computation here
+  const int row = t / NS, phys = t % NS;
+  const uint32_t off = (uint32_t)(row * (uint32_t)row_stride * 2u + (phys ^ swz<NS, KIND>(row)) * 16);
+  const uint32_t step = (uint32_t)(ROWS_PER_PASS * row_stride * 2);  // uniform
+  const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
+  const char* base = reinterpret_cast<const char*>(first);
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass)
+    async_copy16((base + (size_t)pass * step) + off, tile + pass * THREADS * 8 + lds_off);
 }
 
 // Local (per-rank) key range of one block. The local buffer holds the rank's
