@@ -265,73 +265,121 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // separate code so that the common unmasked one has no branches inside.
   auto compute_chunk = [&](auto masked, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
     constexpr bool MASKED = decltype(masked)::value;
+    static_assert(NH == 2, "chunk = two 32-vector halves");
     f32x16 sacc[NH], pacc[NH];
-#pragma unroll
-    for (int hv = 0; hv < NH; ++hv)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sacc[hv][r] = 0.f; pacc[hv][r] = 0.f; }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int hv = 0; hv < NH; ++hv) {
-        const int qrow = hv * 32 + (lane & 31);
-        const int slot = (2 * ks + half) ^ swz_both<NS>(qrow);
-        const u32x4 aq = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
-        const u32x4 ad = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
-        sacc[hv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), kf[ks], sacc[hv], 0, 0, 0);
-        pacc[hv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), vf[ks], pacc[hv], 0, 0, 0);
+    u32x4 qa[3], da[3];      // S / dP operands, up to two pieces ahead
+    u32x4 ta[3], tq[3];      // dO^T / Q^T operands, up to two pieces ahead
+    float4 ml[2], md[2];     // lse log2 e, Delta of 4 vectors (per 8-vector group jj)
+    int4 mlo[2], mhi[2];     // their key intervals (masked chunks only)
+    u32x4 pu, su;            // P and dS of the current 16-vector step, bf16
+
+    auto load_sd = [&](int hv, int ks, int b) {
+      const int qrow = hv * 32 + (lane & 31);
+      const int slot = (2 * ks + half) ^ swz_both<NS>(qrow);
+      qa[b] = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
+      da[b] = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
+    };
+    auto load_upd = [&](int hv, int h2, int dt, int b) {
+      const int vbase = (hv * 32 + 16 * h2) * D;
+      const int o0 = vbase + tr_off[dt][0], o1 = vbase + tr_off[dt][1];
+      const u32x2 d0 = read_tr4(&Db[o0]), d1 = read_tr4(&Db[o1]);
+      const u32x2 q0 = read_tr4(&Qb[o0]), q1 = read_tr4(&Qb[o1]);
+      ta[b] = u32x4{d0.x, d0.y, d1.x, d1.y};
+      tq[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
+    };
+    auto load_meta = [&](int hv, int jj) {
+      const int q0 = hv * 32 + 8 * jj + 4 * half, b = jj & 1;
+      ml[b] = *reinterpret_cast<const float4*>(&Mb[q0]);
+      md[b] = *reinterpret_cast<const float4*>(&Mb[kQC + q0]);
+      if constexpr (MASKED) {
+        mlo[b] = *reinterpret_cast<const int4*>(&Mb[2 * kQC + q0]);
+        mhi[b] = *reinterpret_cast<const int4*>(&Mb[3 * kQC + q0]);
       }
+    };
+    // The chunk runs in pieces: NP = D / 16 per phase, and the P, dS work of
+    // a half is spread over NP pieces, EPP elements each.
+    constexpr int NP = D / 16, DT = D / 32, EPP = 16 / NP;
+    // P and dS of elements EPP w .. EPP w + EPP - 1 of half hv, in place.
+    auto weigh = [&](int hv, int w) {
 #pragma unroll
-    for (int hv = 0; hv < NH; ++hv) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int q0 = hv * 32 + 8 * jj + 4 * half;
-        const float4 l2 = *reinterpret_cast<const float4*>(&Mb[q0]);
-        const float4 dl = *reinterpret_cast<const float4*>(&Mb[kQC + q0]);
-        const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
-        const float dla[4] = {dl.x, dl.y, dl.z, dl.w};
-        float pk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = fast_exp2(fmaf(sacc[hv][4 * jj + i], scale_log2, -l2a[i]));
+      for (int e = 0; e < EPP; ++e) {
+        const int r = EPP * w + e, jj = r >> 2, i = r & 3, b = jj & 1;
+        const float l2 = i == 0 ? ml[b].x : i == 1 ? ml[b].y : i == 2 ? ml[b].z : ml[b].w;
+        const float dl = i == 0 ? md[b].x : i == 1 ? md[b].y : i == 2 ? md[b].z : md[b].w;
+        float pk = fast_exp2(fmaf(sacc[hv][r], scale_log2, -l2));
         if constexpr (MASKED) {
-          const int4 lo = *reinterpret_cast<const int4*>(&Mb[2 * kQC + q0]);
-          const int4 hi = *reinterpret_cast<const int4*>(&Mb[3 * kQC + q0]);
-          pk[0] = (mykey >= lo.x && mykey < hi.x) ? pk[0] : 0.f;
-          pk[1] = (mykey >= lo.y && mykey < hi.y) ? pk[1] : 0.f;
-          pk[2] = (mykey >= lo.z && mykey < hi.z) ? pk[2] : 0.f;
-          pk[3] = (mykey >= lo.w && mykey < hi.w) ? pk[3] : 0.f;
+          const int lo = i == 0 ? mlo[b].x : i == 1 ? mlo[b].y : i == 2 ? mlo[b].z : mlo[b].w;
+          const int hi = i == 0 ? mhi[b].x : i == 1 ? mhi[b].y : i == 2 ? mhi[b].z : mhi[b].w;
+          pk = (mykey >= lo && mykey < hi) ? pk : 0.f;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sacc[hv][4 * jj + i] = pk[i];
-          pacc[hv][4 * jj + i] = pk[i] * (pacc[hv][4 * jj + i] - dla[i]);
-        }
+        sacc[hv][r] = pk;
+        pacc[hv][r] = pk * (pacc[hv][r] - dl);
       }
+    };
+    auto pack = [&](int hv, int h2) {
+      pu.x = pack_bf16x2_hw(sacc[hv][8 * h2 + 0], sacc[hv][8 * h2 + 1]);
+      pu.y = pack_bf16x2_hw(sacc[hv][8 * h2 + 2], sacc[hv][8 * h2 + 3]);
+      pu.z = pack_bf16x2_hw(sacc[hv][8 * h2 + 4], sacc[hv][8 * h2 + 5]);
+      pu.w = pack_bf16x2_hw(sacc[hv][8 * h2 + 6], sacc[hv][8 * h2 + 7]);
+      su.x = pack_bf16x2_hw(pacc[hv][8 * h2 + 0], pacc[hv][8 * h2 + 1]);
+      su.y = pack_bf16x2_hw(pacc[hv][8 * h2 + 2], pacc[hv][8 * h2 + 3]);
+      su.z = pack_bf16x2_hw(pacc[hv][8 * h2 + 4], pacc[hv][8 * h2 + 5]);
+      su.w = pack_bf16x2_hw(pacc[hv][8 * h2 + 6], pacc[hv][8 * h2 + 7]);
+    };
+
+    // One wave per SIMD, so matrix-core and vector work overlap only as far
+    // as the instruction order lets them. The chunk runs as 4 NP pieces of two
+    // products each, fenced so that the compiler keeps them in this order
+    // (nothing moves across __builtin_amdgcn_sched_barrier(0)):
+    //   phase 0: S, dP of half 0 (d-step ks = piece)
+    //   phase 1: S, dP of half 1, with P, dS of half 0
+    //   phase 2: dV^T, dK^T of half 0 (16-vector step h2, column block dt),
+    //            with P, dS of half 1
+    //   phase 3: dV^T, dK^T of half 1
+    // A piece issues the LDS reads of a later one (operand slot = piece mod
+    // 3): two pieces ahead in phases 0 and 3, which have no vector work to
+    // hide the reads behind, one ahead elsewhere.
+    auto load_piece = [&](int x) {
+      const int ph = x / NP, i = x % NP;
+      if (ph < 2) load_sd(ph, i, x % 3);
+      else if (ph < 4) load_upd(ph - 2, i / DT, i % DT, x % 3);
+    };
+    auto dist = [](int x) { return (x / NP == 0 || x / NP == 3) ? 2 : 1; };
+    // The records of 8-vector group jj of half hv are first used in piece
+    // NP (hv + 1) + 4 jj / EPP; they are loaded G = 4 / EPP pieces earlier,
+    // when the group two back (same register slot) is done.
+    constexpr int G = 4 / EPP;
+    load_piece(0);
+    load_piece(1);
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        u32x4 pu, su;
-        pu.x = pack_bf16x2_hw(sacc[hv][8 * h2 + 0], sacc[hv][8 * h2 + 1]);
-        pu.y = pack_bf16x2_hw(sacc[hv][8 * h2 + 2], sacc[hv][8 * h2 + 3]);
-        pu.z = pack_bf16x2_hw(sacc[hv][8 * h2 + 4], sacc[hv][8 * h2 + 5]);
-        pu.w = pack_bf16x2_hw(sacc[hv][8 * h2 + 6], sacc[hv][8 * h2 + 7]);
-        su.x = pack_bf16x2_hw(pacc[hv][8 * h2 + 0], pacc[hv][8 * h2 + 1]);
-        su.y = pack_bf16x2_hw(pacc[hv][8 * h2 + 2], pacc[hv][8 * h2 + 3]);
-        su.z = pack_bf16x2_hw(pacc[hv][8 * h2 + 4], pacc[hv][8 * h2 + 5]);
-        su.w = pack_bf16x2_hw(pacc[hv][8 * h2 + 6], pacc[hv][8 * h2 + 7]);
-        const int vbase = (hv * 32 + 16 * h2) * D;
+    for (int pc = 0; pc < 4 * NP; ++pc) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int o0 = vbase + tr_off[dt][0], o1 = vbase + tr_off[dt][1];
-          const u32x2 d0 = read_tr4(&Db[o0]), d1 = read_tr4(&Db[o1]);
-          const u32x2 q0 = read_tr4(&Qb[o0]), q1 = read_tr4(&Qb[o1]);
-          const u32x4 ad = {d0.x, d0.y, d1.x, d1.y};
-          const u32x4 aq = {q0.x, q0.y, q1.x, q1.y};
-          dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ad), as_bf16x8(pu), dvt[dt], 0, 0, 0);
-          dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), as_bf16x8(su), dkt[dt], 0, 0, 0);
+      for (int x = pc + 1; x <= pc + 2; ++x)
+        if (x >= 2 && x < 4 * NP && x - dist(x) == pc) load_piece(x);
+#pragma unroll
+      for (int hv = 0; hv < NH; ++hv)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (NP * (hv + 1) + (4 * jj) / EPP - G == pc) load_meta(hv, jj);
+      const int ph = pc / NP, i = pc % NP, b = pc % 3;
+      if (ph < 2) {
+        if (i == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) { sacc[ph][r] = 0.f; pacc[ph][r] = 0.f; }
         }
+        sacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[b]), kf[i], sacc[ph], 0, 0, 0);
+        pacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da[b]), vf[i], pacc[ph], 0, 0, 0);
+      } else {
+        const int hv = ph - 2, h2 = i / DT, dt = i % DT;
+        if (dt == 0) pack(hv, h2);
+        dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ta[b]), as_bf16x8(pu), dvt[dt], 0, 0, 0);
+        dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tq[b]), as_bf16x8(su), dkt[dt], 0, 0, 0);
       }
+      if (ph == 1 || ph == 2) weigh(ph - 1, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+
   auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
     const bool active = cr.x < kw0 + 32 && cr.y > kw0;
     if (!active) return;
@@ -437,7 +485,8 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16_t V1[kDqKT * D];
   __shared__ int wave_lo[4], wave_hi[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int s16 = lane & 15;
   const int g = blockIdx.x % hkv;
   const int64_t vec = (int64_t)(blockIdx.x / hkv) * kDqVecPerWG + wave * 32 + (lane & 31);

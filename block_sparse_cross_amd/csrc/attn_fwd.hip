@@ -90,7 +90,8 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16_t V1[kKT * D];
   __shared__ int wave_lo[4], wave_hi[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   // kv head fastest across workgroup ids: consecutive ids land on different
   // XCDs, so each XCD keeps serving the same kv head's keys from its L2.
   const int g = blockIdx.x % hkv;
