@@ -112,10 +112,12 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
   // Key interval union of this wave / workgroup, and the interval every lane
   // of the wave covers (tiles inside it need no per-key mask).
-  const int wlo = wave_min_i(live_lane ? qlo : 0x7fffffff);
-  const int whi = wave_max_i(live_lane ? qhi : -1);
-  const int wall_lo = wave_max_i(live_lane ? qlo : 0x7fffffff);
-  const int wall_hi = wave_min_i(live_lane ? qhi : -1);
+  // (the same in every lane after the reductions; readfirstlane makes that
+  // visible to the compiler, so tests on them are scalar branches)
+  const int wlo = __builtin_amdgcn_readfirstlane(wave_min_i(live_lane ? qlo : 0x7fffffff));
+  const int whi = __builtin_amdgcn_readfirstlane(wave_max_i(live_lane ? qhi : -1));
+  const int wall_lo = __builtin_amdgcn_readfirstlane(wave_max_i(live_lane ? qlo : 0x7fffffff));
+  const int wall_hi = __builtin_amdgcn_readfirstlane(wave_min_i(live_lane ? qhi : -1));
   if (lane == 0) { wave_lo[wave] = wlo; wave_hi[wave] = whi; }
 
   // Query fragment (B operand of S^T = K Q^T): d-slices [16 ks + 8 half, +8).
@@ -134,17 +136,21 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   lo = __builtin_amdgcn_readfirstlane(lo);
   hi = __builtin_amdgcn_readfirstlane(hi);
 
-  // K and V tiles: rows k0 .. k0 + 63 of kv head g (row stride hkv * D); the
+  // K or V tile: rows k0 .. k0 + 63 of kv head g (row stride hkv * D); the
   // last tile of the buffer may run past it and takes the clamped copy.
-  auto issue_tile = [&](int k0, bf16_t* Kn, bf16_t* Vn) {
-    if (k0 + kKT <= n_keys) {
-      const int64_t first = ((int64_t)k0 * hkv + g) * D;
-      issue_tile_async<D, kKT, kFwdThreads, kSwzRows, false>(k + first, (int64_t)hkv * D, Kn, tid);
-      issue_tile_async<D, kKT, kFwdThreads, kSwzTr, false>(v + first, (int64_t)hkv * D, Vn, tid);
-    } else {
-      issue_rows_async<D, kKT, kFwdThreads, kSwzRows>(k, hkv, g, k0, n_keys, Kn, tid);
-      issue_rows_async<D, kKT, kFwdThreads, kSwzTr>(v, hkv, g, k0, n_keys, Vn, tid);
-    }
+  auto issue_k = [&](int k0, bf16_t* dst) {
+    if (k0 + kKT <= n_keys)
+      issue_tile_async<D, kKT, kFwdThreads, kSwzRows>(k + ((int64_t)k0 * hkv + g) * D,
+                                                            (int64_t)hkv * D, dst, tid);
+    else
+      issue_rows_async<D, kKT, kFwdThreads, kSwzRows>(k, hkv, g, k0, n_keys, dst, tid);
+  };
+  auto issue_v = [&](int k0, bf16_t* dst) {
+    if (k0 + kKT <= n_keys)
+      issue_tile_async<D, kKT, kFwdThreads, kSwzTr>(v + ((int64_t)k0 * hkv + g) * D,
+                                                          (int64_t)hkv * D, dst, tid);
+    else
+      issue_rows_async<D, kKT, kFwdThreads, kSwzTr>(v, hkv, g, k0, n_keys, dst, tid);
   };
 
   f32x16 oacc[D / 32];
@@ -154,52 +160,77 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // One tile: wait for its copy, start the copy of the next tile into the
-  // other buffer pair, compute. The buffer pairs are distinct LDS arrays and
-  // the loop below is unrolled by two, so the compiler can tell the copy's LDS
-  // writes from this tile's reads and does not wait for the copy to land.
-  auto tile_step = [&](int k0, const bf16_t* Kt, const bf16_t* Vt, bf16_t* Kn, bf16_t* Vn) {
-    wait_async();
-    __syncthreads();
-    if (k0 + kKT < hi) issue_tile(k0 + kKT, Kn, Vn);
-    if (!(k0 < whi && k0 + kKT > wlo)) return;  // nothing live for this wave
+  // Software pipeline over the key tiles t = 0 .. n_tiles - 1 (keys lo + 64 t
+  // ..): iteration t computes the scores of tile t + 1 while it exponentiates
+  // tile t, then multiplies P(t) V(t) while it takes the row maximum of tile
+  // t + 1. K(j) and V(j) live in slot j % 2 of their double buffers; the copy
+  // of K(t + 2) and V(t + 1) is issued at the top of iteration t, after the
+  // barrier that ends every use of K(t) and V(t - 1).
+  //
+  // The pieces of a phase are fenced (__builtin_amdgcn_sched_barrier(0)) so
+  // that each keeps its two products next to its share of the vector work,
+  // and each issues the LDS reads of the next piece.
+  constexpr int NP = D / 16;    // pieces per phase
+  constexpr int DT = D / 32;    // 32-column blocks of O
+  constexpr int EPP = 32 / NP;  // of a lane's 32 scores, handled per piece
+  const int n_tiles = lo < hi ? (hi - lo + kKT - 1) / kKT : 0;
 
-    // ---- S^T = K Q^T for two 32-key halves ----
-    f32x16 sacc[2];
+  f32x16 sc[2], sn[2];  // scores (then weights) of tile t, scores of tile t + 1
+  u32x4 ka[2][2];       // K operands (mt) for a piece, double-buffered by piece
+  u32x4 va[2][2];       // V^T operands (two products) for a piece
+  u32x4 pu[2][2];       // P of tile t as bf16, per (mt, 16-key step h2)
+  float mloc = -INFINITY;
+
+  auto load_k = [&](const bf16_t* Kt, int ks, int b) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int krow = mt * 32 + (lane & 31);
+      const int slot = (2 * ks + half) ^ swz_rows<NS>(krow);
+      ka[b][mt] = *reinterpret_cast<const u32x4*>(&Kt[krow * D + slot * 8]);
+    }
+  };
+  // products 2 j, 2 j + 1 of P V: (mt, h2) = (2 j) / DT split, dt = (2 j) % DT + {0, 1}
+  auto load_v = [&](const bf16_t* Vt, int j, int b) {
+    const int u0 = 2 * j, mh = u0 / DT, mt = mh >> 1, h2 = mh & 1;
+    const int s16 = lane & 15;
+    const int vrow = mt * 32 + 16 * h2 + 4 * half + (s16 >> 2);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int dt = u0 % DT + e;
+      const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+      const int slot = dcol >> 3, off = dcol & 7;
+      const u32x2 x0 = read_tr4(&Vt[vrow * D + ((slot ^ swz_tr<NS>(vrow)) * 8) + off]);
+      const u32x2 x1 = read_tr4(&Vt[(vrow + 8) * D + ((slot ^ swz_tr<NS>(vrow + 8)) * 8) + off]);
+      va[b][e] = u32x4{x0.x, x0.y, x1.x, x1.y};
+    }
+  };
+  auto zero2 = [](f32x16 (&x)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) x[mt][r] = 0.f;
+  };
+  // keys outside a lane's interval -> -inf (tiles that cut some interval)
+  auto mask_scores = [&](int k0, f32x16 (&x)[2]) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {  // two independent accumulation chains
-        const int krow = mt * 32 + (lane & 31);
-        const int slot = (2 * ks + half) ^ swz_rows<NS>(krow);
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Kt[krow * D + slot * 8]);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        x[mt][r] = (key >= qlo && key < qhi) ? x[mt][r] : -INFINITY;
       }
-    // ---- mask (boundary tiles only), running max ----
-    const bool need_mask = k0 < wall_lo || k0 + kKT > wall_hi;
-    float mloc = -INFINITY;
-    if (need_mask) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float x = (key >= qlo && key < qhi) ? sacc[mt][r] : -INFINITY;
-          sacc[mt][r] = x;
-          mloc = fmaxf(mloc, x);
-        }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mt][r]);
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
-    // ---- lazy rescale: raise the running max only when exceeded by > 8 ----
+  };
+  auto tile_k0 = [&](int t) { return lo + t * kKT; };
+  auto needs_mask = [&](int t) { return tile_k0(t) < wall_lo || tile_k0(t) + kKT > wall_hi; };
+
+  // one pipeline iteration; Kn = K(t + 1), Vc = V(t), Kf / Vf = free slots
+  auto iteration = [&](int t, const bf16_t* Kn, const bf16_t* Vc, bf16_t* Kf, bf16_t* Vf) {
+    wait_async();
+    __syncthreads();
+    if (t + 2 < n_tiles) issue_k(tile_k0(t + 2), Kf);
+    if (t + 1 < n_tiles) issue_v(tile_k0(t + 1), Vf);
+
+    // lazy rescale: raise the running max only when tile t exceeds it by > 8
     if (__any(mloc > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
@@ -211,47 +242,98 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
     const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sacc[mt][r], scale_log2, neg_m));
-        sacc[mt][r] = p;
-        psum += p;
-      }
-    l_run += psum;
 
-    // ---- O^T += V^T P^T, four 16-key steps ----
+    // phase B: S(t + 1) = K(t + 1) Q^T with P(t) = exp2(S(t) c - m)
+    // (scores past the last tile are computed from a stale slot and unused)
+    zero2(sn);
+    float psum = 0.f;
+    load_k(Kn, 0, 0);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int i = 0; i < NP; ++i) {
+      if (i + 1 < NP) load_k(Kn, i + 1, (i + 1) & 1);
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        u32x4 pu;
-        pu.x = pack_bf16x2_hw(sacc[mt][8 * h2 + 0], sacc[mt][8 * h2 + 1]);
-        pu.y = pack_bf16x2_hw(sacc[mt][8 * h2 + 2], sacc[mt][8 * h2 + 3]);
-        pu.z = pack_bf16x2_hw(sacc[mt][8 * h2 + 4], sacc[mt][8 * h2 + 5]);
-        pu.w = pack_bf16x2_hw(sacc[mt][8 * h2 + 6], sacc[mt][8 * h2 + 7]);
-        const bf16x8 pb = as_bf16x8(pu);
-        // keys of this step held by the lane: base + 4 half + {0..3}, +8
-        const int s16 = lane & 15;
-        const int vrow = mt * 32 + 16 * h2 + 4 * half + (s16 >> 2);
+      for (int mt = 0; mt < 2; ++mt)
+        sn[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i & 1][mt]), qf[i], sn[mt], 0, 0, 0);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-          const int slot = dcol >> 3, off = dcol & 7;
-          const u32x2 x0 = read_tr4(&Vt[vrow * D + ((slot ^ swz_tr<NS>(vrow)) * 8) + off]);
-          const u32x2 x1 = read_tr4(&Vt[(vrow + 8) * D + ((slot ^ swz_tr<NS>(vrow + 8)) * 8) + off]);
-          const u32x4 au = {x0.x, x0.y, x1.x, x1.y};
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(au), pb, oacc[dt], 0, 0, 0);
+      for (int e = 0; e < EPP; ++e) {
+        const int x = EPP * i + e, mt = x >> 4, r = x & 15;
+        const float pv = fast_exp2(fmaf(sc[mt][r], scale_log2, neg_m));
+        sc[mt][r] = pv;
+        psum += pv;
+        if ((r & 7) == 7) {
+          const int h2 = r >> 3;
+          pu[mt][h2].x = pack_bf16x2_hw(sc[mt][8 * h2 + 0], sc[mt][8 * h2 + 1]);
+          pu[mt][h2].y = pack_bf16x2_hw(sc[mt][8 * h2 + 2], sc[mt][8 * h2 + 3]);
+          pu[mt][h2].z = pack_bf16x2_hw(sc[mt][8 * h2 + 4], sc[mt][8 * h2 + 5]);
+          pu[mt][h2].w = pack_bf16x2_hw(sc[mt][8 * h2 + 6], sc[mt][8 * h2 + 7]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += psum;
+
+    // phase C: O^T += V(t)^T P(t) with the row maximum of S(t + 1). No
+    // branch may separate the phases (the compiler would sink phase B's
+    // vector work past it), so boundary tiles are masked afterwards and
+    // their maximum taken again.
+    float mx = -INFINITY;
+    load_v(Vc, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      if (j + 1 < NP) load_v(Vc, j + 1, (j + 1) & 1);
+      const int u0 = 2 * j, mh = u0 / DT, mt = mh >> 1, h2 = mh & 1;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int dt = u0 % DT + e;
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j & 1][e]), as_bf16x8(pu[mt][h2]),
+                                                           oacc[dt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) {
+        const int x = EPP * j + e;
+        mx = fmaxf(mx, sn[x >> 4][x & 15]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (t + 1 < n_tiles && needs_mask(t + 1)) {
+      mask_scores(tile_k0(t + 1), sn);
+      mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sn[mt][r]);
+    }
+    mloc = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) sc[mt] = sn[mt];
   };
 
-  if (lo < hi) issue_tile(lo, K0, V0);
-  for (int k0 = lo; k0 < hi; k0 += 2 * kKT) {
-    tile_step(k0, K0, V0, K1, V1);
-    if (k0 + kKT < hi) tile_step(k0 + kKT, K1, V1, K0, V0);
+  if (n_tiles > 0) {
+    issue_k(tile_k0(0), K0);
+    issue_v(tile_k0(0), V0);
+    if (n_tiles > 1) issue_k(tile_k0(1), K1);
+    wait_async();
+    __syncthreads();
+    // scores and row maximum of tile 0
+    zero2(sc);
+#pragma unroll
+    for (int ks = 0; ks < NP; ++ks) {
+      load_k(K0, ks, 0);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[0][mt]), qf[ks], sc[mt], 0, 0, 0);
+    }
+    if (needs_mask(0)) mask_scores(tile_k0(0), sc);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mt][r]);
+    mloc = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+  }
+  for (int t = 0; t < n_tiles; t += 2) {
+    iteration(t, K1, V0, K0, V1);
+    if (t + 1 < n_tiles) iteration(t + 1, K0, V1, K1, V0);
   }
 
   // ---- epilogue: normalise, store o_p and lse_p ----
