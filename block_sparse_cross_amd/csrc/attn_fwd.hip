@@ -138,17 +138,19 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
   // K or V tile: rows k0 .. k0 + 63 of kv head g (row stride hkv * D); the
   // last tile of the buffer may run past it and takes the clamped copy.
+  const uint32_t k_off = tile_lane_offset<D, kFwdThreads, kSwzRows>((int64_t)hkv * D, tid);
+  const uint32_t v_off = tile_lane_offset<D, kFwdThreads, kSwzTr>((int64_t)hkv * D, tid);
   auto issue_k = [&](int k0, bf16_t* dst) {
     if (k0 + kKT <= n_keys)
-      issue_tile_async<D, kKT, kFwdThreads, kSwzRows>(k + ((int64_t)k0 * hkv + g) * D,
-                                                            (int64_t)hkv * D, dst, tid);
+      issue_tile_async_off<D, kKT, kFwdThreads>(k + ((int64_t)k0 * hkv + g) * D, (int64_t)hkv * D,
+                                                k_off, dst, tid);
     else
       issue_rows_async<D, kKT, kFwdThreads, kSwzRows>(k, hkv, g, k0, n_keys, dst, tid);
   };
   auto issue_v = [&](int k0, bf16_t* dst) {
     if (k0 + kKT <= n_keys)
-      issue_tile_async<D, kKT, kFwdThreads, kSwzTr>(v + ((int64_t)k0 * hkv + g) * D,
-                                                          (int64_t)hkv * D, dst, tid);
+      issue_tile_async_off<D, kKT, kFwdThreads>(v + ((int64_t)k0 * hkv + g) * D, (int64_t)hkv * D,
+                                                v_off, dst, tid);
     else
       issue_rows_async<D, kKT, kFwdThreads, kSwzTr>(v, hkv, g, k0, n_keys, dst, tid);
   };
@@ -175,7 +177,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   constexpr int EPP = 32 / NP;  // of a lane's 32 scores, handled per piece
   const int n_tiles = lo < hi ? (hi - lo + kKT - 1) / kKT : 0;
 
-  f32x16 sc[2], sn[2];  // scores (then weights) of tile t, scores of tile t + 1
+  f32x16 sa[2], sb[2];  // scores (then weights) of tiles t and t + 1, alternating
   u32x4 ka[2][2];       // K operands (mt) for a piece, double-buffered by piece
   u32x4 va[2][2];       // V^T operands (two products) for a piece
   u32x4 pu[2][2];       // P of tile t as bf16, per (mt, 16-key step h2)
@@ -224,7 +226,8 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   auto needs_mask = [&](int t) { return tile_k0(t) < wall_lo || tile_k0(t) + kKT > wall_hi; };
 
   // one pipeline iteration; Kn = K(t + 1), Vc = V(t), Kf / Vf = free slots
-  auto iteration = [&](int t, const bf16_t* Kn, const bf16_t* Vc, bf16_t* Kf, bf16_t* Vf) {
+  auto iteration = [&](int t, const bf16_t* Kn, const bf16_t* Vc, bf16_t* Kf, bf16_t* Vf,
+                       f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     wait_async();
     __syncthreads();
     if (t + 2 < n_tiles) issue_k(tile_k0(t + 2), Kf);
@@ -260,6 +263,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         const float pv = fast_exp2(fmaf(sc[mt][r], scale_log2, neg_m));
         sc[mt][r] = pv;
         psum += pv;
+        asm volatile("" : "+v"(psum));  // keep the sum in this piece
         if ((r & 7) == 7) {
           const int h2 = r >> 3;
           pu[mt][h2].x = pack_bf16x2_hw(sc[mt][8 * h2 + 0], sc[mt][8 * h2 + 1]);
@@ -304,8 +308,6 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sn[mt][r]);
     }
     mloc = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) sc[mt] = sn[mt];
   };
 
   if (n_tiles > 0) {
@@ -315,25 +317,25 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     wait_async();
     __syncthreads();
     // scores and row maximum of tile 0
-    zero2(sc);
+    zero2(sa);
 #pragma unroll
     for (int ks = 0; ks < NP; ++ks) {
       load_k(K0, ks, 0);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        sc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[0][mt]), qf[ks], sc[mt], 0, 0, 0);
+        sa[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[0][mt]), qf[ks], sa[mt], 0, 0, 0);
     }
-    if (needs_mask(0)) mask_scores(tile_k0(0), sc);
+    if (needs_mask(0)) mask_scores(tile_k0(0), sa);
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mt][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[mt][r]);
     mloc = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
   }
   for (int t = 0; t < n_tiles; t += 2) {
-    iteration(t, K1, V0, K0, V1);
-    if (t + 1 < n_tiles) iteration(t + 1, K0, V1, K1, V0);
+    iteration(t, K1, V0, K0, V1, sa, sb);
+    if (t + 1 < n_tiles) iteration(t + 1, K0, V1, K1, V0, sb, sa);
   }
 
   // ---- epilogue: normalise, store o_p and lse_p ----

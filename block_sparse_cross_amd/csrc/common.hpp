@@ -183,6 +183,34 @@ __device__ __forceinline__ void issue_tile_async(const bf16_t* first, int64_t ro
     async_copy16((base + (size_t)pass * step) + off, tile + pass * THREADS * 8 + lds_off);
 }
 
+// The same copy with the lane's byte offset computed once by the caller
+// (tile_lane_offset) and kept in one register: a kernel with registers to
+// spare saves the per-call offset arithmetic. The offset is made opaque at
+// each call so that the compiler does not hoist a 64-bit address per pass.
+template <int D, int THREADS, int KIND>
+__device__ __forceinline__ uint32_t tile_lane_offset(int64_t row_stride, int tid) {
+  constexpr int NS = D / 8;
+  const int row = tid / NS, phys = tid % NS;
+  return (uint32_t)(row * (uint32_t)row_stride * 2u + (phys ^ swz<NS, KIND>(row)) * 16);
+}
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void issue_tile_async_off(const bf16_t* first, int64_t row_stride,
+                                                     uint32_t lane_off, bf16_t* tile, int tid) {
+  constexpr int NS = D / 8;
+  constexpr int PASSES = ROWS * NS / THREADS;
+  constexpr int ROWS_PER_PASS = THREADS / NS;
+  static_assert(PASSES * THREADS == ROWS * NS, "tile must split evenly over the threads");
+  static_assert(ROWS_PER_PASS % 16 == 0, "pass step must keep the swizzle");
+  uint32_t off = lane_off;
+  asm volatile("" : "+v"(off));
+  const uint32_t step = (uint32_t)(ROWS_PER_PASS * row_stride * 2);  // uniform
+  const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
+  const char* base = reinterpret_cast<const char*>(first);
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass)
+    async_copy16((base + (size_t)pass * step) + off, tile + pass * THREADS * 8 + lds_off);
+}
+
 // Local (per-rank) key range of one block. The local buffer holds the rank's
 // chunks in ascending global position, so the keys a window [s, a) reaches
 // form one contiguous local interval [lo, hi): lo counts local keys before s,
