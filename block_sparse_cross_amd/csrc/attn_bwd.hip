@@ -267,8 +267,9 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     constexpr bool MASKED = decltype(masked)::value;
     static_assert(NH == 2, "chunk = two 32-vector halves");
     f32x16 sacc[NH], pacc[NH];
-    u32x4 qa[3], da[3];      // S / dP operands, up to two pieces ahead
-    u32x4 ta[3], tq[3];      // dO^T / Q^T operands, up to two pieces ahead
+    // operands of a piece (two products), up to two pieces ahead: Q and dO
+    // rows for S / dP, dO^T and Q^T fragments for dV^T / dK^T
+    u32x4 opa[3], opb[3];
     float4 ml[2], md[2];     // lse log2 e, Delta of 4 vectors (per 8-vector group jj)
     int4 mlo[2], mhi[2];     // their key intervals (masked chunks only)
     u32x4 pu, su;            // P and dS of the current 16-vector step, bf16
@@ -276,16 +277,16 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     auto load_sd = [&](int hv, int ks, int b) {
       const int qrow = hv * 32 + (lane & 31);
       const int slot = (2 * ks + half) ^ swz_both<NS>(qrow);
-      qa[b] = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
-      da[b] = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
+      opa[b] = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
+      opb[b] = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
     };
     auto load_upd = [&](int hv, int h2, int dt, int b) {
       const int vbase = (hv * 32 + 16 * h2) * D;
       const int o0 = vbase + tr_off[dt][0], o1 = vbase + tr_off[dt][1];
       const u32x2 d0 = read_tr4(&Db[o0]), d1 = read_tr4(&Db[o1]);
       const u32x2 q0 = read_tr4(&Qb[o0]), q1 = read_tr4(&Qb[o1]);
-      ta[b] = u32x4{d0.x, d0.y, d1.x, d1.y};
-      tq[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
+      opa[b] = u32x4{d0.x, d0.y, d1.x, d1.y};
+      opb[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
     };
     auto load_meta = [&](int hv, int jj) {
       const int q0 = hv * 32 + 8 * jj + 4 * half, b = jj & 1;
@@ -367,13 +368,13 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
           for (int r = 0; r < 16; ++r) { sacc[ph][r] = 0.f; pacc[ph][r] = 0.f; }
         }
-        sacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[b]), kf[i], sacc[ph], 0, 0, 0);
-        pacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da[b]), vf[i], pacc[ph], 0, 0, 0);
+        sacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opa[b]), kf[i], sacc[ph], 0, 0, 0);
+        pacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opb[b]), vf[i], pacc[ph], 0, 0, 0);
       } else {
         const int hv = ph - 2, h2 = i / DT, dt = i % DT;
         if (dt == 0) pack(hv, h2);
-        dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ta[b]), as_bf16x8(pu), dvt[dt], 0, 0, 0);
-        dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tq[b]), as_bf16x8(su), dkt[dt], 0, 0, 0);
+        dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opa[b]), as_bf16x8(pu), dvt[dt], 0, 0, 0);
+        dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opb[b]), as_bf16x8(su), dkt[dt], 0, 0, 0);
       }
       if (ph == 1 || ph == 2) weigh(ph - 1, i);
       __builtin_amdgcn_sched_barrier(0);
@@ -489,7 +490,8 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int s16 = lane & 15;
   const int g = blockIdx.x % hkv;
-  const int64_t vec = (int64_t)(blockIdx.x / hkv) * kDqVecPerWG + wave * 32 + (lane & 31);
+  // vector groups in reverse (longest windows first), as in the forward
+  const int64_t vec = (int64_t)((gridDim.x / hkv) - 1 - blockIdx.x / hkv) * kDqVecPerWG + wave * 32 + (lane & 31);
   const bool valid = vec < n_vec;
   int64_t row = 0;
   int hh = 0, qlo = 0, qhi = 0;

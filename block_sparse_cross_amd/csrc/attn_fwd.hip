@@ -95,7 +95,10 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // kv head fastest across workgroup ids: consecutive ids land on different
   // XCDs, so each XCD keeps serving the same kv head's keys from its L2.
   const int g = blockIdx.x % hkv;
-  const int64_t vgroup = blockIdx.x / hkv;
+  // Vector groups in reverse: blocks are ordered by ascending anchor within a
+  // sample, so late groups have the longest windows; starting them first
+  // shortens the tail of the launch.
+  const int64_t vgroup = (gridDim.x / hkv) - 1 - blockIdx.x / hkv;
   const int64_t vec = vgroup * kVecPerWG + wave * kVecPerWave + (lane & 31);
   const bool valid = vec < n_vec;
   int64_t row = 0;
