@@ -13,6 +13,8 @@ live query-key pair, backward 10*d*Hq) of all ranks per second of step time.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +27,99 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# Everything that decides the kernels' machine code: measured HBM traffic is
+# only reported while these files hash to the value recorded with it.
+KERNEL_SOURCES = ["block_sparse_cross_amd/csrc/" + f for f in
+                  ("api.hip", "attn_bwd.hip", "attn_fwd.hip", "merge.hip", "plan.hip",
+                   "common.hpp", "internal.hpp")] + ["block_sparse_cross_amd/build.py",
+                                                     "include/splitkv.h"]
+
+# The kernels one call of each entry point launches (names as in a trace).
+ENTRY_KERNELS = {
+    "splitkv_plan": ["chunk_cost_kernel", "lpt_kernel"],
+    "splitkv_attn_fwd": ["block_range_kernel", "attn_fwd_bf16_kernel"],
+    "splitkv_lse_merge": ["lse_merge_kernel"],
+    "splitkv_attn_bwd": ["block_range_kernel", "bwd_prep_kernel", "chunk_range_kernel",
+                         "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"],
+}
+COPY_CALIBRATION_BYTES = 1 << 30   # the --copy-calibration device copy
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Per-launch HBM traffic recorded under profiles/ for this workload, if it
+    was taken with the current kernel sources; else None."""
+    want = sources_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("workload") == workload and rec.get("sources_sha256") == want:
+                        return rec
+    return None
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str) -> str:
+    """Markdown summary of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE,
+    KiB per dispatch) of `bench.py --copy-calibration`: each counter is scaled by
+    what it reads for the 1 GiB device copy, then summed over the kernels of one
+    call of each entry point."""
+    import csv
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter:
+                        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    factors = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_kernel(d, counter)
+        copies = [v for name, vs in vals.items() if "copyBuffer" in name for v in vs]
+        big = max(copies) if copies else 0.0
+        if big <= 0:
+            raise SystemExit("no copy dispatch found for %s calibration" % counter)
+        factors[counter] = COPY_CALIBRATION_BYTES / (big * 1024.0)
+        for key, kernels in ENTRY_KERNELS.items():
+            tot = 0.0
+            for k in kernels:
+                ks = [v for name, vs in vals.items() if k in name for v in vs]
+                if ks:
+                    tot += sum(ks) / len(ks)
+            out.setdefault(key, {})[counter] = tot * 1024.0 * factors[counter]
+    rec = {"workload": workload, "sources_sha256": sources_hash(),
+           "calibration": {"fetch_factor": round(factors["FETCH_SIZE"], 4),
+                           "write_factor": round(factors["WRITE_SIZE"], 4)},
+           "per_launch_bytes": {k: {"fetch": round(v["FETCH_SIZE"]), "write": round(v["WRITE_SIZE"])}
+                                for k, v in out.items()}}
+    lines = ["# HBM traffic per call: %s" % workload, "",
+             "Commands (run from the repository root on one MI355X, one counter per pass):", "",
+             "```", command, "```", "",
+             "Each counter is scaled by the factor that makes the 1 GiB device copy of "
+             "`--copy-calibration` read (FETCH_SIZE) and write (WRITE_SIZE) 1 GiB: "
+             "fetch x%.4f, write x%.4f. Figures are per call of the entry point (the mean "
+             "per dispatch of each of its kernels, summed)." % (factors["FETCH_SIZE"],
+                                                                factors["WRITE_SIZE"]), "",
+             "| entry point | fetch (GB) | write (GB) |", "|---|---:|---:|"]
+    for k, v in rec["per_launch_bytes"].items():
+        lines.append("| %s | %.3f | %.3f |" % (k, v["fetch"] / 1e9, v["write"] / 1e9))
+    lines += ["", "Kernel sources hash (bench.py reports `roofline.traffic` only while it "
+              "matches): `%s`" % rec["sources_sha256"], "", "traffic-json: " + json.dumps(rec)]
+    return "\n".join(lines) + "\n"
 
 
 def parse():
@@ -39,11 +134,19 @@ def parse():
                     help="query rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--command", default="",
+                    help="with --summarize-counters: the profiling commands, for the record")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(args.summarize_counters[0], args.summarize_counters[1],
+                                            args.workload, args.command))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -154,6 +257,12 @@ def main():
     merge_gbs = merge_bytes / (phase[2] * 1e-3) / 1e9
     dominant = "bwd" if phase[3] >= phase[1] else "fwd"
     ach = bwd_tflops if dominant == "bwd" else fwd_tflops
+    entry = "splitkv_attn_bwd" if dominant == "bwd" else "splitkv_attn_fwd"
+    rec = load_traffic(args.workload)
+    traffic = None
+    if rec is not None and entry in rec["per_launch_bytes"]:
+        t = rec["per_launch_bytes"][entry]
+        traffic = t["fetch"] + t["write"]
 
     result = {
         "metric": "mask-live attn fwd+bwd TFLOP/s (% MFMA peak) + LSE-merge GB/s, 1 MI355X",
@@ -196,7 +305,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            # HBM bytes (read + write) per call, from the calibrated counters
+            # under profiles/ while they match the current kernel sources
+            "traffic": traffic,
         },
         "setup_s": round(setup_s, 1),
     }
