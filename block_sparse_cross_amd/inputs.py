@@ -29,7 +29,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 # tensor ids of the keyed random streams
-T_ANCHORS, T_Q, T_K, T_V, T_DO, T_O, T_LSE, T_OPART, T_LPART = range(9)
+T_ANCHORS, T_Q, T_K, T_V, T_DO, T_O, T_LSE, T_OPART, T_LPART, T_KB, T_VB = range(11)
 
 KV_UNIT = 256  # rows of k/v per keyed random stream
 
@@ -203,6 +203,15 @@ def gen_kv_rows(w: Workload, seed: int, which: str, start: int, count: int) -> n
     full = np.concatenate(parts, axis=0)
     off = start - u0 * KV_UNIT
     return np.ascontiguousarray(full[off:off + count])
+
+
+def gen_block_kv(w: Workload, seed: int, which: str, blocks=None) -> np.ndarray:
+    """Keys or values of the draft blocks' own B tokens [len(blocks)*B, hkv, d]
+    (the "block keys" of Figure 1: one row per query row, in block order)."""
+    tid = {"k": T_KB, "v": T_VB}[which]
+    blocks = range(w.N) if blocks is None else blocks
+    return np.concatenate([normal_values(rng(seed, tid, int(i)), (w.B, w.hkv, w.d), w.scale,
+                                         w.dtype) for i in blocks], axis=0)
 
 
 def gen_local_kv(w: Workload, seed: int, chunk_ids, which: str) -> np.ndarray:

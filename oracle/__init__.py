@@ -5,7 +5,8 @@ and the CPU-baseline leg of the benchmark, never by the product path. It shares
 no code with the HIP library; only the seeded input generators are common.
 
 Each wrapper converts numpy inputs to the C types and returns numpy outputs;
-all arithmetic is in oracle.c (see its header for the equations followed).
+all arithmetic is in oracle.c (see its header for the equations followed),
+except that full_mask_bwd adds the two key sets' dq contributions.
 """
 from __future__ import annotations
 
@@ -216,6 +217,49 @@ def attn_bwd(B: int, s, a, q, dout, lse, dlt, key_pos, k, v, scale: float,
                           _p(dq, ctypes.c_double), len(dkv_keys), _p(dkv_keys, ctypes.c_int64),
                           _p(dk, ctypes.c_double), _p(dv, ctypes.c_double))
     return dq, dk, dv
+
+
+# ------------------------------------------------- full mask (own blocks) --
+def own_block_windows(n_blocks: int, B: int):
+    """Windows of the own-block part of the mask (Figure 1 and §3.1 of the Split-KV
+    paper: a block's rows also see all B tokens of their own block). With the
+    block keys in block order at positions 0 .. n_blocks*B - 1, block i's window
+    is [iB, (i+1)B). Returns (s', a', key positions)."""
+    i = np.arange(n_blocks, dtype=np.int64)
+    return i * B, (i + 1) * B, np.arange(n_blocks * B, dtype=np.int64)
+
+
+def full_mask_attn(B: int, s, a, q, ctx_pos, k, v, kb, vb, scale: float):
+    """Attention under the whole block-sparse mask of Figure 1 for every query
+    row: the context window [s_i, a_i) of the context keys (positions ctx_pos)
+    and the own block's B block keys (kb, vb [Q, hkv, d], block order). Written
+    as the method writes it: the two partials (Eq. 3) merged by Eq. 4.
+    Returns (o [Q, hq, d], lse [Q, hq]) in fp64."""
+    q = _f64(q)
+    Q, hq, d = q.shape
+    rows = np.arange(Q, dtype=np.int64)
+    o_c, l_c = partial_attn(rows, B, s, a, q, ctx_pos, k, v, scale)
+    sb, ab, pb = own_block_windows(Q // B, B)
+    o_b, l_b = partial_attn(rows, B, sb, ab, q, pb, kb, vb, scale)
+    o, lse = merge(np.stack([o_c.reshape(Q * hq, d), o_b.reshape(Q * hq, d)]),
+                   np.stack([l_c.reshape(-1), l_b.reshape(-1)]))
+    return o.reshape(Q, hq, d), lse.reshape(Q, hq)
+
+
+def full_mask_bwd(B: int, s, a, q, dout, o, lse, ctx_pos, k, v, kb, vb, scale: float):
+    """Backward of full_mask_attn given its output o and lse (Algorithm 1: the
+    global lse and Delta = <do, o>, then each key set's local backward; dq sums
+    the two). Returns (dq [Q, hq, d], dk, dv [n_ctx, hkv, d], dkb, dvb [Q, hkv, d])."""
+    q = _f64(q)
+    Q = q.shape[0]
+    dl = delta(o, dout)
+    rows = np.arange(Q, dtype=np.int64)
+    dq_c, dk, dv = attn_bwd(B, s, a, q, dout, lse, dl, ctx_pos, k, v, scale, rows,
+                            np.arange(len(_i64(ctx_pos)), dtype=np.int64))
+    sb, ab, pb = own_block_windows(Q // B, B)
+    dq_b, dkb, dvb = attn_bwd(B, sb, ab, q, dout, lse, dl, pb, kb, vb, scale, rows,
+                              np.arange(Q, dtype=np.int64))
+    return dq_c + dq_b, dk, dv, dkb, dvb
 
 
 def local_key_positions(chunk_ids, m: int) -> np.ndarray:
