@@ -132,6 +132,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1200,
                     help="query rows in the oracle's timed sample")
+    ap.add_argument("--own-blocks", action="store_true",
+                    help="whole mask: also the own-block partial of every block (its B "
+                         "block keys), merged with the P context partials and in the backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -188,8 +191,14 @@ def main():
         locs.append((to_dev(ids.astype(np.int64) * w.m), k, v))
     Q, hq, d = w.Q, w.hq, w.d
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    o_parts = torch.empty((w.P, Q, hq, d), dtype=tdt, device=dev)
-    l_parts = torch.empty((w.P, Q, hq), dtype=torch.float32, device=dev)
+    n_parts = w.P + (1 if args.own_blocks else 0)
+    o_parts = torch.empty((n_parts, Q, hq, d), dtype=tdt, device=dev)
+    l_parts = torch.empty((n_parts, Q, hq), dtype=torch.float32, device=dev)
+    if args.own_blocks:   # block keys/values and the own-block windows
+        kb = to_dev(inputs.gen_block_kv(w, seed, "k"))
+        vb = to_dev(inputs.gen_block_kv(w, seed, "v"))
+        bs, ba, bcs, blen = binding.own_block_local(sd, w.B)
+        dkb, dvb = torch.empty_like(kb), torch.empty_like(vb)
     o = torch.empty((Q, hq, d), dtype=tdt, device=dev)
     lse = torch.empty((Q, hq), dtype=torch.float32, device=dev)
     dq = torch.empty((Q, hq, d), dtype=torch.float32, device=dev)
@@ -217,6 +226,9 @@ def main():
         for p, (cs, k, v) in enumerate(locs):
             binding.splitkv_attn_fwd(sd, ad, w.B, cs, w.m, q, k, v,
                                      out=(o_parts[p], l_parts[p]), workspace=ws)
+        if args.own_blocks:
+            binding.splitkv_attn_fwd(bs, ba, w.B, bcs, blen, q, kb, vb,
+                                     out=(o_parts[w.P], l_parts[w.P]), workspace=ws)
         mark(2)
         binding.splitkv_lse_merge(o_parts, l_parts, out=(o, lse))
         mark(3)
@@ -224,6 +236,9 @@ def main():
         for p, (cs, k, v) in enumerate(locs):
             binding.splitkv_attn_bwd(sd, ad, w.B, cs, w.m, q, k, v, o if p == 0 else None, do,
                                      lse, dq, delta=delta, out=(dks[p], dvs[p]), workspace=ws)
+        if args.own_blocks:
+            binding.splitkv_attn_bwd(bs, ba, w.B, bcs, blen, q, kb, vb, None, do, lse, dq,
+                                     delta=delta, out=(dkb, dvb), workspace=ws)
         mark(4)
 
     for _ in range(args.warmup):
@@ -246,6 +261,9 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     pairs = int(cost.sum())                  # sum over ranks of live (row, key) pairs per head
+    D = (w.N // w.P) * w.B * w.B             # own-block pairs per rank (Section 4.2's D)
+    if args.own_blocks:
+        pairs += w.N * w.B * w.B             # every row also sees its block's B keys
     fwd_flops = 4.0 * d * hq * pairs
     bwd_flops = 10.0 * d * hq * pairs
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
@@ -253,12 +271,12 @@ def main():
     bwd_tflops = bwd_flops / (phase[3] * 1e-3) / 1e12
     e_in = 2 if tdt == torch.bfloat16 else 4
     rows = Q * hq
-    merge_bytes = w.P * rows * (d * e_in + 4) + rows * (d * e_in + 4)
+    merge_bytes = n_parts * rows * (d * e_in + 4) + rows * (d * e_in + 4)
     merge_gbs = merge_bytes / (phase[2] * 1e-3) / 1e9
     dominant = "bwd" if phase[3] >= phase[1] else "fwd"
     ach = bwd_tflops if dominant == "bwd" else fwd_tflops
     entry = "splitkv_attn_bwd" if dominant == "bwd" else "splitkv_attn_fwd"
-    rec = load_traffic(args.workload)
+    rec = load_traffic(args.workload + ("+own" if args.own_blocks else ""))
     traffic = None
     if rec is not None and entry in rec["per_launch_bytes"]:
         t = rec["per_launch_bytes"][entry]
@@ -280,9 +298,13 @@ def main():
         "config": {
             "workload": "%s: b=%d x L=%d context (S=%d), %d anchors/sample x B=%d (Q=%d), "
                         "Hq/Hkv/d=%d/%d/%d, m=%d, P=%d ranks x J=%d chunks, all ranks "
-                        "emulated on one GPU" % (w.name, w.b, w.L, w.S, w.A, w.B, Q, hq,
-                                                 w.hkv, d, w.m, w.P, w.J),
-            "step": "plan + fwd(all ranks) + merge + bwd(all ranks)",
+                        "emulated on one GPU%s" % (w.name, w.b, w.L, w.S, w.A, w.B, Q, hq,
+                                                   w.hkv, d, w.m, w.P, w.J,
+                                                   ", plus every block's own B keys"
+                                                   if args.own_blocks else ""),
+            "step": ("plan + fwd(all ranks + own blocks) + merge of P+1 + bwd(all ranks + own "
+                     "blocks)" if args.own_blocks else
+                     "plan + fwd(all ranks) + merge + bwd(all ranks)"),
             "live_pairs_per_head": pairs,
         },
         "fwd_tflops": round(fwd_tflops, 2),
@@ -295,6 +317,8 @@ def main():
         "phase_ms": {"plan": round(phase[0], 4), "fwd_all_ranks": round(phase[1], 4),
                      "merge": round(phase[2], 4), "bwd_all_ranks": round(phase[3], 4)},
         "rank_load_max_over_mean": round(float(load.max() / load.mean()), 5),
+        # rho with every rank's own blocks added (W_p = C_p + D, Section 4.2)
+        "rank_load_max_over_mean_with_D": round(float((load.max() + D) / (load.mean() + D)), 5),
         "roofline": {
             "bound": "mfma",
             "kernel": ("splitkv_attn_bwd (attn_bwd_dkdv_kernel + attn_bwd_dq_kernel)"

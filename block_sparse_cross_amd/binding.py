@@ -179,6 +179,19 @@ def splitkv_plan(s: torch.Tensor, a: torch.Tensor, block_size: int, S: int, m: i
     return out
 
 
+def own_block_local(s: torch.Tensor, block_size: int):
+    """Windows and key table for the own-block part of the mask (Figure 1 of the
+    Split-KV paper: a block's rows also attend all B tokens of their own block).
+    The block keys are laid out in block order as one chunk of n_blocks*B
+    positions, so block i's window is [iB, (i+1)B). Returns (s', a',
+    chunk_start, chunk_len) to pass to splitkv_attn_fwd / splitkv_attn_bwd with
+    the block keys and values."""
+    n = s.numel()
+    i = torch.arange(n, dtype=torch.int64, device=s.device)
+    return (i * block_size, (i + 1) * block_size,
+            torch.zeros(1, dtype=torch.int64, device=s.device), n * block_size)
+
+
 def splitkv_attn_fwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v,
                      scale: Optional[float] = None, o_dtype: Optional[torch.dtype] = None,
                      out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
