@@ -27,11 +27,17 @@ CFLAGS = [
     "-I" + INCLUDE, "-I" + CSRC,
     "-Wall", "-Wno-unused-function",
 ]
+# Per-file code generation choices. The backward's dK/dV kernel holds its dK, dV
+# accumulators in AGPRs; the matrix products of the scores then default to the
+# AGPR form too, and every score is copied back before the softmax. The VGPR
+# form keeps the scores where the vector ALU reads them (measured: dK/dV about
+# 2% faster, no change to the arithmetic).
+EXTRA_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

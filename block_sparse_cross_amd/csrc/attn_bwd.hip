@@ -255,6 +255,20 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     asm volatile("" : "+v"(tr_off[dt][0]), "+v"(tr_off[dt][1]));
   }
 
+  // Element offsets of this lane's row-major reads of Q and dO (row lane % 32
+  // of a half, d-step ks; the second half adds 32 rows) and of its first record
+  // in a 4-vector group. Opaque, like tr_off, so that each buffer's base
+  // becomes an immediate instead of one register per (buffer, offset).
+  int row_off[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int qrow = lane & 31;
+    row_off[ks] = qrow * D + (((2 * ks + half) ^ swz_both<NS>(qrow)) * 8);
+    asm volatile("" : "+v"(row_off[ks]));
+  }
+  int rec_off = 4 * half;
+  asm volatile("" : "+v"(rec_off));
+
   // S = Q K^T and dP = dO V^T (lane = key, 16 vectors per lane), P, dS,
   // dV^T += dO^T P, dK^T += Q^T dS, for the chunk's 32-vector halves. The
   // products of all halves are issued before the elementwise work, so one
@@ -275,10 +289,8 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     u32x4 pu, su;            // P and dS of the current 16-vector step, bf16
 
     auto load_sd = [&](int hv, int ks, int b) {
-      const int qrow = hv * 32 + (lane & 31);
-      const int slot = (2 * ks + half) ^ swz_both<NS>(qrow);
-      opa[b] = *reinterpret_cast<const u32x4*>(&Qb[qrow * D + slot * 8]);
-      opb[b] = *reinterpret_cast<const u32x4*>(&Db[qrow * D + slot * 8]);
+      opa[b] = *reinterpret_cast<const u32x4*>(&Qb[hv * 32 * D + row_off[ks]]);
+      opb[b] = *reinterpret_cast<const u32x4*>(&Db[hv * 32 * D + row_off[ks]]);
     };
     auto load_upd = [&](int hv, int h2, int dt, int b) {
       const int vbase = (hv * 32 + 16 * h2) * D;
@@ -289,7 +301,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       opb[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
     };
     auto load_meta = [&](int hv, int jj) {
-      const int q0 = hv * 32 + 8 * jj + 4 * half, b = jj & 1;
+      const int q0 = hv * 32 + 8 * jj + rec_off, b = jj & 1;
       ml[b] = *reinterpret_cast<const float4*>(&Mb[q0]);
       md[b] = *reinterpret_cast<const float4*>(&Mb[kQC + q0]);
       if constexpr (MASKED) {
