@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_zigzag_loads.restype = ctypes.c_int
         L.oracle_contiguous_loads.argtypes = [ctypes.c_int64, i64p, ctypes.c_int32, i64p]
         L.oracle_contiguous_loads.restype = ctypes.c_int
+        L.oracle_baseline_plan.argtypes = [ctypes.c_int32, ctypes.c_int64, i64p, i64p, i64p,
+                                           ctypes.c_int32, i64p, i64p]
+        L.oracle_baseline_plan.restype = ctypes.c_int64
         L.oracle_imbalance.argtypes = [ctypes.c_int32, i64p, ctypes.c_int64, ctypes.c_int64]
         L.oracle_imbalance.restype = ctypes.c_double
         L.oracle_partial_attn.argtypes = [ctypes.c_int64, i64p, ctypes.c_int64, i64p, i64p,
@@ -145,6 +148,21 @@ def contiguous_loads(prof, P: int) -> np.ndarray:
                                      _p(out, ctypes.c_int64)) != 0:
         raise ValueError("context length must be divisible by P")
     return out
+
+
+def baseline_plan(strategy: int, sample_start, sample_len, prof, P: int):
+    """No balance (strategy 0) or Zigzag (1) as ranges: (range_cost [R], load [P])."""
+    st, ln, pr = _i64(sample_start), _i64(sample_len), _i64(prof)
+    R = P if strategy == 0 else 2 * P * len(st)
+    cost = np.zeros(R, dtype=np.int64)
+    load = np.zeros(P, dtype=np.int64)
+    got = lib().oracle_baseline_plan(int(strategy), len(st), _p(st, ctypes.c_int64),
+                                     _p(ln, ctypes.c_int64), _p(pr, ctypes.c_int64), P,
+                                     _p(cost, ctypes.c_int64), _p(load, ctypes.c_int64))
+    if got < 0:
+        raise ValueError("sample lengths do not divide into the assignment's ranges")
+    assert got == R
+    return cost, load
 
 
 def imbalance(ctx_load, n_blocks: int, B: int) -> float:

@@ -162,6 +162,47 @@ EXPORT int oracle_contiguous_loads(int64_t S, const int64_t* prof, int32_t P, in
     return 0;
 }
 
+/* Both comparators as explicit ranges, in the order the product reports them */
+/* (strategy 0 = No balance, 1 = Zigzag):                                    */
+/*   No balance: range p = [p*S/P, (p+1)*S/P) owned by rank p, S = sum len.   */
+/*   Zigzag: range u*2P + c = chunk c of sample u, owned by rank c if c < P,  */
+/*   else by rank 2P-1-c.                                                     */
+/* A range's cost is the sum of the profile over its positions; a rank's     */
+/* load is the sum of its ranges' costs. The samples are packed in order     */
+/* (st[u] = sum of the earlier lengths). Returns the number of ranges R, or  */
+/* -1 if a length does not divide.                                           */
+EXPORT int64_t oracle_baseline_plan(int32_t strategy, int64_t n_samples, const int64_t* st,
+                                    const int64_t* len, const int64_t* prof, int32_t P,
+                                    int64_t* range_cost, int64_t* load) {
+    int64_t S = 0;
+    for (int64_t u = 0; u < n_samples; ++u) S += len[u];
+    for (int32_t p = 0; p < P; ++p) load[p] = 0;
+    if (strategy == 0) {
+        if (S % P != 0) return -1;
+        int64_t w = S / P;
+        for (int32_t p = 0; p < P; ++p) {
+            int64_t c = 0;
+            for (int64_t x = (int64_t)p * w; x < (int64_t)(p + 1) * w; ++x) c += prof[x];
+            range_cost[p] = c;
+            load[p] += c;
+        }
+        return P;
+    }
+    for (int64_t u = 0; u < n_samples; ++u)
+        if (len[u] % (2 * P) != 0) return -1;
+    for (int64_t u = 0; u < n_samples; ++u) {
+        int64_t w = len[u] / (2 * P);
+        for (int32_t c = 0; c < 2 * P; ++c) {
+            int32_t owner = c < P ? c : 2 * P - 1 - c;
+            int64_t lo = st[u] + (int64_t)c * w, cost = 0;
+            for (int64_t x = lo; x < lo + w; ++x) cost += prof[x];
+            range_cost[u * 2 * P + c] = cost;
+            load[owner] += cost;
+        }
+    }
+    return 2 * (int64_t)P * n_samples;
+}
+
 /* §4.2: W_p = C_p + D with D = (N/P) B^2; rho = max_p W_p / mean_p W_p. */
 EXPORT double oracle_imbalance(int32_t P, const int64_t* ctx_load, int64_t n_blocks, int64_t B) {
     double D = (double)n_blocks / (double)P * (double)(B * B);
