@@ -27,8 +27,10 @@ SPLITKV_FP32 = 1
 
 SPLITKV_OP_PLAN, SPLITKV_OP_FWD, SPLITKV_OP_BWD, SPLITKV_OP_MERGE = 0, 1, 2, 3
 
-EXPORTED = ("splitkv_workspace_bytes", "splitkv_plan", "splitkv_attn_fwd", "splitkv_lse_merge",
-            "splitkv_attn_bwd", "splitkv_status_str")
+SPLITKV_BASELINE_NO_BALANCE, SPLITKV_BASELINE_ZIGZAG = 0, 1
+
+EXPORTED = ("splitkv_workspace_bytes", "splitkv_plan", "splitkv_plan_baseline",
+            "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_attn_bwd", "splitkv_status_str")
 
 
 class SplitKVError(RuntimeError):
@@ -70,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.splitkv_plan.argtypes = [A, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_int32, vp, vp, vp, vp, vp]
         L.splitkv_plan.restype = ctypes.c_int
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.splitkv_plan_baseline.argtypes = [ctypes.c_int, A, ctypes.c_int32, i64p, i64p,
+                                            ctypes.c_int32, vp, vp, vp]
+        L.splitkv_plan_baseline.restype = ctypes.c_int
         L.splitkv_attn_fwd.argtypes = [A, H, Lc, vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
         L.splitkv_attn_fwd.restype = ctypes.c_int
         L.splitkv_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp,
@@ -176,6 +182,37 @@ def splitkv_plan(s: torch.Tensor, a: torch.Tensor, block_size: int, S: int, m: i
     _check("splitkv_plan", lib().splitkv_plan(ctypes.byref(an), int(S), int(m), int(P), int(J),
                                               _ptr(cost), _ptr(owner), _ptr(chunks), _ptr(load),
                                               _stream(stream)))
+    return out
+
+
+def baseline_range_count(strategy: int, n_samples: int, P: int) -> int:
+    """Number of ranges splitkv_plan_baseline prices (P, or 2P per sample)."""
+    return P if strategy == SPLITKV_BASELINE_NO_BALANCE else 2 * P * n_samples
+
+
+def splitkv_plan_baseline(strategy: int, s: torch.Tensor, a: torch.Tensor, block_size: int,
+                          sample_start, sample_len, P: int,
+                          out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                          stream: Optional[torch.cuda.Stream] = None):
+    """Context work of a position-based assignment (No balance or Zigzag) on the GPU.
+
+    sample_start, sample_len: the packed samples (host integer sequences).
+    Returns (range_cost int64 [R], rank_load int64 [P]) as device tensors."""
+    n = len(sample_start)
+    st = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in sample_start])
+    ln = (ctypes.c_int64 * max(len(sample_len), 1))(*[int(x) for x in sample_len])
+    if len(sample_len) != n:
+        raise ValueError("sample_start and sample_len differ in length")
+    dev = s.device
+    if out is None:
+        R = baseline_range_count(strategy, n, P)
+        out = (torch.empty(max(R, 1), dtype=torch.int64, device=dev),
+               torch.empty(max(P, 1), dtype=torch.int64, device=dev))
+    cost, load = out
+    an = make_anchors(s, a, block_size)
+    _check("splitkv_plan_baseline",
+           lib().splitkv_plan_baseline(int(strategy), ctypes.byref(an), n, st, ln, int(P),
+                                       _ptr(cost), _ptr(load), _stream(stream)))
     return out
 
 

@@ -112,9 +112,43 @@ int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int
       rank_load == nullptr)
     return SPLITKV_ERR_INVALID_ARG;
   if (P > kMaxPlanRanks || (int64_t)P * J > kMaxPlanChunks) return SPLITKV_ERR_UNSUPPORTED;
+  // every chunk cost is at most B * N * m, so a rank's load is below B * N * S
+  if ((__int128)an->block_size * an->n_blocks * S >= ((__int128)1 << 53))
+    return SPLITKV_ERR_UNSUPPORTED;
   return hip_status(launch_plan(an->s, an->a, an->n_blocks, an->block_size, m, P, J, chunk_cost,
                                 chunk_owner, rank_chunks, rank_load,
                                 static_cast<hipStream_t>(stream)));
+}
+
+int splitkv_plan_baseline(int strategy, const splitkv_anchors* an, int32_t n_samples,
+                          const int64_t* sample_start, const int64_t* sample_len, int32_t P,
+                          int64_t* range_cost, int64_t* rank_load, void* stream) {
+  int st = check_anchors(an);
+  if (st != SPLITKV_OK) return st;
+  if (strategy != SPLITKV_BASELINE_NO_BALANCE && strategy != SPLITKV_BASELINE_ZIGZAG)
+    return SPLITKV_ERR_INVALID_ARG;
+  if (P < 1 || n_samples < 1 || sample_start == nullptr || sample_len == nullptr ||
+      range_cost == nullptr || rank_load == nullptr)
+    return SPLITKV_ERR_INVALID_ARG;
+  if (P > kMaxPlanRanks || n_samples > kMaxBaselineSamples) return SPLITKV_ERR_UNSUPPORTED;
+  BaselineSamples smp;
+  smp.n = n_samples;
+  int64_t next = 0;
+  for (int32_t u = 0; u < n_samples; ++u) {
+    // packed in order from 0; the sum stays far below 2^62 for valid lengths
+    if (sample_start[u] != next || sample_len[u] < 1 || sample_len[u] > (int64_t(1) << 48))
+      return SPLITKV_ERR_INVALID_ARG;
+    if (strategy == SPLITKV_BASELINE_ZIGZAG && sample_len[u] % (2 * (int64_t)P) != 0)
+      return SPLITKV_ERR_INVALID_ARG;
+    smp.start[u] = sample_start[u];
+    smp.len[u] = sample_len[u];
+    next += sample_len[u];
+  }
+  const int64_t S = next;
+  if (strategy == SPLITKV_BASELINE_NO_BALANCE && S % P != 0) return SPLITKV_ERR_INVALID_ARG;
+  return hip_status(launch_plan_baseline(strategy, an->s, an->a, an->n_blocks, an->block_size,
+                                         smp, P, S, range_cost, rank_load,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int splitkv_attn_fwd(const splitkv_anchors* an, const splitkv_heads* hd,

@@ -14,6 +14,14 @@ namespace splitkv {
 constexpr int kMaxPlanRanks = 1024;
 constexpr int kMaxPlanChunks = 4096;
 constexpr int kBwdChunk = 64;  // query vectors per chunk of the dK/dV kernel
+constexpr int kMaxBaselineSamples = 128;
+
+// Packed sample table of a position-based assignment, passed by value.
+struct BaselineSamples {
+  int32_t n;
+  int64_t start[kMaxBaselineSamples];
+  int64_t len[kMaxBaselineSamples];
+};
 
 // Workspace layout (device bytes), 256-byte aligned segments.
 struct FwdWorkspace {
@@ -32,6 +40,11 @@ BwdWorkspace bwd_workspace_layout(int64_t n_blocks, int32_t block_size, int32_t 
 hipError_t launch_plan(const int64_t* s, const int64_t* a, int64_t n_blocks, int32_t B,
                        int64_t m, int32_t P, int32_t J, int64_t* cost, int32_t* owner,
                        int32_t* rank_chunks, int64_t* rank_load, hipStream_t stream);
+
+hipError_t launch_plan_baseline(int strategy, const int64_t* s, const int64_t* a,
+                                int64_t n_blocks, int32_t B, const BaselineSamples& samples,
+                                int32_t P, int64_t S, int64_t* range_cost, int64_t* rank_load,
+                                hipStream_t stream);
 
 hipError_t launch_block_ranges(const int64_t* s, const int64_t* a, int64_t n_blocks,
                                const int64_t* chunk_start, int32_t n_chunks, int64_t m,

@@ -39,6 +39,60 @@ chunk_cost_kernel(const int64_t* __restrict__ s, const int64_t* __restrict__ a,
   }
 }
 
+// Position-based assignments (Zigzag of §3.3 / Figure 5(b); the contiguous
+// "No balance" split of §5.5). One workgroup per range prices it like Eq. 6
+// (overlap of every anchor window with the range, times B); a second kernel
+// sums each rank's ranges. Range order and ownership are those of the entry
+// point's contract.
+__global__ void __launch_bounds__(kCostThreads)
+range_cost_kernel(const int64_t* __restrict__ s, const int64_t* __restrict__ a, int64_t n_blocks,
+                  int64_t B, int strategy, int P, int64_t S, BaselineSamples smp,
+                  int64_t* __restrict__ range_cost) {
+  const int64_t r = blockIdx.x;
+  int64_t lo, width;
+  if (strategy == SPLITKV_BASELINE_NO_BALANCE) {
+    width = S / P;
+    lo = r * width;
+  } else {
+    const int u = (int)(r / (2 * P));
+    const int c = (int)(r % (2 * P));
+    width = smp.len[u] / (2 * P);
+    lo = smp.start[u] + (int64_t)c * width;
+  }
+  const int64_t hi = lo + width;
+  long long t = 0;
+  for (int64_t i = threadIdx.x; i < n_blocks; i += kCostThreads) {
+    const int64_t x0 = max(s[i], lo), x1 = min(a[i], hi);
+    if (x1 > x0) t += x1 - x0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+  __shared__ long long part[kCostThreads / kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (lane == 0) part[wave] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long c = 0;
+    for (int w = 0; w < kCostThreads / kWave; ++w) c += part[w];
+    range_cost[r] = B * c;
+  }
+}
+
+__global__ void __launch_bounds__(kCostThreads)
+rank_sum_kernel(const int64_t* __restrict__ range_cost, int strategy, int P, int n_samples,
+                int64_t* __restrict__ rank_load) {
+  const int p = blockIdx.x * kCostThreads + threadIdx.x;
+  if (p >= P) return;
+  long long load = 0;
+  if (strategy == SPLITKV_BASELINE_NO_BALANCE) {
+    load = range_cost[p];
+  } else {
+    for (int u = 0; u < n_samples; ++u)
+      load += range_cost[(int64_t)u * 2 * P + p] + range_cost[(int64_t)u * 2 * P + 2 * P - 1 - p];
+  }
+  rank_load[p] = load;
+}
+
 // Bitonic sort of n (power of two) (key, idx) pairs in LDS. `desc_key`
 // selects key-descending order; ties always break by ascending idx.
 __device__ void bitonic_sort(long long* key, int* idx, int n, bool desc_key) {
@@ -66,14 +120,50 @@ __device__ void bitonic_sort(long long* key, int* idx, int n, bool desc_key) {
   }
 }
 
-// (load, rank) lexicographic minimum across a wave; every lane gets it.
-__device__ __forceinline__ void wave_argmin(long long& load, int& rank) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    long long ol = __shfl_xor(load, off);
-    int orank = __shfl_xor(rank, off);
-    if (ol < load || (ol == load && orank < rank)) { load = ol; rank = orank; }
-  }
+// Greedy keys: a rank's (load, rank) pair packed as load * 1024 + rank, so the
+// lexicographic minimum (least load, then lowest rank) is the integer minimum.
+// Loads stay below 2^53 (the host checks B * N * S, which bounds any chunk
+// total, since every overlap is clipped to its chunk), so keys fit in 63 bits.
+constexpr int kRankBits = 10;
+constexpr unsigned long long kNoKey = ~0ull;
+
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_min_step(unsigned long long v) {
+  const int lo = (int)(unsigned)v, hi = (int)(unsigned)(v >> 32);
+  const unsigned olo = (unsigned)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const unsigned ohi = (unsigned)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+  return o < v ? o : v;
+}
+
+__device__ __forceinline__ unsigned long long lane_value(unsigned long long v, int lane) {
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), lane);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, lane);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Every lane takes the value of the next lane up (wave-wide DPP shift); the
+// last lane keeps its own.
+__device__ __forceinline__ unsigned long long wave_shift_down(unsigned long long v) {
+  const int lo = (int)(unsigned)v, hi = (int)(unsigned)(v >> 32);
+  const unsigned slo = (unsigned)__builtin_amdgcn_update_dpp(lo, lo, 0x130, 0xF, 0xF, false);
+  const unsigned shi = (unsigned)__builtin_amdgcn_update_dpp(hi, hi, 0x130, 0xF, 0xF, false);
+  return ((unsigned long long)shi << 32) | slo;
+}
+
+// Minimum key of the wave, returned as a wave-uniform value: minima of lane
+// quads (two quad permutations), of 8 lanes (half-row mirror) and of 16 lanes
+// (row mirror) through DPP, then the four row minima read out.
+__device__ __forceinline__ unsigned long long wave_min_key(unsigned long long v) {
+  v = dpp_min_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_min_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_min_step<0x141>(v);  // row_half_mirror
+  v = dpp_min_step<0x140>(v);  // row_mirror
+  unsigned long long r0 = lane_value(v, 0), r1 = lane_value(v, 16);
+  unsigned long long r2 = lane_value(v, 32), r3 = lane_value(v, 48);
+  r0 = r0 < r1 ? r0 : r1;
+  r2 = r2 < r3 ? r2 : r3;
+  return r0 < r2 ? r0 : r2;
 }
 
 // One workgroup: sort chunks by cost (descending), hand them out greedily, then
@@ -85,8 +175,7 @@ lpt_kernel(const int64_t* __restrict__ cost, int n_chunks, int P, int J,
   __shared__ long long key[kMaxPlanChunks];
   __shared__ int idx[kMaxPlanChunks];
   __shared__ int owner[kMaxPlanChunks];
-  __shared__ long long best_load[2][kLptThreads / kWave];
-  __shared__ int best_rank[2][kLptThreads / kWave];
+  __shared__ unsigned long long best_key[2][kLptThreads / kWave];
 
   int n = 1;
   while (n < n_chunks) n <<= 1;
@@ -97,40 +186,69 @@ lpt_kernel(const int64_t* __restrict__ cost, int n_chunks, int P, int J,
   __syncthreads();
   bitonic_sort(key, idx, n, /*desc_key=*/true);
 
-  // Greedy: thread p owns rank p; argmin over ranks with < J chunks.
+  // Greedy: thread p keeps rank p's load and chunk count. The sorted costs are
+  // taken 64 at a time into a register (lane k holds step t0 + k) and read out
+  // as uniform values; step t0 + k's owner is kept by lane k and written once
+  // per 64 steps.
   const int p = threadIdx.x;
   const int lane = p % kWave, wave = p / kWave;
   const int n_waves = (P + kWave - 1) / kWave;
   long long load = 0;
   int held = 0;
-  const long long kNone = 0x7fffffffffffffffLL;
   if (n_waves == 1) {
+    // P <= 64: the wave also keeps the ranks in order, lane l holding the l-th
+    // smallest key (ranks with J chunks hold kNoKey, at the end). The least
+    // loaded open rank is lane 0; after it takes the chunk its new key is put
+    // back at the slot given by the number of keys below it, the lanes before
+    // that slot moving up by one.
     if (wave == 0) {
-      for (int t = 0; t < n_chunks; ++t) {
-        long long cand = (p < P && held < J) ? load : kNone;
-        int r = p;
-        wave_argmin(cand, r);
-        if (p == r) { load += key[t]; held += 1; }
-        if (p == 0) owner[idx[t]] = r;
+      unsigned long long sk = lane < P ? (unsigned long long)lane : kNoKey;  // all loads 0
+      for (int t0 = 0; t0 < n_chunks; t0 += kWave) {
+        const int cnt = min(kWave, n_chunks - t0);
+        const long long kv = lane < cnt ? key[t0 + lane] : 0;
+        int my_owner = 0;
+        for (int k = 0; k < cnt; ++k) {
+          const unsigned long long up = wave_shift_down(sk);  // lane l: key of lane l + 1
+          const unsigned long long front = lane_value(sk, 0);
+          const int r = (int)(front & ((1u << kRankBits) - 1));
+          const long long kt = (long long)lane_value((unsigned long long)kv, k);
+          if (lane == r) { load += kt; held += 1; }
+          const int held_r = __builtin_amdgcn_readlane(held, r);
+          const unsigned long long nk =
+              held_r < J ? ((((front >> kRankBits) + (unsigned long long)kt) << kRankBits) |
+                            (unsigned)r)
+                         : kNoKey;
+          const int pos = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sk < nk) & ~1ull);
+          sk = lane < pos ? up : (lane == pos ? nk : sk);
+          if (lane == k) my_owner = r;
+        }
+        if (lane < cnt) owner[idx[t0 + lane]] = my_owner;
       }
     }
   } else {
-    for (int t = 0; t < n_chunks; ++t) {
-      long long cand = (p < P && held < J) ? load : kNone;
-      int r = p;
-      wave_argmin(cand, r);
-      const int buf = t & 1;
-      if (lane == 0 && wave < n_waves) { best_load[buf][wave] = cand; best_rank[buf][wave] = r; }
-      __syncthreads();
-      long long bl = best_load[buf][0];
-      int br = best_rank[buf][0];
-      for (int w = 1; w < n_waves; ++w) {
-        long long l2 = best_load[buf][w];
-        int r2 = best_rank[buf][w];
-        if (l2 < bl || (l2 == bl && r2 < br)) { bl = l2; br = r2; }
+    // P > 64: a lexicographic (load, rank) argmin over all ranks per step.
+    for (int t0 = 0; t0 < n_chunks; t0 += kWave) {
+      const int cnt = min(kWave, n_chunks - t0);
+      const long long kv = lane < cnt ? key[t0 + lane] : 0;
+      int my_owner = 0;
+      for (int k = 0; k < cnt; ++k) {
+        const unsigned long long cand =
+            (p < P && held < J) ? ((unsigned long long)load << kRankBits) | (unsigned)p : kNoKey;
+        const int buf = k & 1;
+        const unsigned long long wbest = wave_min_key(cand);  // whole wave, before the lane test
+        if (lane == 0) best_key[buf][wave] = wbest;
+        __syncthreads();
+        unsigned long long b = best_key[buf][0];
+        for (int w = 1; w < n_waves; ++w) {
+          const unsigned long long o = best_key[buf][w];
+          b = o < b ? o : b;
+        }
+        const int r = (int)(b & ((1u << kRankBits) - 1));
+        const long long kt = (long long)lane_value((unsigned long long)kv, k);
+        if (p == r) { load += kt; held += 1; }
+        if (lane == k) my_owner = r;
       }
-      if (p == br) { load += key[t]; held += 1; }
-      if (p == 0) owner[idx[t]] = br;
+      if (wave == 0 && lane < cnt) owner[idx[t0 + lane]] = my_owner;
     }
   }
   __syncthreads();
@@ -149,6 +267,22 @@ lpt_kernel(const int64_t* __restrict__ cost, int n_chunks, int P, int J,
 }
 
 }  // namespace
+
+hipError_t launch_plan_baseline(int strategy, const int64_t* s, const int64_t* a,
+                                int64_t n_blocks, int32_t B, const BaselineSamples& samples,
+                                int32_t P, int64_t S, int64_t* range_cost, int64_t* rank_load,
+                                hipStream_t stream) {
+  const int64_t n_ranges =
+      strategy == SPLITKV_BASELINE_NO_BALANCE ? P : 2 * (int64_t)P * samples.n;
+  hipLaunchKernelGGL(range_cost_kernel, dim3((unsigned)n_ranges), dim3(kCostThreads), 0, stream,
+                     s, a, n_blocks, (int64_t)B, strategy, P, S, samples, range_cost);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(rank_sum_kernel, dim3((P + kCostThreads - 1) / kCostThreads),
+                     dim3(kCostThreads), 0, stream, range_cost, strategy, P, samples.n,
+                     rank_load);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const int64_t* s, const int64_t* a, int64_t n_blocks, int32_t B,
                        int64_t m, int32_t P, int32_t J, int64_t* cost, int32_t* owner,

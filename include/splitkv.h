@@ -94,11 +94,38 @@ size_t splitkv_workspace_bytes(int op, const splitkv_anchors* an, const splitkv_
  * Outputs (device): chunk_cost int64 [P*J], chunk_owner int32 [P*J],
  *   rank_chunks int32 [P][J] (each rank's chunks ascending), rank_load int64 [P]
  *   (= C_p, the context work of rank p).
- * Requires P*J*m == S, P <= 1024, P*J <= 4096. Integer only: the result is
- * unique and reproducible bit for bit. */
+ * Requires P*J*m == S, P <= 1024, P*J <= 4096, B*N*S < 2^53 (else
+ * SPLITKV_ERR_UNSUPPORTED). Integer only: the result is unique and
+ * reproducible bit for bit. */
 int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int32_t J,
                  int64_t* chunk_cost, int32_t* chunk_owner, int32_t* rank_chunks,
                  int64_t* rank_load, void* stream);
+
+/* The two position-based assignments the cost-aware plan is measured against
+ * (§3.3 and Figure 5(b) for Zigzag; §5.5 and Figure 9 for No balance). */
+typedef enum {
+    SPLITKV_BASELINE_NO_BALANCE = 0, /* rank p owns the p-th of P equal contiguous parts of [0, S) */
+    SPLITKV_BASELINE_ZIGZAG = 1      /* each sample in 2P equal chunks; rank p owns p and 2P-1-p  */
+} splitkv_baseline;
+
+/* Context work of a position-based assignment, priced like Eq. 6 but over the
+ * assignment's own ranges:
+ *   range_cost[r] = B * sum_i |[s_i, a_i) ∩ [lo_r, hi_r)|   (int64)
+ *   rank_load[p]  = sum of range_cost over the ranges rank p owns (= C_p).
+ * Ranges, in output order:
+ *   NO_BALANCE: R = P ranges; range p = [p*S/P, (p+1)*S/P), owned by rank p,
+ *     where S = sample_start[n-1] + sample_len[n-1].
+ *   ZIGZAG: R = 2P * n_samples ranges; range u*2P + c is chunk c of sample u,
+ *     [st_u + c*L_u/(2P), st_u + (c+1)*L_u/(2P)), owned by rank c for c < P and
+ *     by rank 2P-1-c otherwise.
+ * sample_start, sample_len: HOST int64 [n_samples], the packed samples in order
+ * (sample_start[0] == 0, each sample starts where the previous one ends, every
+ * length >= 1); 1 <= n_samples <= 128. P <= 1024. NO_BALANCE requires S % P == 0,
+ * ZIGZAG requires every L_u % (2P) == 0 (else SPLITKV_ERR_INVALID_ARG).
+ * Outputs (device): range_cost int64 [R], rank_load int64 [P]. Integer only. */
+int splitkv_plan_baseline(int strategy, const splitkv_anchors* an, int32_t n_samples,
+                          const int64_t* sample_start, const int64_t* sample_len, int32_t P,
+                          int64_t* range_cost, int64_t* rank_load, void* stream);
 
 /* Local partial attention, Eq. 3: for every query row r (block i) and head h,
  * over the local keys whose global position lies in [s_i, a_i):
