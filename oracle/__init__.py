@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_baseline_plan.argtypes = [ctypes.c_int32, ctypes.c_int64, i64p, i64p, i64p,
                                            ctypes.c_int32, i64p, i64p]
         L.oracle_baseline_plan.restype = ctypes.c_int64
+        L.oracle_lse_reduce.argtypes = [ctypes.c_int32, ctypes.c_int64, f64p, f64p]
+        L.oracle_lse_reduce.restype = None
+        L.oracle_lse_rescale.argtypes = [ctypes.c_int64, ctypes.c_int32, f64p, f64p, f64p, f64p]
+        L.oracle_lse_rescale.restype = None
         L.oracle_imbalance.argtypes = [ctypes.c_int32, i64p, ctypes.c_int64, ctypes.c_int64]
         L.oracle_imbalance.restype = ctypes.c_double
         L.oracle_partial_attn.argtypes = [ctypes.c_int64, i64p, ctypes.c_int64, i64p, i64p,
@@ -200,6 +204,25 @@ def merge(o_parts, lse_parts):
     lib().oracle_merge(P, rows, d, _p(o_parts, ctypes.c_double), _p(lse_parts, ctypes.c_double),
                        _p(o, ctypes.c_double), _p(lse, ctypes.c_double))
     return o, lse
+
+
+def lse_reduce(lse_parts) -> np.ndarray:
+    """lse_parts [P, rows] -> lse [rows] (the LSE half of Eq. 4)."""
+    lp = _f64(lse_parts)
+    P, rows = lp.shape
+    out = np.zeros(rows, dtype=np.float64)
+    lib().oracle_lse_reduce(P, rows, _p(lp, ctypes.c_double), _p(out, ctypes.c_double))
+    return out
+
+
+def lse_rescale(o_part, lse_part, lse) -> np.ndarray:
+    """o_part [rows, d], lse_part, lse [rows] -> exp(lse_part - lse) o_part (0 if empty)."""
+    o_part, lp, l = _f64(o_part), _f64(lse_part), _f64(lse)
+    rows, d = o_part.shape
+    out = np.zeros((rows, d), dtype=np.float64)
+    lib().oracle_lse_rescale(rows, d, _p(o_part, ctypes.c_double), _p(lp, ctypes.c_double),
+                             _p(l, ctypes.c_double), _p(out, ctypes.c_double))
+    return out
 
 
 def delta(o, dout) -> np.ndarray:

@@ -16,6 +16,7 @@
  *   Eq. 6 (§4.2)        chunk cost; the cost-aware LPT rule with J per rank
  *   §4.2 (balance)      D = (N/P) B^2, W_p = C_p + D, rho = max W / mean W
  *   §3.3, Figure 5(b)   Zigzag: 2P chunks per sample, rank p gets p and 2P-1-p
+ *   §4.1, Algorithm 1   MERGE in per-rank form: LSE reduction, then rescaling
  *
  * Floating point is fp64 throughout, inputs included: the tests widen the exact
  * bf16/fp32 values the GPU consumed to fp64 before calling in.
@@ -315,6 +316,36 @@ EXPORT void oracle_merge(int32_t P, int64_t rows, int32_t d, const double* o_par
 /* Algorithm 1, MERGE_BWD: the global per-(row, head) statistic               */
 /* Delta = <do, o> with o the merged (globally normalised) output.            */
 /* ------------------------------------------------------------------------- */
+/* ------------------------------------------------------------------------- */
+/* Eq. 4 in the two halves each rank applies in Algorithm 1's MERGE when the  */
+/* partials live on different devices: the LSE statistics are reduced first   */
+/* (lse = log sum_p exp lse_p, all -inf gives -inf), then each rank rescales  */
+/* its own partial, o_bar_p = exp(lse_p - lse) o_p (0 where lse_p = -inf).    */
+/* Summed over p, the o_bar_p are the merged output.                          */
+/* ------------------------------------------------------------------------- */
+EXPORT void oracle_lse_reduce(int32_t P, int64_t rows, const double* lse_parts, double* lse) {
+    for (int64_t r = 0; r < rows; ++r) {
+        double mx = -INFINITY;
+        for (int32_t p = 0; p < P; ++p)
+            if (lse_parts[(int64_t)p * rows + r] > mx) mx = lse_parts[(int64_t)p * rows + r];
+        if (mx == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double sum = 0.0;
+        for (int32_t p = 0; p < P; ++p) sum += exp(lse_parts[(int64_t)p * rows + r] - mx);
+        lse[r] = mx + log(sum);
+    }
+}
+
+EXPORT void oracle_lse_rescale(int64_t rows, int32_t d, const double* o_part,
+                               const double* lse_part, const double* lse, double* o_bar) {
+    for (int64_t r = 0; r < rows; ++r) {
+        double w = lse_part[r] == -INFINITY ? 0.0 : exp(lse_part[r] - lse[r]);
+        for (int32_t c = 0; c < d; ++c) o_bar[r * d + c] = w * o_part[r * d + c];
+    }
+}
+
 EXPORT void oracle_delta(int64_t rows, int32_t hq, int32_t d, const double* o,
                          const double* dout, double* delta) {
 #pragma omp parallel for schedule(static)
