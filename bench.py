@@ -4,6 +4,9 @@ One step = one pass of the whole hot path over one synthetic micro-batch:
   plan (chunk costs + LPT) -> partial attention forward of every emulated rank
   -> LSE merge of the P partials -> backward of every emulated rank (Delta
   computed once from the merged output, dq accumulated over ranks).
+  With --merge-form per-rank the merge is done as each rank would do it with
+  the partials on different devices: an LSE reduction, each rank rescaling its
+  own partial, and Delta accumulated from the rescaled partials.
 The rank-local K/V buffers are materialised once before timing (in the real
 system that is the per-step all-to-all, outside this path).
 
@@ -40,6 +43,9 @@ ENTRY_KERNELS = {
     "splitkv_plan": ["chunk_cost_kernel", "lpt_kernel"],
     "splitkv_attn_fwd": ["block_range_kernel", "attn_fwd_bf16_kernel"],
     "splitkv_lse_merge": ["lse_merge_kernel"],
+    "splitkv_lse_reduce": ["lse_reduce_kernel"],
+    "splitkv_lse_rescale": ["lse_rescale_kernel"],
+    "splitkv_delta": ["delta_rows_kernel"],
     "splitkv_attn_bwd": ["block_range_kernel", "bwd_prep_kernel", "chunk_range_kernel",
                          "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"],
 }
@@ -135,6 +141,11 @@ def parse():
     ap.add_argument("--own-blocks", action="store_true",
                     help="whole mask: also the own-block partial of every block (its B "
                          "block keys), merged with the P context partials and in the backward")
+    ap.add_argument("--merge-form", choices=("merged", "per-rank"), default="merged",
+                    help="merged: one LSE-merge kernel over the P partials and Delta from the "
+                         "merged output; per-rank: the form each rank applies when the partials "
+                         "sit on different devices (LSE reduction, each rank rescales its own "
+                         "partial, Delta accumulated from the rescaled partials)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -213,6 +224,7 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
+    per_rank = args.merge_form == "per-rank"
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     n_ev = 5
 
@@ -230,11 +242,20 @@ def main():
             binding.splitkv_attn_fwd(bs, ba, w.B, bcs, blen, q, kb, vb,
                                      out=(o_parts[w.P], l_parts[w.P]), workspace=ws)
         mark(2)
-        binding.splitkv_lse_merge(o_parts, l_parts, out=(o, lse))
+        if per_rank:
+            binding.splitkv_lse_reduce(l_parts, out=lse)
+            for p in range(n_parts):
+                binding.splitkv_lse_rescale(o_parts[p], l_parts[p], lse, out=o_parts[p])
+        else:
+            binding.splitkv_lse_merge(o_parts, l_parts, out=(o, lse))
         mark(3)
         dq.zero_()
+        if per_rank:
+            for p in range(n_parts):
+                binding.splitkv_delta(o_parts[p], do, delta=delta, accumulate=p > 0)
         for p, (cs, k, v) in enumerate(locs):
-            binding.splitkv_attn_bwd(sd, ad, w.B, cs, w.m, q, k, v, o if p == 0 else None, do,
+            binding.splitkv_attn_bwd(sd, ad, w.B, cs, w.m, q, k, v,
+                                     o if p == 0 and not per_rank else None, do,
                                      lse, dq, delta=delta, out=(dks[p], dvs[p]), workspace=ws)
         if args.own_blocks:
             binding.splitkv_attn_bwd(bs, ba, w.B, bcs, blen, q, kb, vb, None, do, lse, dq,
@@ -271,7 +292,10 @@ def main():
     bwd_tflops = bwd_flops / (phase[3] * 1e-3) / 1e12
     e_in = 2 if tdt == torch.bfloat16 else 4
     rows = Q * hq
-    merge_bytes = n_parts * rows * (d * e_in + 4) + rows * (d * e_in + 4)
+    if per_rank:   # LSE reduction, then each partial read and written once (in place)
+        merge_bytes = n_parts * rows * 4 + rows * 4 + n_parts * rows * (2 * d * e_in + 8)
+    else:
+        merge_bytes = n_parts * rows * (d * e_in + 4) + rows * (d * e_in + 4)
     merge_gbs = merge_bytes / (phase[2] * 1e-3) / 1e9
     dominant = "bwd" if phase[3] >= phase[1] else "fwd"
     ach = bwd_tflops if dominant == "bwd" else fwd_tflops
@@ -306,6 +330,7 @@ def main():
                      "blocks)" if args.own_blocks else
                      "plan + fwd(all ranks) + merge + bwd(all ranks)"),
             "live_pairs_per_head": pairs,
+            "merge_form": args.merge_form,
         },
         "fwd_tflops": round(fwd_tflops, 2),
         "bwd_tflops": round(bwd_tflops, 2),

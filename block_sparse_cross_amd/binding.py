@@ -30,7 +30,8 @@ SPLITKV_OP_PLAN, SPLITKV_OP_FWD, SPLITKV_OP_BWD, SPLITKV_OP_MERGE = 0, 1, 2, 3
 SPLITKV_BASELINE_NO_BALANCE, SPLITKV_BASELINE_ZIGZAG = 0, 1
 
 EXPORTED = ("splitkv_workspace_bytes", "splitkv_plan", "splitkv_plan_baseline",
-            "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_attn_bwd", "splitkv_status_str")
+            "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
+            "splitkv_delta", "splitkv_attn_bwd", "splitkv_status_str")
 
 
 class SplitKVError(RuntimeError):
@@ -81,6 +82,14 @@ def lib() -> ctypes.CDLL:
         L.splitkv_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp,
                                         ctypes.c_int, vp, vp, ctypes.c_int, vp, vp]
         L.splitkv_lse_merge.restype = ctypes.c_int
+        L.splitkv_lse_reduce.argtypes = [ctypes.c_int32, ctypes.c_int64, vp, vp, vp]
+        L.splitkv_lse_reduce.restype = ctypes.c_int
+        L.splitkv_lse_rescale.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int, vp, vp,
+                                          vp, ctypes.c_int, vp]
+        L.splitkv_lse_rescale.restype = ctypes.c_int
+        L.splitkv_delta.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int, vp,
+                                    ctypes.c_int, vp, ctypes.c_int, vp]
+        L.splitkv_delta.restype = ctypes.c_int
         L.splitkv_attn_bwd.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.splitkv_attn_bwd.restype = ctypes.c_int
         L.splitkv_status_str.argtypes = [ctypes.c_int]
@@ -283,6 +292,60 @@ def splitkv_lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
         int(P), int(rows), int(d), _ptr(o_parts), _dtype_code(o_parts.dtype), _ptr(lse_parts),
         _ptr(o), _dtype_code(o.dtype), _ptr(lse), _stream(stream)))
     return o, lse
+
+
+def splitkv_lse_reduce(lse_parts: torch.Tensor, out: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """LSE half of Eq. 4: lse_parts fp32 [P, rows...] -> lse fp32 [rows...]."""
+    if lse_parts.dtype != torch.float32 or lse_parts.dim() < 2:
+        raise ValueError("lse_parts must be fp32 [P, rows...]")
+    P, rows = lse_parts.shape[0], lse_parts[0].numel()
+    if out is None:
+        out = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=lse_parts.device)
+    if out.numel() != rows or out.dtype != torch.float32:
+        raise ValueError("output shape disagrees")
+    _check("splitkv_lse_reduce", lib().splitkv_lse_reduce(int(P), int(rows), _ptr(lse_parts),
+                                                          _ptr(out), _stream(stream)))
+    return out
+
+
+def splitkv_lse_rescale(o_part: torch.Tensor, lse_part: torch.Tensor, lse: torch.Tensor,
+                        out_dtype: Optional[torch.dtype] = None,
+                        out: Optional[torch.Tensor] = None,
+                        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """One rank's rescaled partial exp(lse_part - lse) * o_part (rows..., d)."""
+    d = o_part.shape[-1]
+    rows = lse_part.numel()
+    if o_part.numel() != rows * d or lse.numel() != rows or \
+            lse_part.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("partial, its lse and the reduced lse disagree")
+    if out is None:
+        out_dtype = o_part.dtype if out_dtype is None else out_dtype
+        out = torch.empty(o_part.shape, dtype=out_dtype, device=o_part.device)
+    if out.numel() != rows * d:
+        raise ValueError("output shape disagrees")
+    _check("splitkv_lse_rescale", lib().splitkv_lse_rescale(
+        int(rows), int(d), _ptr(o_part), _dtype_code(o_part.dtype), _ptr(lse_part), _ptr(lse),
+        _ptr(out), _dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def splitkv_delta(o: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tensor] = None,
+                  accumulate: bool = False,
+                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Delta = <dout, o> per row of the last dimension (+= with accumulate)."""
+    d = o.shape[-1]
+    if dout.shape != o.shape:
+        raise ValueError("o and dout disagree")
+    rows = o.numel() // d
+    if delta is None:
+        delta = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
+    if delta.numel() != rows or delta.dtype != torch.float32:
+        raise ValueError("delta shape disagrees")
+    _check("splitkv_delta", lib().splitkv_delta(
+        int(rows), int(d), _ptr(o), _dtype_code(o.dtype), _ptr(dout), _dtype_code(dout.dtype),
+        _ptr(delta), int(bool(accumulate)), _stream(stream)))
+    return delta
 
 
 def splitkv_attn_bwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v, o, dout, lse,

@@ -188,6 +188,46 @@ int splitkv_lse_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts, i
                                  static_cast<hipStream_t>(stream)));
 }
 
+int splitkv_lse_reduce(int32_t P, int64_t rows, const float* lse_parts, float* lse,
+                       void* stream) {
+  if (P < 1 || rows < 0) return SPLITKV_ERR_INVALID_ARG;
+  if (rows == 0) return SPLITKV_OK;
+  if (lse_parts == nullptr || lse == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if ((rows + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  return hip_status(launch_lse_reduce(P, rows, lse_parts, lse, static_cast<hipStream_t>(stream)));
+}
+
+int splitkv_lse_rescale(int64_t rows, int32_t d, const void* o_part, int in_dtype,
+                        const float* lse_part, const float* lse, void* o_bar, int out_dtype,
+                        void* stream) {
+  if (rows < 0 || d < 8 || d % 8 != 0) return SPLITKV_ERR_INVALID_ARG;
+  if ((in_dtype != SPLITKV_BF16 && in_dtype != SPLITKV_FP32) ||
+      (out_dtype != SPLITKV_BF16 && out_dtype != SPLITKV_FP32))
+    return SPLITKV_ERR_UNSUPPORTED;
+  if (rows == 0) return SPLITKV_OK;
+  if (o_part == nullptr || lse_part == nullptr || lse == nullptr || o_bar == nullptr)
+    return SPLITKV_ERR_INVALID_ARG;
+  // in place only when the element types agree
+  if (o_part == o_bar && in_dtype != out_dtype) return SPLITKV_ERR_INVALID_ARG;
+  if ((rows * (d / 8) + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  return hip_status(launch_lse_rescale(rows, d, o_part, in_dtype, lse_part, lse, o_bar,
+                                       out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+int splitkv_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const void* dout,
+                  int do_dtype, float* delta, int accumulate, void* stream) {
+  if (rows < 0 || d < 8 || d % 8 != 0 || d / 8 > 64 || ((d / 8) & (d / 8 - 1)) != 0)
+    return SPLITKV_ERR_INVALID_ARG;
+  if ((o_dtype != SPLITKV_BF16 && o_dtype != SPLITKV_FP32) ||
+      (do_dtype != SPLITKV_BF16 && do_dtype != SPLITKV_FP32))
+    return SPLITKV_ERR_UNSUPPORTED;
+  if (rows == 0) return SPLITKV_OK;
+  if (o == nullptr || dout == nullptr || delta == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if ((rows * (d / 8) + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  return hip_status(launch_delta(rows, d, o, o_dtype, dout, do_dtype, delta, accumulate != 0,
+                                 static_cast<hipStream_t>(stream)));
+}
+
 int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
                      const splitkv_local* loc, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, float* delta, float* dq,

@@ -58,6 +58,16 @@ hipError_t launch_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts,
                         const float* lse_parts, void* o, int out_dtype, float* lse,
                         hipStream_t stream);
 
+hipError_t launch_lse_reduce(int32_t P, int64_t rows, const float* lse_parts, float* lse,
+                             hipStream_t stream);
+
+hipError_t launch_lse_rescale(int64_t rows, int32_t d, const void* o_part, int in_dtype,
+                              const float* lse_part, const float* lse, void* o_bar,
+                              int out_dtype, hipStream_t stream);
+
+hipError_t launch_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const void* dout,
+                        int do_dtype, float* delta, int accumulate, hipStream_t stream);
+
 hipError_t launch_bwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
                       const int2* block_range, void* meta, void* chunk_range, const void* q,
                       const void* k, const void* v, const void* o, const void* dout,

@@ -104,6 +104,92 @@ lse_merge_kernel(int P, int64_t rows, int d, const Tin* __restrict__ o_parts,
   if (seg == 0) lse[row] = mx + __logf(wsum);
 }
 
+// Eq. 4 split into the two halves each rank applies when the partials sit on
+// different devices (Algorithm 1's MERGE after the LSE all-reduce). First the
+// LSE statistics: lse = log sum_p exp(lse_p), one thread per row, the P reads
+// of a row strided by `rows` so a wave's loads are coalesced.
+__global__ void __launch_bounds__(kMergeThreads)
+lse_reduce_kernel(int P, int64_t rows, const float* __restrict__ lse_parts,
+                  float* __restrict__ lse) {
+  const int64_t row = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int p = 0; p < P; ++p) mx = fmaxf(mx, lse_parts[(int64_t)p * rows + row]);
+  if (mx == -INFINITY) {
+    lse[row] = -INFINITY;
+    return;
+  }
+  float sum = 0.f;
+  for (int p = 0; p < P; ++p) sum += __expf(lse_parts[(int64_t)p * rows + row] - mx);
+  lse[row] = mx + __logf(sum);
+}
+
+// Then each rank's own partial: o_bar = exp(lse_p - lse) o_p, zero where the
+// partial is empty (lse_p = -inf). One thread per 8 consecutive elements.
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(kMergeThreads)
+lse_rescale_kernel(int64_t rows, int d, const Tin* __restrict__ o_part,
+                   const float* __restrict__ lse_part, const float* __restrict__ lse,
+                   Tout* __restrict__ o_bar) {
+  const int segs = d / 8;
+  const int64_t unit = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (unit >= rows * segs) return;
+  const int64_t row = unit / segs;
+  const float lp = lse_part[row];
+  const float w = lp == -INFINITY ? 0.f : __expf(lp - lse[row]);
+  float x[8];
+  Vec8<Tin>::load(o_part + unit * 8, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= w;
+  Vec8<Tout>::store(o_bar + unit * 8, x);
+}
+
+// Delta[r] (+)= <do[r], o[r]> over rows of d elements (the quantity Algorithm
+// 1's MERGE_BWD all-reduces; from a rank's rescaled partial it is that rank's
+// share). One thread per 8 elements; the d/8 threads of a row (a power of two
+// <= 64, so they share a wave) sum with lane exchanges.
+template <typename To, typename Td>
+__global__ void __launch_bounds__(kMergeThreads)
+delta_rows_kernel(int64_t rows, int d, const To* __restrict__ o, const Td* __restrict__ dout,
+                  float* __restrict__ delta, int accumulate) {
+  const int segs = d / 8;
+  const int64_t unit = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (unit >= rows * segs) return;
+  float x[8], y[8];
+  Vec8<To>::load(o + unit * 8, x);
+  Vec8<Td>::load(dout + unit * 8, y);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
+  for (int off = segs / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (unit % segs == 0) {
+    const int64_t row = unit / segs;
+    delta[row] = accumulate ? delta[row] + acc : acc;
+  }
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_rescale_t(int64_t rows, int32_t d, const void* o_part, const float* lse_part,
+                            const float* lse, void* o_bar, hipStream_t stream) {
+  const int64_t units = rows * (d / 8);
+  const int64_t grid = (units + kMergeThreads - 1) / kMergeThreads;
+  hipLaunchKernelGGL((lse_rescale_kernel<Tin, Tout>), dim3((unsigned)grid), dim3(kMergeThreads),
+                     0, stream, rows, d, static_cast<const Tin*>(o_part), lse_part, lse,
+                     static_cast<Tout*>(o_bar));
+  return hipGetLastError();
+}
+
+template <typename To, typename Td>
+hipError_t launch_delta_t(int64_t rows, int32_t d, const void* o, const void* dout, float* delta,
+                          int accumulate, hipStream_t stream) {
+  const int64_t units = rows * (d / 8);
+  const int64_t grid = (units + kMergeThreads - 1) / kMergeThreads;
+  hipLaunchKernelGGL((delta_rows_kernel<To, Td>), dim3((unsigned)grid), dim3(kMergeThreads), 0,
+                     stream, rows, d, static_cast<const To*>(o), static_cast<const Td*>(dout),
+                     delta, accumulate);
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tout>
 hipError_t launch_merge_t(int32_t P, int64_t rows, int32_t d, const void* o_parts,
                           const float* lse_parts, void* o, float* lse, hipStream_t stream) {
@@ -128,6 +214,40 @@ hipError_t launch_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts,
   if (in_dtype == SPLITKV_FP32 && out_dtype == SPLITKV_BF16)
     return launch_merge_t<float, bf16_t>(P, rows, d, o_parts, lse_parts, o, lse, stream);
   return launch_merge_t<float, float>(P, rows, d, o_parts, lse_parts, o, lse, stream);
+}
+
+hipError_t launch_lse_reduce(int32_t P, int64_t rows, const float* lse_parts, float* lse,
+                             hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t grid = (rows + kMergeThreads - 1) / kMergeThreads;
+  hipLaunchKernelGGL(lse_reduce_kernel, dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, P,
+                     rows, lse_parts, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_rescale(int64_t rows, int32_t d, const void* o_part, int in_dtype,
+                              const float* lse_part, const float* lse, void* o_bar,
+                              int out_dtype, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (in_dtype == SPLITKV_BF16 && out_dtype == SPLITKV_BF16)
+    return launch_rescale_t<bf16_t, bf16_t>(rows, d, o_part, lse_part, lse, o_bar, stream);
+  if (in_dtype == SPLITKV_BF16 && out_dtype == SPLITKV_FP32)
+    return launch_rescale_t<bf16_t, float>(rows, d, o_part, lse_part, lse, o_bar, stream);
+  if (in_dtype == SPLITKV_FP32 && out_dtype == SPLITKV_BF16)
+    return launch_rescale_t<float, bf16_t>(rows, d, o_part, lse_part, lse, o_bar, stream);
+  return launch_rescale_t<float, float>(rows, d, o_part, lse_part, lse, o_bar, stream);
+}
+
+hipError_t launch_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const void* dout,
+                        int do_dtype, float* delta, int accumulate, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (o_dtype == SPLITKV_BF16 && do_dtype == SPLITKV_BF16)
+    return launch_delta_t<bf16_t, bf16_t>(rows, d, o, dout, delta, accumulate, stream);
+  if (o_dtype == SPLITKV_BF16 && do_dtype == SPLITKV_FP32)
+    return launch_delta_t<bf16_t, float>(rows, d, o, dout, delta, accumulate, stream);
+  if (o_dtype == SPLITKV_FP32 && do_dtype == SPLITKV_BF16)
+    return launch_delta_t<float, bf16_t>(rows, d, o, dout, delta, accumulate, stream);
+  return launch_delta_t<float, float>(rows, d, o, dout, delta, accumulate, stream);
 }
 
 }  // namespace splitkv

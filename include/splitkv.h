@@ -147,6 +147,33 @@ int splitkv_attn_fwd(const splitkv_anchors* an, const splitkv_heads* hd,
 int splitkv_lse_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts, int in_dtype,
                       const float* lse_parts, void* o, int out_dtype, float* lse, void* stream);
 
+/* Eq. 4 in the two halves each rank applies when the partials sit on
+ * different devices (Algorithm 1, MERGE after the all-reduce of the LSE
+ * statistics). Rows = Q*hq.
+ * splitkv_lse_reduce: lse = log sum_p exp(lse_p) per row; all partials empty
+ *   gives -inf. lse_parts fp32 [P][rows], lse fp32 [rows]. P >= 1.
+ * splitkv_lse_rescale: o_bar = exp(lse_p - lse) o_p for one rank's partial
+ *   (o_bar = 0 where lse_p = -inf); summed over the ranks, the o_bar are the
+ *   merged output of splitkv_lse_merge. o_part [rows][d] in in_dtype, lse_part
+ *   and lse fp32 [rows], o_bar [rows][d] in out_dtype; d % 8 == 0. lse must be
+ *   the reduction of the partials (so lse >= lse_p). o_bar may alias o_part
+ *   when the two dtypes agree (in place). */
+int splitkv_lse_reduce(int32_t P, int64_t rows, const float* lse_parts, float* lse,
+                       void* stream);
+int splitkv_lse_rescale(int64_t rows, int32_t d, const void* o_part, int in_dtype,
+                        const float* lse_part, const float* lse, void* o_bar, int out_dtype,
+                        void* stream);
+
+/* Delta of Algorithm 1's MERGE_BWD: delta[r] = <do[r], o[r]> (accumulate == 0)
+ * or delta[r] += <do[r], o[r]> (accumulate != 0), over rows of d elements.
+ * With a rank's rescaled partial o_bar_p as `o` this is the rank's share of
+ * Delta, and accumulating over the ranks is the all-reduce; the result can be
+ * handed to splitkv_attn_bwd with o == NULL. o [rows][d] in o_dtype, dout
+ * [rows][d] in do_dtype, delta fp32 [rows]. d % 8 == 0 and d/8 a power of two
+ * <= 64. */
+int splitkv_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const void* dout,
+                  int do_dtype, float* delta, int accumulate, void* stream);
+
 /* Backward of the local partial, Algorithm 1 (MERGE_BWD then AttnBwd_p), with
  * the GLOBAL (merged) lse and Delta = <do, o>:
  *   P = exp(scale <q, k_x> - lse[r,h]);  dv_x += P do;  ds = P (<do, v_x> - Delta[r,h]);
