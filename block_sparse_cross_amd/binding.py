@@ -31,7 +31,9 @@ SPLITKV_BASELINE_NO_BALANCE, SPLITKV_BASELINE_ZIGZAG = 0, 1
 
 EXPORTED = ("splitkv_workspace_bytes", "splitkv_plan", "splitkv_plan_baseline",
             "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
-            "splitkv_delta", "splitkv_attn_bwd", "splitkv_status_str")
+            "splitkv_delta", "splitkv_gemm", "splitkv_attn_bwd", "splitkv_status_str")
+
+SPLITKV_GEMM_NT, SPLITKV_GEMM_NN, SPLITKV_GEMM_TN = 0, 1, 2
 
 
 class SplitKVError(RuntimeError):
@@ -90,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.splitkv_delta.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int, vp,
                                     ctypes.c_int, vp, ctypes.c_int, vp]
         L.splitkv_delta.restype = ctypes.c_int
+        L.splitkv_gemm.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
+        L.splitkv_gemm.restype = ctypes.c_int
         L.splitkv_attn_bwd.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.splitkv_attn_bwd.restype = ctypes.c_int
         L.splitkv_status_str.argtypes = [ctypes.c_int]
@@ -346,6 +351,37 @@ def splitkv_delta(o: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Ten
         int(rows), int(d), _ptr(o), _dtype_code(o.dtype), _ptr(dout), _dtype_code(dout.dtype),
         _ptr(delta), int(bool(accumulate)), _stream(stream)))
     return delta
+
+
+def splitkv_gemm(layout: int, A: torch.Tensor, B: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 out_dtype: torch.dtype = torch.float32, bias: Optional[torch.Tensor] = None,
+                 accumulate: bool = False,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """bf16 product: NT A[M,K] B[N,K]^T, NN A[M,K] B[K,N], TN A[K,M]^T B[K,N] (+ bias, += C)."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16 or A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-d bf16")
+    if layout == SPLITKV_GEMM_NT:
+        (M, K), (N, K2) = A.shape, B.shape
+    elif layout == SPLITKV_GEMM_NN:
+        (M, K), (K2, N) = A.shape, B.shape
+    elif layout == SPLITKV_GEMM_TN:
+        (K, M), (K2, N) = A.shape, B.shape
+    else:
+        raise ValueError("unknown layout")
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs out")
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if out.shape != (M, N):
+        raise ValueError("output shape disagrees")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N):
+        raise ValueError("bias must be fp32 [N]")
+    _check("splitkv_gemm", lib().splitkv_gemm(int(layout), int(M), int(N), int(K), _ptr(A), _ptr(B),
+                                              _ptr(out), _dtype_code(out.dtype), _ptr(bias),
+                                              int(bool(accumulate)), _stream(stream)))
+    return out
 
 
 def splitkv_attn_bwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v, o, dout, lse,

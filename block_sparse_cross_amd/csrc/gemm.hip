@@ -1,0 +1,401 @@
+// Dense bf16 matrix products for the projections around the attention of one
+// draft layer (QProj, KeyValueProj, OProj and their backward; Algorithm 1 of
+// "Split-KV: Efficient Context Parallelism for Training Diffusion Drafters").
+// With OProj linear, each rank's rescaled partial is projected on its own and
+// the results summed with the bias added once (Eq. 5): the accumulate flag and
+// the optional bias of the epilogue express exactly that.
+//
+//   C[M][N] (+)= op(A) op(B) (+ bias)    fp32 accumulation, C in fp32 or bf16
+//   NT: A [M][K], B [N][K]  (x W^T: forward projections)
+//   NN: A [M][K], B [K][N]  (dY W: gradient of a projection's input)
+//   TN: A [K][M], B [K][N]  (dY^T X: gradient of a projection's weight)
+//
+// Work decomposition. A workgroup of 8 waves (two per SIMD) computes a
+// 256 x 256 tile of C; wave (wm, wn) owns 64 rows x 128 columns as 2 x 4
+// blocks of the 32x32x16 bf16 matrix-core product (128 fp32 accumulators per
+// lane). K advances 32 at a time through a ring of 4 LDS stages (32 KB each):
+// the A and B slices are copied global -> LDS with asynchronous 16-byte loads
+// three steps ahead of their use, each step waits only for its own slice
+// (vmcnt leaves the later slices in flight) and passes one barrier.
+//
+// Operand tiles in LDS. A slice whose rows run along K ("k-major": A in NT and
+// NN, B in NT) is stored [256][32], 64-byte rows, and read 8 k-values per
+// lane with one 16-byte LDS read; its 16-byte slots are XOR-permuted by
+// (row / 4) mod 4, so the 16 rows a quarter-wave reads land on 16 distinct
+// bank groups. A slice whose rows run along M or N ("mn-major": B in NN and
+// TN, A in TN) is stored [32][256] and read transposed (ds_read_b64_tr_b16,
+// 4 k-values per read, two per fragment); its slots are permuted by
+// 4 (row mod 4), so the 4 rows of a transposing read hit distinct banks.
+//
+// Edges. M and N need not be multiples of the tile: rows and columns past the
+// end are read from the last valid row or 8-column group (finite filler) and
+// never stored. The last K step zero-fills the slots past K (K is a multiple
+// of 8, so a 16-byte slot is wholly inside or outside), so they add nothing.
+// The grid is ordered so that each XCD (workgroups are dealt round-robin over
+// the 8 XCDs) takes a contiguous run of tiles, grouped 8 tile-rows at a time,
+// so tiles that share A rows or B columns meet in the same L2.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace splitkv {
+
+namespace {
+
+constexpr int kWM = 4;                      // waves along M (2 along N): 8 waves, two per SIMD
+constexpr int kGemmThreads = 64 * 2 * kWM;
+constexpr int kMI = 256 / kWM / 32;         // 32-row blocks per wave (2)
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kStages = 2;                  // LDS ring of operand slices
+constexpr int kNSK = kBK / 8;               // 16-byte slots per k-major row
+constexpr int kKS = kBK / 16;               // 16-deep product steps per slice
+constexpr int kTileElems = kBM * kBK;       // both operand slices hold 256 x kBK elements
+constexpr int kPasses = kTileElems / 8 / kGemmThreads;  // 16-byte copies per thread per slice
+constexpr int kCopiesPerStage = 2 * kPasses;
+constexpr int kGroupRows = 8;               // tile-rows per group of the grid order
+constexpr int kXcds = 8;
+
+// k-major slice [256][kBK]: kNSK slots per row; 16 consecutive rows span
+// 16 kNSK slots, and slot ^ ((row / (16 / kNSK)) mod kNSK) puts the same
+// logical slot of those rows on 16 distinct bank groups
+__device__ __forceinline__ int kmaj_swz(int row) { return (row / (16 / kNSK)) & (kNSK - 1); }
+// mn-major slice [kBK][256]: 32 slots per row, slot ^ 4 (row & 3)
+__device__ __forceinline__ int mnmaj_swz(int row) { return 4 * (row & 3); }
+
+// Copy one k-major slice: rows r0 .. r0 + 255 (clamped to < R) of a row-major
+// [R][ld] matrix, columns k0 .. k0 + kBK - 1 (slots at or past K zero-filled
+// when TAIL). Thread t, pass p handles LDS slot u = kGemmThreads p + t: row
+// u / kNSK, physical slot u % kNSK, holding logical slot phys ^ swz(row).
+template <bool TAIL>
+__device__ __forceinline__ void copy_kmajor(const bf16_t* __restrict__ src, int64_t R, int64_t ld,
+                                            int64_t r0, int64_t k0, int64_t K, bf16_t* tile,
+                                            int tid) {
+  const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int u = pass * kGemmThreads + tid;
+    const int row = u / kNSK, phys = u % kNSK;
+    const int lslot = phys ^ kmaj_swz(row);
+    const int64_t r = min(r0 + row, R - 1);
+    const int64_t k = k0 + 8 * lslot;
+    bf16_t* dst = tile + pass * kGemmThreads * 8 + lds_off;
+    if (!TAIL || k < K) {
+      async_copy16(src + r * ld + k, dst);
+    } else {
+      *reinterpret_cast<u32x4*>(tile + (int64_t)u * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Copy one mn-major slice: rows k0 .. k0 + kBK - 1 (rows at or past K zero-filled
+// when TAIL) of a row-major [K][C] matrix, columns c0 .. c0 + 255 (8-column
+// groups past C read from the last group). LDS slot u: row u / 32, physical
+// slot u % 32.
+template <bool TAIL>
+__device__ __forceinline__ void copy_mnmajor(const bf16_t* __restrict__ src, int64_t C, int64_t c0,
+                                             int64_t k0, int64_t K, bf16_t* tile, int tid) {
+  const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int u = pass * kGemmThreads + tid;
+    const int row = u >> 5, phys = u & 31;
+    const int lslot = phys ^ mnmaj_swz(row);
+    const int64_t c = min(c0 + 8 * lslot, C - 8);
+    const int64_t k = k0 + row;
+    bf16_t* dst = tile + pass * kGemmThreads * 8 + lds_off;
+    if (!TAIL || k < K) {
+      async_copy16(src + k * C + c, dst);
+    } else {
+      *reinterpret_cast<u32x4*>(tile + (int64_t)u * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Fragment of 32 rows (r0 ..) x 16 k (step ks) from a k-major slice: lane l
+// holds row r0 + (l mod 32), k-values 16 ks + 8 (l / 32) .. + 8.
+__device__ __forceinline__ bf16x8 frag_kmajor(const bf16_t* tile, int r0, int ks, int lane) {
+  const int row = r0 + (lane & 31);
+  const int lslot = 2 * ks + (lane >> 5);
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(tile + row * kBK + ((lslot ^ kmaj_swz(row)) * 8)));
+}
+
+// The same fragment from an mn-major slice (columns c0 .. c0 + 31 of rows =
+// k): two transposing reads of 4 k-values. In 16-lane group g (lanes 16 g ..),
+// lane s addresses k-row kb + s / 4 and columns cb + 4 (s mod 4), where
+// kb = 16 ks + 8 (g / 2) (+ 4 for the second read) and cb = c0 + 16 (g mod 2).
+__device__ __forceinline__ bf16x8 frag_mnmajor(const bf16_t* tile, int c0, int ks, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int kb = 16 * ks + 8 * (g >> 1) + (s >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (s & 3);
+  const int slot = col >> 3, within = col & 7;
+  const int row0 = kb, row1 = kb + 4;
+  const u32x2 lo = read_tr4(tile + row0 * kBN + (((slot ^ mnmaj_swz(row0)) * 8) + within));
+  const u32x2 hi = read_tr4(tile + row1 * kBN + (((slot ^ mnmaj_swz(row1)) * 8) + within));
+  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+template <int LAYOUT>
+struct Layout {
+  static constexpr bool A_KMAJOR = LAYOUT != SPLITKV_GEMM_TN;
+  static constexpr bool B_KMAJOR = LAYOUT == SPLITKV_GEMM_NT;
+};
+
+template <int LAYOUT>
+__device__ __forceinline__ bf16x8 frag_a(const bf16_t* ta, int wm, int i, int ks, int lane) {
+  return Layout<LAYOUT>::A_KMAJOR ? frag_kmajor(ta, wm * (kMI * 32) + 32 * i, ks, lane)
+                                  : frag_mnmajor(ta, wm * (kMI * 32) + 32 * i, ks, lane);
+}
+template <int LAYOUT>
+__device__ __forceinline__ bf16x8 frag_b(const bf16_t* tb, int wn, int j, int ks, int lane) {
+  return Layout<LAYOUT>::B_KMAJOR ? frag_kmajor(tb, wn * 128 + 32 * j, ks, lane)
+                                  : frag_mnmajor(tb, wn * 128 + 32 * j, ks, lane);
+}
+
+template <int LAYOUT, bool TAIL>
+__device__ __forceinline__ void copy_step(const bf16_t* A, const bf16_t* B, int64_t M, int64_t N,
+                                          int64_t K, int64_t m0, int64_t n0, int64_t k0,
+                                          bf16_t* ta, bf16_t* tb, int tid) {
+  if constexpr (Layout<LAYOUT>::A_KMAJOR)
+    copy_kmajor<TAIL>(A, M, K, m0, k0, K, ta, tid);
+  else
+    copy_mnmajor<TAIL>(A, M, m0, k0, K, ta, tid);
+  if constexpr (Layout<LAYOUT>::B_KMAJOR)
+    copy_kmajor<TAIL>(B, N, K, n0, k0, K, tb, tid);
+  else
+    copy_mnmajor<TAIL>(B, N, n0, k0, K, tb, tid);
+}
+
+// Per-lane byte offsets of a thread's copies within a full slice (k0 = 0),
+// computed once per workgroup; a step adds the uniform base of its slice.
+// k-major: row r0 + row (clamped), logical slot lslot: (r * ld + 8 lslot) * 2.
+__device__ __forceinline__ void kmajor_offsets(int64_t R, int64_t ld, int64_t r0, int tid,
+                                               uint32_t* off) {
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int u = pass * kGemmThreads + tid;
+    const int row = u / kNSK, lslot = (u % kNSK) ^ kmaj_swz(row);
+    const int64_t r = min(r0 + row, R - 1);
+    off[pass] = (uint32_t)((r * ld + 8 * lslot) * 2);
+  }
+}
+// mn-major: k-row row, column c0 + 8 lslot (clamped): (row * C + c) * 2.
+__device__ __forceinline__ void mnmajor_offsets(int64_t C, int64_t c0, int tid, uint32_t* off) {
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int u = pass * kGemmThreads + tid;
+    const int row = u >> 5, lslot = (u & 31) ^ mnmaj_swz(row);
+    const int64_t c = min(c0 + 8 * lslot, C - 8);
+    off[pass] = (uint32_t)((row * C + c) * 2);
+  }
+}
+
+// A full slice from precomputed offsets: `base` is the slice's first element
+// (uniform). The offsets are made opaque so that the compiler keeps one 32-bit
+// register per copy instead of hoisting a 64-bit address per copy and slice.
+__device__ __forceinline__ void copy_offsets(const bf16_t* base, const uint32_t* off, bf16_t* tile,
+                                             int tid) {
+  const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
+  const char* b = reinterpret_cast<const char*>(base);
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    uint32_t o = off[pass];
+    asm volatile("" : "+v"(o));
+    async_copy16(b + o, tile + pass * kGemmThreads * 8 + lds_off);
+  }
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void issue_stage_fast(const bf16_t* A, const bf16_t* B, int64_t M,
+                                                 int64_t N, int kt, const uint32_t* aoff,
+                                                 const uint32_t* boff, bf16_t* ta, bf16_t* tb,
+                                                 int tid) {
+  const int64_t k0 = (int64_t)kt * kBK;
+  copy_offsets(Layout<LAYOUT>::A_KMAJOR ? A + k0 : A + k0 * M, aoff, ta, tid);
+  copy_offsets(Layout<LAYOUT>::B_KMAJOR ? B + k0 : B + k0 * N, boff, tb, tid);
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void issue_stage(const bf16_t* A, const bf16_t* B, int64_t M, int64_t N,
+                                            int64_t K, int64_t m0, int64_t n0, int kt,
+                                            bf16_t* ta, bf16_t* tb, int tid) {
+  const int64_t k0 = (int64_t)kt * kBK;
+  if (k0 + kBK > K)
+    copy_step<LAYOUT, true>(A, B, M, N, K, m0, n0, k0, ta, tb, tid);
+  else
+    copy_step<LAYOUT, false>(A, B, M, N, K, m0, n0, k0, ta, tb, tid);
+}
+
+// s_waitcnt with vmcnt = N (6 bits: low 4 at bit 0, high 2 at bit 14) and the
+// other counters left free.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int LAYOUT, typename Tc>
+__global__ void __launch_bounds__(kGemmThreads, 1)
+gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
+                 const bf16_t* __restrict__ B, Tc* __restrict__ Cm,
+                 const float* __restrict__ bias, int accumulate) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kStages][2][kTileElems];  // [stage][A, B]
+
+  // grid order: each XCD a contiguous run of tiles, grouped kGroupRows tile-rows
+  const int n_tm = (int)((M + kBM - 1) / kBM), n_tn = (int)((N + kBN - 1) / kBN);
+  const int nb = n_tm * n_tn;
+  int bid = blockIdx.x;
+  if (nb % kXcds == 0) bid = (bid % kXcds) * (nb / kXcds) + bid / kXcds;
+  const int group = bid / (kGroupRows * n_tn);
+  const int first = group * kGroupRows;
+  const int rows_in_group = min(n_tm - first, kGroupRows);
+  const int tm = first + (bid % (kGroupRows * n_tn)) % rows_in_group;
+  const int tn = (bid % (kGroupRows * n_tn)) / rows_in_group;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16 acc[kMI][4];
+#pragma unroll
+  for (int i = 0; i < kMI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int n_k = (int)((K + kBK - 1) / kBK);
+  const int n_full = (int)(K / kBK);  // slices wholly inside K
+  uint32_t aoff[kPasses], boff[kPasses];
+  if constexpr (Layout<LAYOUT>::A_KMAJOR)
+    kmajor_offsets(M, K, m0, tid, aoff);
+  else
+    mnmajor_offsets(M, m0, tid, aoff);
+  if constexpr (Layout<LAYOUT>::B_KMAJOR)
+    kmajor_offsets(N, K, n0, tid, boff);
+  else
+    mnmajor_offsets(N, n0, tid, boff);
+  // prologue: slices 0 .. kStages - 2 in flight
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (s < n_full)
+      issue_stage_fast<LAYOUT>(A, B, M, N, s, aoff, boff, lds[s][0], lds[s][1], tid);
+    else if (s < n_k)
+      issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, s, lds[s][0], lds[s][1], tid);
+  }
+
+  for (int kt = 0; kt < n_k; ++kt) {
+    // Slice kt has landed once at most the copies of the slices issued after
+    // it are outstanding (they complete in issue order); the last slice may
+    // also have zero-filled part of its tile through LDS writes.
+    // A ragged last slice issues fewer copies (some slots are zero-filled
+    // instead), so while it is among the later slices everything is awaited.
+    if constexpr (kStages == 2) {
+      wait_async();
+    } else {
+      static_assert(kStages == 4, "waits below are written for 2 or 4 stages");
+      const int later = min(kStages - 2, n_k - 1 - kt);
+      const bool ragged_later = (K % kBK != 0) && kt + later == n_k - 1;
+      if (ragged_later)
+        wait_async();
+      else if (later >= 2)
+        wait_vm<2 * kCopiesPerStage>();
+      else if (later == 1)
+        wait_vm<kCopiesPerStage>();
+      else
+        wait_async();
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // slice kt visible to all; every wave is done with kt - 1
+    asm volatile("" ::: "memory");
+    if (kt + kStages - 1 < n_full) {
+      const int s = (kt + kStages - 1) % kStages;
+      issue_stage_fast<LAYOUT>(A, B, M, N, kt + kStages - 1, aoff, boff, lds[s][0], lds[s][1],
+                               tid);
+    } else if (kt + kStages - 1 < n_k) {
+      const int s = (kt + kStages - 1) % kStages;
+      issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, kt + kStages - 1, lds[s][0], lds[s][1], tid);
+    }
+    const bf16_t* ta = lds[kt % kStages][0];
+    const bf16_t* tb = lds[kt % kStages][1];
+    // kKS 16-deep steps; the fragments of step ks + 1 are read while the
+    // products of step ks run (fenced pieces keep the reads early).
+    bf16x8 a[2][kMI], b[2][4];
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) a[0][i] = frag_a<LAYOUT>(ta, wm, i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[0][j] = frag_b<LAYOUT>(tb, wn, j, 0, lane);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const int c = ks & 1, nx = c ^ 1;
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) {
+        if (i == 0 && ks + 1 < kKS) {
+#pragma unroll
+          for (int i2 = 0; i2 < kMI; ++i2) a[nx][i2] = frag_a<LAYOUT>(ta, wm, i2, ks + 1, lane);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b[nx][j] = frag_b<LAYOUT>(tb, wn, j, ks + 1, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // Epilogue: lane l of block (i, j) holds column 32 j + (l mod 32) of rows
+  // 32 i + 8 (e / 4) + 4 (l / 32) + (e mod 4), e = 0 .. 15.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
+    if (n >= N) continue;
+    const float bn = bias != nullptr ? bias[n] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm * (kMI * 32) + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (m < M) {
+          Tc* p = Cm + m * N + n;
+          float x = acc[i][j][e] + bn;
+          if (accumulate) x += Elem<Tc>::load(p);
+          Elem<Tc>::store(p, x);
+        }
+      }
+    }
+  }
+}
+
+template <int LAYOUT>
+hipError_t launch_gemm_l(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
+                         int c_dtype, const float* bias, int accumulate, hipStream_t stream) {
+  const int64_t nb = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(B);
+  if (c_dtype == SPLITKV_FP32)
+    hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, float>), dim3((unsigned)nb), dim3(kGemmThreads),
+                       0, stream, M, N, K, a, b, static_cast<float*>(C), bias, accumulate);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, bf16_t>), dim3((unsigned)nb),
+                       dim3(kGemmThreads), 0, stream, M, N, K, a, b, static_cast<bf16_t*>(C),
+                       bias, accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                       void* C, int c_dtype, const float* bias, int accumulate,
+                       hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  switch (layout) {
+    case SPLITKV_GEMM_NT:
+      return launch_gemm_l<SPLITKV_GEMM_NT>(M, N, K, A, B, C, c_dtype, bias, accumulate, stream);
+    case SPLITKV_GEMM_NN:
+      return launch_gemm_l<SPLITKV_GEMM_NN>(M, N, K, A, B, C, c_dtype, bias, accumulate, stream);
+    default:
+      return launch_gemm_l<SPLITKV_GEMM_TN>(M, N, K, A, B, C, c_dtype, bias, accumulate, stream);
+  }
+}
+
+}  // namespace splitkv

@@ -68,6 +68,10 @@ hipError_t launch_lse_rescale(int64_t rows, int32_t d, const void* o_part, int i
 hipError_t launch_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const void* dout,
                         int do_dtype, float* delta, int accumulate, hipStream_t stream);
 
+hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                       void* C, int c_dtype, const float* bias, int accumulate,
+                       hipStream_t stream);
+
 hipError_t launch_bwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
                       const int2* block_range, void* meta, void* chunk_range, const void* q,
                       const void* k, const void* v, const void* o, const void* dout,

@@ -30,6 +30,9 @@ import numpy as np
 
 # tensor ids of the keyed random streams
 T_ANCHORS, T_Q, T_K, T_V, T_DO, T_O, T_LSE, T_OPART, T_LPART, T_KB, T_VB = range(11)
+# draft-layer tensors around the attention (hidden states, context features,
+# projection weights, output bias, output gradient) and plain test matrices
+T_X, T_CTX, T_WQ, T_WK, T_WV, T_WO, T_BO, T_DY, T_MAT = range(11, 20)
 
 KV_UNIT = 256  # rows of k/v per keyed random stream
 
@@ -260,6 +263,25 @@ def random_tiny_anchors(g: np.random.Generator, n_samples: int, L: int, A: int,
         s_all.append(np.full(A, u * L, dtype=np.int64))
         a_all.append(a)
     return np.concatenate(s_all), np.concatenate(a_all)
+
+
+def gen_matrix(rows: int, cols: int, seed: int, tensor_id: int, scale: float = 1.0,
+               dtype: str = "bf16", first_row: int = 0) -> np.ndarray:
+    """Rows [first_row, first_row + rows) of a seeded [*, cols] N(0,1)*scale matrix,
+    drawn in units of 256 rows so that any row range regenerates on its own."""
+    out = []
+    r = first_row
+    end = first_row + rows
+    while r < end:
+        unit = r // KV_UNIT
+        u0 = unit * KV_UNIT
+        block = normal_values(rng(seed, tensor_id, unit), (KV_UNIT, cols), scale, dtype)
+        take = min(end, u0 + KV_UNIT) - r
+        out.append(block[r - u0:r - u0 + take])
+        r += take
+    if not out:
+        return normal_values(rng(seed, tensor_id, 0), (0, cols), scale, dtype)
+    return np.ascontiguousarray(np.concatenate(out, axis=0))
 
 
 def list_workloads() -> List[str]:

@@ -174,6 +174,27 @@ int splitkv_lse_rescale(int64_t rows, int32_t d, const void* o_part, int in_dtyp
 int splitkv_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const void* dout,
                   int do_dtype, float* delta, int accumulate, void* stream);
 
+/* Dense projections around the attention of one draft layer (Algorithm 1:
+ * QProj, KeyValueProj, OProj and their gradients). bf16 operands, fp32
+ * accumulation:
+ *   C[M][N] = op(A) op(B) + bias     (accumulate == 0)
+ *   C[M][N] += op(A) op(B) + bias    (accumulate != 0)
+ *   SPLITKV_GEMM_NT: A [M][K], B [N][K], op(B) = B^T   (x W^T)
+ *   SPLITKV_GEMM_NN: A [M][K], B [K][N]                (dY W)
+ *   SPLITKV_GEMM_TN: A [K][M], B [K][N], op(A) = A^T   (dY^T X)
+ * All matrices dense row-major; C in c_dtype (fp32 or bf16); bias NULL or fp32
+ * [N]. With OProj linear, Eq. 5 sums each rank's projected partial and adds the
+ * bias once: accumulate the P products into one fp32 C, passing bias on one of
+ * them. M, N, K multiples of 8 (16-byte rows), K >= 8; M*K and N*K below 2^31
+ * (else SPLITKV_ERR_UNSUPPORTED). */
+typedef enum {
+    SPLITKV_GEMM_NT = 0,
+    SPLITKV_GEMM_NN = 1,
+    SPLITKV_GEMM_TN = 2
+} splitkv_gemm_layout;
+int splitkv_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                 void* C, int c_dtype, const float* bias, int accumulate, void* stream);
+
 /* Backward of the local partial, Algorithm 1 (MERGE_BWD then AttnBwd_p), with
  * the GLOBAL (merged) lse and Delta = <do, o>:
  *   P = exp(scale <q, k_x> - lse[r,h]);  dv_x += P do;  ds = P (<do, v_x> - Delta[r,h]);

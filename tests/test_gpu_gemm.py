@@ -1,0 +1,87 @@
+"""GPU bf16 products (the projections of one draft layer) against the fp64
+product of the exact bf16 inputs: all three layouts, ragged edges in M, N and
+K, fp32 and bf16 outputs, bias and accumulation."""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_cross_amd import binding, inputs
+from tests.helpers import assert_close_f32, to_dev, to_f64, vals64
+
+pytestmark = pytest.mark.gpu
+
+NT, NN, TN = binding.SPLITKV_GEMM_NT, binding.SPLITKV_GEMM_NN, binding.SPLITKV_GEMM_TN
+
+
+def operands(layout, M, N, K, seed):
+    sa = (M, K) if layout != TN else (K, M)
+    sb = (N, K) if layout == NT else (K, N)
+    A = inputs.gen_matrix(sa[0], sa[1], seed, inputs.T_MAT, 1.0)
+    B = inputs.gen_matrix(sb[0], sb[1], seed + 1, inputs.T_MAT, K ** -0.5)
+    a, b = vals64(A), vals64(B)
+    ref = (a if layout != TN else a.T) @ (b.T if layout == NT else b)
+    return A, B, ref
+
+
+def assert_close_bf16_out(got, ref, what):
+    # one bf16 rounding of the fp32 result: |err| <= 2^-8 |ref| (+ fp32 accumulation)
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-4 * np.abs(ref).max()
+    assert (err <= bound).all(), "%s: worst excess %.3e" % (what, float((err - bound).max()))
+
+
+SHAPES = [(256, 256, 64), (8, 8, 8), (264, 136, 72), (1000, 520, 1032), (512, 768, 40),
+          (2048, 1536, 2048)]
+
+
+@pytest.mark.parametrize("layout", [NT, NN, TN])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_fp32_out(layout, M, N, K):
+    A, B, ref = operands(layout, M, N, K, seed=M + N + K)
+    C = binding.splitkv_gemm(layout, to_dev(A), to_dev(B))
+    torch.cuda.synchronize()
+    assert_close_f32(to_f64(C), ref, "gemm %d %dx%dx%d" % (layout, M, N, K))
+
+
+@pytest.mark.parametrize("layout", [NT, NN, TN])
+def test_gemm_bf16_out_bias_accumulate(layout):
+    M, N, K = 392, 264, 328
+    A, B, ref = operands(layout, M, N, K, seed=5)
+    bias = np.random.default_rng(5).standard_normal(N).astype(np.float32)
+    C0 = inputs.gen_matrix(M, N, 9, inputs.T_MAT, 1.0, dtype="fp32")
+    Cd = to_dev(C0)
+    binding.splitkv_gemm(layout, to_dev(A), to_dev(B), out=Cd, bias=to_dev(bias),
+                         accumulate=True)
+    Cb = binding.splitkv_gemm(layout, to_dev(A), to_dev(B), out_dtype=torch.bfloat16,
+                              bias=to_dev(bias))
+    torch.cuda.synchronize()
+    assert_close_f32(to_f64(Cd), ref + bias[None, :] + C0, "accumulate + bias")
+    assert_close_bf16_out(to_f64(Cb), ref + bias[None, :], "bf16 out + bias")
+
+
+def test_gemm_sum_of_products_with_bias_once():
+    # Eq. 5 shape: four products accumulated into one fp32 output, bias once
+    M, N, K = 264, 520, 256
+    C = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    bias = np.linspace(-1, 1, N).astype(np.float32)
+    ref = np.zeros((M, N)) + bias[None, :]
+    for p in range(4):
+        A, B, r = operands(NT, M, N, K, seed=100 + 7 * p)
+        binding.splitkv_gemm(NT, to_dev(A), to_dev(B), out=C, accumulate=True,
+                             bias=to_dev(bias) if p == 0 else None)
+        ref += r
+    torch.cuda.synchronize()
+    assert_close_f32(to_f64(C), ref, "sum of products")
+
+
+def test_gemm_rejects_bad_shapes():
+    x = torch.zeros((16, 12), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((16, 16), 3.0, dtype=torch.float32, device="cuda")
+    st = binding.lib().splitkv_gemm(NT, 16, 16, 12, x.data_ptr(), x.data_ptr(), out.data_ptr(),
+                                    binding.SPLITKV_FP32, None, 0, None)
+    assert st == binding.SPLITKV_ERR_INVALID_ARG   # K % 8 != 0
+    st = binding.lib().splitkv_gemm(7, 16, 16, 16, x.data_ptr(), x.data_ptr(), out.data_ptr(),
+                                    binding.SPLITKV_FP32, None, 0, None)
+    assert st == binding.SPLITKV_ERR_INVALID_ARG   # unknown layout
+    torch.cuda.synchronize()
+    assert (out == 3.0).all()
