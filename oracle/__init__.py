@@ -6,7 +6,9 @@ no code with the HIP library; only the seeded input generators are common.
 
 Each wrapper converts numpy inputs to the C types and returns numpy outputs;
 all arithmetic is in oracle.c (see its header for the equations followed),
-except that full_mask_bwd adds the two key sets' dq contributions.
+except that full_mask_bwd adds the two key sets' dq contributions and the
+draft-layer composition (draft_layer_forward / draft_layer_backward) takes its
+projections as numpy fp64 matrix products around the C attention routines.
 """
 from __future__ import annotations
 
@@ -308,3 +310,71 @@ def local_key_positions(chunk_ids, m: int) -> np.ndarray:
     (chunk j covers [j*m, (j+1)*m)), in buffer order."""
     ids = _i64(chunk_ids)
     return (ids[:, None] * m + np.arange(m, dtype=np.int64)[None, :]).reshape(-1)
+
+
+# -------------------------------------------------------------- draft layer --
+def draft_layer_forward(X, U, Wq, Wk, Wv, Wo, bo, s, a, B: int, hq: int, hkv: int, d: int,
+                        scale: float, bundles, m: int):
+    """One draft layer's attention block in Split-KV form (Algorithm 1, forward):
+    q = QProj(X) = X Wq^T (all query rows on every rank); rank p projects its own
+    context rows k_p = U_p Wk^T, v_p = U_p Wv^T (U_p: the rows of its chunks,
+    `bundles[p]`, each of m positions); Attn gives (o_p, l_p) (Eq. 3); the LSE
+    statistics are reduced and each rank rescales its partial (Eq. 4); OProj is
+    applied to every rescaled partial and the results summed, the bias added once
+    (Eq. 5). Shapes: X [Q, H], U [S, H], Wq [hq d, H], Wk, Wv [hkv d, H],
+    Wo [H, hq d], bo [H]. Returns a dict of the fp64 intermediates and Y [Q, H]."""
+    X, U, Wq, Wk, Wv, Wo, bo = (_f64(x) for x in (X, U, Wq, Wk, Wv, Wo, bo))
+    Q = X.shape[0]
+    q = (X @ Wq.T).reshape(Q, hq, d)
+    rows = np.arange(Q)
+    parts = []
+    for chunks in bundles:
+        pos = local_key_positions(chunks, m)
+        k = (U[pos] @ Wk.T).reshape(len(pos), hkv, d)
+        v = (U[pos] @ Wv.T).reshape(len(pos), hkv, d)
+        o_p, l_p = partial_attn(rows, B, s, a, q, pos, k, v, scale)
+        parts.append({"pos": pos, "k": k, "v": v, "o": o_p, "l": l_p})
+    lse = lse_reduce(np.stack([pt["l"].reshape(-1) for pt in parts]))
+    Y = np.zeros((Q, Wo.shape[0]), dtype=np.float64)
+    for pt in parts:
+        pt["obar"] = lse_rescale(pt["o"].reshape(-1, d), pt["l"].reshape(-1), lse).reshape(Q, hq, d)
+        Y += pt["obar"].reshape(Q, hq * d) @ Wo.T
+    Y += bo[None, :]
+    return {"q": q, "parts": parts, "lse": lse.reshape(Q, hq), "Y": Y}
+
+
+def draft_layer_backward(fwd, dY, X, U, Wq, Wk, Wv, Wo, s, a, B: int, hq: int, hkv: int,
+                         d: int, scale: float):
+    """Backward of draft_layer_forward (Algorithm 1, backward): OProjBwd gives the
+    output-gradient do = dY Wo (the same for every rank, since Y sums the ranks'
+    projections), dWo = sum_p dY^T obar_p and dbo = the column sums of dY;
+    MERGE_BWD all-reduces Delta = sum_p <do, obar_p>; each rank's AttnBwd_p with
+    the global lse and Delta gives its dq contribution (summed over ranks), dk_p
+    and dv_p; QProjBwd and KeyValueProjBwd give dX, dWq and each rank's dU_p
+    (its own context rows), dWk, dWv. Returns a dict of fp64 gradients; dU is
+    assembled over the ranks' rows."""
+    dY, X, U, Wq, Wk, Wv, Wo = (_f64(x) for x in (dY, X, U, Wq, Wk, Wv, Wo))
+    Q = X.shape[0]
+    q, lse, parts = fwd["q"], fwd["lse"], fwd["parts"]
+    do = (dY @ Wo).reshape(Q, hq, d)
+    dWo = sum(dY.T @ pt["obar"].reshape(Q, hq * d) for pt in parts)
+    dbo = dY.sum(axis=0)
+    dlt = sum(delta(pt["obar"], do) for pt in parts)
+    rows = np.arange(Q)
+    dq = np.zeros((Q, hq, d))
+    dU = np.zeros_like(U)
+    dWk = np.zeros_like(Wk)
+    dWv = np.zeros_like(Wv)
+    for pt in parts:
+        n = len(pt["pos"])
+        dq_p, dk, dv = attn_bwd(B, s, a, q, do, lse, dlt, pt["pos"], pt["k"], pt["v"], scale,
+                                rows, np.arange(n))
+        dq += dq_p
+        dk2, dv2 = dk.reshape(n, hkv * d), dv.reshape(n, hkv * d)
+        dU[pt["pos"]] += dk2 @ Wk + dv2 @ Wv
+        dWk += dk2.T @ U[pt["pos"]]
+        dWv += dv2.T @ U[pt["pos"]]
+    dq2 = dq.reshape(Q, hq * d)
+    return {"dX": dq2 @ Wq, "dWq": dq2.T @ X, "dU": dU, "dWk": dWk, "dWv": dWv, "dWo": dWo,
+            "dbo": dbo, "do": do, "delta": dlt, "dq": dq}
+
