@@ -146,6 +146,12 @@ def parse():
                          "merged output; per-rank: the form each rank applies when the partials "
                          "sit on different devices (LSE reduction, each rank rescales its own "
                          "partial, Delta accumulated from the rescaled partials)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time one whole draft layer instead: QProj, every rank's KeyValueProj, "
+                         "attention, the per-rank merge and output projection (Eq. 5), and the "
+                         "backward of all of it")
+    ap.add_argument("--d-model", type=int, default=5120,
+                    help="hidden size H for --layer (Table 2: 5120 for the 32/8/128 drafter)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -168,6 +174,9 @@ def main():
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
         sys.exit(2)
+    if args.layer:
+        layer_bench(args)
+        return
 
     import torch
     from block_sparse_cross_amd import binding, inputs
@@ -371,6 +380,103 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, seed, s, a, bundles, load, q, locs, args)
+    print(json.dumps(result), flush=True)
+
+
+def layer_bench(args):
+    """One whole draft layer (forward + backward) per step on one GPU, all ranks emulated."""
+    import torch
+    from block_sparse_cross_amd import binding, inputs
+    from block_sparse_cross_amd.layer import DraftLayer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = inputs.WORKLOADS[args.workload]
+    assert w.dtype == "bf16", "--layer runs the bf16 workloads"
+    H, seed = args.d_model, args.seed
+    nq, nkv = w.hq * w.d, w.hkv * w.d
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+                torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    t_setup = time.time()
+    s, a = inputs.workload_anchors(w, seed)
+    sd, ad = dev(s), dev(a)
+    plan_out = binding.splitkv_plan(sd, ad, w.B, w.S, w.m, w.P, w.J)
+    torch.cuda.synchronize()
+    cost = plan_out[0].cpu().numpy()
+    bundles = plan_out[2].cpu().numpy()
+    X = dev(inputs.gen_matrix(w.Q, H, seed, inputs.T_X, 1.0))
+    dY = dev(inputs.gen_matrix(w.Q, H, seed, inputs.T_DY, 1.0))
+    Wq = dev(inputs.gen_matrix(nq, H, seed, inputs.T_WQ, H ** -0.5))
+    Wk = dev(inputs.gen_matrix(nkv, H, seed, inputs.T_WK, H ** -0.5))
+    Wv = dev(inputs.gen_matrix(nkv, H, seed, inputs.T_WV, H ** -0.5))
+    Wo = dev(inputs.gen_matrix(H, nq, seed, inputs.T_WO, nq ** -0.5))
+    bo = dev(inputs.gen_matrix(1, H, seed, inputs.T_BO, 1.0, dtype="fp32")[0])
+    U = [dev(np.concatenate([inputs.gen_matrix(w.m, H, seed, inputs.T_CTX, 1.0,
+                                               first_row=int(j) * w.m) for j in b]))
+         for b in bundles]
+    cs = [dev(b.astype(np.int64) * w.m) for b in bundles]
+    layer = DraftLayer(sd, ad, w.B, w.hq, w.hkv, w.d, cs, w.m, Wq, Wk, Wv, Wo, bo)
+    grads = None
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    def step(events=None):
+        nonlocal grads
+        if events is not None:
+            events[0].record()
+        binding.splitkv_plan(sd, ad, w.B, w.S, w.m, w.P, w.J, out=plan_out)
+        if events is not None:
+            events[1].record()
+        layer.forward(X, U)
+        if events is not None:
+            events[2].record()
+        grads = layer.backward(dY, grads)
+        if events is not None:
+            events[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    phase = np.zeros(3)
+    for e in events:
+        for j in range(3):
+            phase[j] += e[j].elapsed_time(e[j + 1])
+    phase /= args.steps
+    pairs = int(cost.sum())
+    attn_flops = 14.0 * w.d * w.hq * pairs        # credited: 4 forward + 10 backward per pair
+    gemm_flops = layer.gemm_flops()
+    value = (attn_flops + gemm_flops) / (ms_step * 1e-3) / 1e12
+    result = {
+        "metric": "draft-layer fwd+bwd TFLOP/s (mask-live attention + projections), 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": "%s with d_model=%d: Q=%d query rows, S=%d context rows, P=%d ranks x "
+                        "J=%d chunks of m=%d, Hq/Hkv/d=%d/%d/%d, all ranks emulated on one GPU"
+                        % (w.name, H, w.Q, w.S, w.P, w.J, w.m, w.hq, w.hkv, w.d),
+            "step": "plan + layer forward (QProj, per-rank KeyValueProj, attention, LSE "
+                    "reduction, per-rank rescale and OProj summed with the bias once) + layer "
+                    "backward (OProjBwd, Delta, attention backward, QProj/KeyValueProj backward)",
+            "live_pairs_per_head": pairs},
+        "attn_flops_credited": attn_flops, "gemm_flops": gemm_flops,
+        "phase_ms": {"plan": round(phase[0], 4), "layer_fwd": round(phase[1], 4),
+                     "layer_bwd": round(phase[2], 4)},
+        "roofline": {"bound": "mfma", "kernel": "whole draft layer (attention + projections)",
+                     "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "setup_s": round(setup_s, 1),
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -31,7 +31,8 @@ SPLITKV_BASELINE_NO_BALANCE, SPLITKV_BASELINE_ZIGZAG = 0, 1
 
 EXPORTED = ("splitkv_workspace_bytes", "splitkv_plan", "splitkv_plan_baseline",
             "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
-            "splitkv_delta", "splitkv_gemm", "splitkv_attn_bwd", "splitkv_status_str")
+            "splitkv_delta", "splitkv_gemm", "splitkv_cast_bf16", "splitkv_attn_bwd",
+            "splitkv_status_str")
 
 SPLITKV_GEMM_NT, SPLITKV_GEMM_NN, SPLITKV_GEMM_TN = 0, 1, 2
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.splitkv_gemm.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
         L.splitkv_gemm.restype = ctypes.c_int
+        L.splitkv_cast_bf16.argtypes = [ctypes.c_int64, vp, vp, vp]
+        L.splitkv_cast_bf16.restype = ctypes.c_int
         L.splitkv_attn_bwd.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.splitkv_attn_bwd.restype = ctypes.c_int
         L.splitkv_status_str.argtypes = [ctypes.c_int]
@@ -381,6 +384,20 @@ def splitkv_gemm(layout: int, A: torch.Tensor, B: torch.Tensor, out: Optional[to
     _check("splitkv_gemm", lib().splitkv_gemm(int(layout), int(M), int(N), int(K), _ptr(A), _ptr(B),
                                               _ptr(out), _dtype_code(out.dtype), _ptr(bias),
                                               int(bool(accumulate)), _stream(stream)))
+    return out
+
+
+def splitkv_cast_bf16(src: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """fp32 tensor -> bf16 tensor of the same shape (round to nearest even)."""
+    if src.dtype != torch.float32:
+        raise ValueError("src must be fp32")
+    if out is None:
+        out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+    if out.numel() != src.numel() or out.dtype != torch.bfloat16:
+        raise ValueError("output disagrees")
+    _check("splitkv_cast_bf16", lib().splitkv_cast_bf16(int(src.numel()), _ptr(src), _ptr(out),
+                                                        _stream(stream)))
     return out
 
 

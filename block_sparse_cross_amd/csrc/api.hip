@@ -228,6 +228,14 @@ int splitkv_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const voi
                                  static_cast<hipStream_t>(stream)));
 }
 
+int splitkv_cast_bf16(int64_t n, const float* src, void* dst, void* stream) {
+  if (n < 0 || n % 8 != 0) return SPLITKV_ERR_INVALID_ARG;
+  if (n == 0) return SPLITKV_OK;
+  if (src == nullptr || dst == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if ((n / 8 + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  return hip_status(launch_cast_bf16(n, src, dst, static_cast<hipStream_t>(stream)));
+}
+
 int splitkv_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                  void* C, int c_dtype, const float* bias, int accumulate, void* stream) {
   if (layout != SPLITKV_GEMM_NT && layout != SPLITKV_GEMM_NN && layout != SPLITKV_GEMM_TN)

@@ -27,6 +27,13 @@
 // 4 k-values per read, two per fragment); its slots are permuted by
 // 4 (row mod 4), so the 4 rows of a transposing read hit distinct banks.
 //
+// Split K. When the output has too few tiles to fill one round of the chip
+// (a rank's weight gradient 1024 x 5120 from K = 16384 rows is 80 tiles) and C
+// is fp32, K is cut into splits of at least 8 slices; each (tile, split) workgroup adds its
+// partial product into C with atomic fp32 adds (C zeroed first unless the call
+// accumulates; the bias comes with split 0). The order of those adds varies
+// from run to run, so such results are reproducible to rounding only.
+//
 // Edges. M and N need not be multiples of the tile: rows and columns past the
 // end are read from the last valid row or 8-column group (finite filler) and
 // never stored. The last K step zero-fills the slots past K (K is a multiple
@@ -236,14 +243,19 @@ template <int LAYOUT, typename Tc>
 __global__ void __launch_bounds__(kGemmThreads, 1)
 gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
                  const bf16_t* __restrict__ B, Tc* __restrict__ Cm,
-                 const float* __restrict__ bias, int accumulate) {
+                 const float* __restrict__ bias, int accumulate, int splits,
+                 int slices_per_split) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[kStages][2][kTileElems];  // [stage][A, B]
 
-  // grid order: each XCD a contiguous run of tiles, grouped kGroupRows tile-rows
+  // grid order: each XCD a contiguous run of (tile, K-split) items, tiles
+  // grouped kGroupRows tile-rows
   const int n_tm = (int)((M + kBM - 1) / kBM), n_tn = (int)((N + kBN - 1) / kBN);
   const int nb = n_tm * n_tn;
-  int bid = blockIdx.x;
-  if (nb % kXcds == 0) bid = (bid % kXcds) * (nb / kXcds) + bid / kXcds;
+  const int total = nb * splits;
+  int item = blockIdx.x;
+  if (total % kXcds == 0) item = (item % kXcds) * (total / kXcds) + item / kXcds;
+  const int split = item % splits;
+  const int bid = item / splits;
   const int group = bid / (kGroupRows * n_tn);
   const int first = group * kGroupRows;
   const int rows_in_group = min(n_tm - first, kGroupRows);
@@ -265,6 +277,9 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
 
   const int n_k = (int)((K + kBK - 1) / kBK);
   const int n_full = (int)(K / kBK);  // slices wholly inside K
+  // this workgroup's K slices (all of them unless K is split)
+  const int kt_begin = split * slices_per_split;
+  const int kt_end = min(n_k, kt_begin + slices_per_split);
   uint32_t aoff[kPasses], boff[kPasses];
   if constexpr (Layout<LAYOUT>::A_KMAJOR)
     kmajor_offsets(M, K, m0, tid, aoff);
@@ -274,16 +289,19 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
     kmajor_offsets(N, K, n0, tid, boff);
   else
     mnmajor_offsets(N, n0, tid, boff);
-  // prologue: slices 0 .. kStages - 2 in flight
+  // prologue: the first kStages - 1 slices in flight
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (s < n_full)
-      issue_stage_fast<LAYOUT>(A, B, M, N, s, aoff, boff, lds[s][0], lds[s][1], tid);
-    else if (s < n_k)
-      issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, s, lds[s][0], lds[s][1], tid);
+  for (int s0 = 0; s0 < kStages - 1; ++s0) {
+    const int s = kt_begin + s0;
+    if (s < min(n_full, kt_end))
+      issue_stage_fast<LAYOUT>(A, B, M, N, s, aoff, boff, lds[s % kStages][0],
+                               lds[s % kStages][1], tid);
+    else if (s < kt_end)
+      issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, s, lds[s % kStages][0], lds[s % kStages][1],
+                          tid);
   }
 
-  for (int kt = 0; kt < n_k; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     // Slice kt has landed once at most the copies of the slices issued after
     // it are outstanding (they complete in issue order); the last slice may
     // also have zero-filled part of its tile through LDS writes.
@@ -293,7 +311,7 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
       wait_async();
     } else {
       static_assert(kStages == 4, "waits below are written for 2 or 4 stages");
-      const int later = min(kStages - 2, n_k - 1 - kt);
+      const int later = min(kStages - 2, kt_end - 1 - kt);
       const bool ragged_later = (K % kBK != 0) && kt + later == n_k - 1;
       if (ragged_later)
         wait_async();
@@ -307,11 +325,11 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();  // slice kt visible to all; every wave is done with kt - 1
     asm volatile("" ::: "memory");
-    if (kt + kStages - 1 < n_full) {
+    if (kt + kStages - 1 < min(n_full, kt_end)) {
       const int s = (kt + kStages - 1) % kStages;
       issue_stage_fast<LAYOUT>(A, B, M, N, kt + kStages - 1, aoff, boff, lds[s][0], lds[s][1],
                                tid);
-    } else if (kt + kStages - 1 < n_k) {
+    } else if (kt + kStages - 1 < kt_end) {
       const int s = (kt + kStages - 1) % kStages;
       issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, kt + kStages - 1, lds[s][0], lds[s][1], tid);
     }
@@ -349,7 +367,7 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
   for (int j = 0; j < 4; ++j) {
     const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
     if (n >= N) continue;
-    const float bn = bias != nullptr ? bias[n] : 0.f;
+    const float bn = (bias != nullptr && split == 0) ? bias[n] : 0.f;
 #pragma unroll
     for (int i = 0; i < kMI; ++i) {
 #pragma unroll
@@ -358,6 +376,12 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
         if (m < M) {
           Tc* p = Cm + m * N + n;
           float x = acc[i][j][e] + bn;
+          if constexpr (sizeof(Tc) == 4) {
+            if (splits > 1) {  // K split: the partial sums meet in C (zeroed first if needed)
+              atomicAdd(reinterpret_cast<float*>(p), x);
+              continue;
+            }
+          }
           if (accumulate) x += Elem<Tc>::load(p);
           Elem<Tc>::store(p, x);
         }
@@ -366,19 +390,48 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
   }
 }
 
+__global__ void __launch_bounds__(256)
+zero_f32_kernel(int64_t n4, float4* __restrict__ p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// K is split only when the tiles fill less than one round of the 256 CUs, into
+// as many splits as still fit in that round (measured on the per-rank weight
+// gradient 1024 x 5120 from K = 16384, 80 tiles: 3 splits 241 us, 2: 280 us,
+// 13: 442 us, none: 483 us; with more tiles the atomic adds cost more than the
+// fuller rounds save). A split keeps at least 8 slices.
+constexpr int kCus = 256;
+constexpr int kMinSlicesPerSplit = 8;
+
 template <int LAYOUT>
 hipError_t launch_gemm_l(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
                          int c_dtype, const float* bias, int accumulate, hipStream_t stream) {
   const int64_t nb = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int n_k = (int)((K + kBK - 1) / kBK);
+  // Too few tiles to fill the chip: split K over workgroups (fp32 output only;
+  // the splits add their partial products into C atomically).
+  int splits = 1;
+  if (c_dtype == SPLITKV_FP32 && nb < kCus / 2)
+    splits = max(1, min((int)(kCus / nb), n_k / kMinSlicesPerSplit));
+  const int sps = (n_k + splits - 1) / splits;
+  splits = (n_k + sps - 1) / sps;
+  if (splits > 1 && !accumulate) {
+    const int64_t n4 = M * N / 4;  // N % 8 == 0
+    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                       n4, static_cast<float4*>(C));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* b = static_cast<const bf16_t*>(B);
+  const dim3 grid((unsigned)(nb * splits));
   if (c_dtype == SPLITKV_FP32)
-    hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, float>), dim3((unsigned)nb), dim3(kGemmThreads),
-                       0, stream, M, N, K, a, b, static_cast<float*>(C), bias, accumulate);
+    hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, float>), grid, dim3(kGemmThreads), 0, stream, M,
+                       N, K, a, b, static_cast<float*>(C), bias, accumulate, splits, sps);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, bf16_t>), dim3((unsigned)nb),
-                       dim3(kGemmThreads), 0, stream, M, N, K, a, b, static_cast<bf16_t*>(C),
-                       bias, accumulate);
+    hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, bf16_t>), grid, dim3(kGemmThreads), 0, stream,
+                       M, N, K, a, b, static_cast<bf16_t*>(C), bias, accumulate, 1, n_k);
   return hipGetLastError();
 }
 

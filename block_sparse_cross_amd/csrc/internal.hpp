@@ -68,6 +68,8 @@ hipError_t launch_lse_rescale(int64_t rows, int32_t d, const void* o_part, int i
 hipError_t launch_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const void* dout,
                         int do_dtype, float* delta, int accumulate, hipStream_t stream);
 
+hipError_t launch_cast_bf16(int64_t n, const float* src, void* dst, hipStream_t stream);
+
 hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                        void* C, int c_dtype, const float* bias, int accumulate,
                        hipStream_t stream);

@@ -168,6 +168,16 @@ delta_rows_kernel(int64_t rows, int d, const To* __restrict__ o, const Td* __res
   }
 }
 
+// fp32 -> bf16 (round to nearest even), 8 elements per thread.
+__global__ void __launch_bounds__(kMergeThreads)
+cast_bf16_kernel(int64_t units, const float* __restrict__ src, bf16_t* __restrict__ dst) {
+  const int64_t unit = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (unit >= units) return;
+  float x[8];
+  Vec8<float>::load(src + unit * 8, x);
+  Vec8<bf16_t>::store(dst + unit * 8, x);
+}
+
 template <typename Tin, typename Tout>
 hipError_t launch_rescale_t(int64_t rows, int32_t d, const void* o_part, const float* lse_part,
                             const float* lse, void* o_bar, hipStream_t stream) {
@@ -248,6 +258,15 @@ hipError_t launch_delta(int64_t rows, int32_t d, const void* o, int o_dtype, con
   if (o_dtype == SPLITKV_FP32 && do_dtype == SPLITKV_BF16)
     return launch_delta_t<float, bf16_t>(rows, d, o, dout, delta, accumulate, stream);
   return launch_delta_t<float, float>(rows, d, o, dout, delta, accumulate, stream);
+}
+
+hipError_t launch_cast_bf16(int64_t n, const float* src, void* dst, hipStream_t stream) {
+  const int64_t units = n / 8;
+  if (units == 0) return hipSuccess;
+  const int64_t grid = (units + kMergeThreads - 1) / kMergeThreads;
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)grid), dim3(kMergeThreads), 0, stream,
+                     units, src, static_cast<bf16_t*>(dst));
+  return hipGetLastError();
 }
 
 }  // namespace splitkv

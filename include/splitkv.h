@@ -195,6 +195,10 @@ typedef enum {
 int splitkv_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                  void* C, int c_dtype, const float* bias, int accumulate, void* stream);
 
+/* fp32 -> bf16 conversion (round to nearest even) of n elements, n % 8 == 0:
+ * the rank-summed dq becomes the bf16 operand of QProj's backward products. */
+int splitkv_cast_bf16(int64_t n, const float* src, void* dst, void* stream);
+
 /* Backward of the local partial, Algorithm 1 (MERGE_BWD then AttnBwd_p), with
  * the GLOBAL (merged) lse and Delta = <do, o>:
  *   P = exp(scale <q, k_x> - lse[r,h]);  dv_x += P do;  ds = P (<do, v_x> - Delta[r,h]);

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "splitkv.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(splitkv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(splitkv_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")

@@ -85,3 +85,20 @@ def test_gemm_rejects_bad_shapes():
     assert st == binding.SPLITKV_ERR_INVALID_ARG   # unknown layout
     torch.cuda.synchronize()
     assert (out == 3.0).all()
+
+
+# Few output tiles and a long K: the K range is split over workgroups whose
+# partial products are added into C atomically (the weight-gradient shapes).
+@pytest.mark.parametrize("layout", [NT, NN, TN])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 2048), (1024, 512, 16384), (264, 8, 8200),
+                                   (512, 1032, 4104)])
+def test_gemm_split_k(layout, M, N, K):
+    A, B, ref = operands(layout, M, N, K, seed=3 * M + N + K)
+    bias = np.linspace(-2, 2, N).astype(np.float32)
+    C = binding.splitkv_gemm(layout, to_dev(A), to_dev(B), bias=to_dev(bias))
+    C0 = inputs.gen_matrix(M, N, 4, inputs.T_MAT, 1.0, dtype="fp32")
+    Ca = to_dev(C0)
+    binding.splitkv_gemm(layout, to_dev(A), to_dev(B), out=Ca, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close_f32(to_f64(C), ref + bias[None, :], "split-K")
+    assert_close_f32(to_f64(Ca), ref + C0, "split-K accumulate")
