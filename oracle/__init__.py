@@ -314,7 +314,7 @@ def local_key_positions(chunk_ids, m: int) -> np.ndarray:
 
 # -------------------------------------------------------------- draft layer --
 def draft_layer_forward(X, U, Wq, Wk, Wv, Wo, bo, s, a, B: int, hq: int, hkv: int, d: int,
-                        scale: float, bundles, m: int):
+                        scale: float, bundles, m: int, own_blocks: bool = False):
     """One draft layer's attention block in Split-KV form (Algorithm 1, forward):
     q = QProj(X) = X Wq^T (all query rows on every rank); rank p projects its own
     context rows k_p = U_p Wk^T, v_p = U_p Wv^T (U_p: the rows of its chunks,
@@ -322,7 +322,11 @@ def draft_layer_forward(X, U, Wq, Wk, Wv, Wo, bo, s, a, B: int, hq: int, hkv: in
     statistics are reduced and each rank rescales its partial (Eq. 4); OProj is
     applied to every rescaled partial and the results summed, the bias added once
     (Eq. 5). Shapes: X [Q, H], U [S, H], Wq [hq d, H], Wk, Wv [hkv d, H],
-    Wo [H, hq d], bo [H]. Returns a dict of the fp64 intermediates and Y [Q, H]."""
+    Wo [H, hq d], bo [H]. With own_blocks, the whole mask of Figure 1: every
+    block's rows also attend their block's B tokens, whose keys and values are
+    the same projections of the block rows' own hidden states (kb = X Wk^T,
+    vb = X Wv^T), one more partial in the merge. Returns a dict of the fp64
+    intermediates and Y [Q, H]."""
     X, U, Wq, Wk, Wv, Wo, bo = (_f64(x) for x in (X, U, Wq, Wk, Wv, Wo, bo))
     Q = X.shape[0]
     q = (X @ Wq.T).reshape(Q, hq, d)
@@ -334,6 +338,12 @@ def draft_layer_forward(X, U, Wq, Wk, Wv, Wo, bo, s, a, B: int, hq: int, hkv: in
         v = (U[pos] @ Wv.T).reshape(len(pos), hkv, d)
         o_p, l_p = partial_attn(rows, B, s, a, q, pos, k, v, scale)
         parts.append({"pos": pos, "k": k, "v": v, "o": o_p, "l": l_p})
+    if own_blocks:
+        bs, ba, bpos = own_block_windows(len(s), B)
+        kb = (X @ Wk.T).reshape(Q, hkv, d)
+        vb = (X @ Wv.T).reshape(Q, hkv, d)
+        o_b, l_b = partial_attn(rows, B, bs, ba, q, bpos, kb, vb, scale)
+        parts.append({"pos": None, "k": kb, "v": vb, "o": o_b, "l": l_b, "own": True})
     lse = lse_reduce(np.stack([pt["l"].reshape(-1) for pt in parts]))
     Y = np.zeros((Q, Wo.shape[0]), dtype=np.float64)
     for pt in parts:
@@ -351,8 +361,9 @@ def draft_layer_backward(fwd, dY, X, U, Wq, Wk, Wv, Wo, s, a, B: int, hq: int, h
     MERGE_BWD all-reduces Delta = sum_p <do, obar_p>; each rank's AttnBwd_p with
     the global lse and Delta gives its dq contribution (summed over ranks), dk_p
     and dv_p; QProjBwd and KeyValueProjBwd give dX, dWq and each rank's dU_p
-    (its own context rows), dWk, dWv. Returns a dict of fp64 gradients; dU is
-    assembled over the ranks' rows."""
+    (its own context rows), dWk, dWv (with the own-block partial, its key and
+    value gradients flow back through the same projections into dX). Returns a
+    dict of fp64 gradients; dU is assembled over the ranks' rows."""
     dY, X, U, Wq, Wk, Wv, Wo = (_f64(x) for x in (dY, X, U, Wq, Wk, Wv, Wo))
     Q = X.shape[0]
     q, lse, parts = fwd["q"], fwd["lse"], fwd["parts"]
@@ -365,7 +376,19 @@ def draft_layer_backward(fwd, dY, X, U, Wq, Wk, Wv, Wo, s, a, B: int, hq: int, h
     dU = np.zeros_like(U)
     dWk = np.zeros_like(Wk)
     dWv = np.zeros_like(Wv)
+    dX = np.zeros_like(X)
     for pt in parts:
+        if pt.get("own"):
+            # own-block partial: keys are the block rows' projections of X
+            bs, ba, bpos = own_block_windows(len(s), B)
+            dq_p, dk, dv = attn_bwd(B, bs, ba, q, do, lse, dlt, bpos, pt["k"], pt["v"], scale,
+                                    rows, np.arange(Q))
+            dq += dq_p
+            dk2, dv2 = dk.reshape(Q, hkv * d), dv.reshape(Q, hkv * d)
+            dX += dk2 @ Wk + dv2 @ Wv
+            dWk += dk2.T @ X
+            dWv += dv2.T @ X
+            continue
         n = len(pt["pos"])
         dq_p, dk, dv = attn_bwd(B, s, a, q, do, lse, dlt, pt["pos"], pt["k"], pt["v"], scale,
                                 rows, np.arange(n))
@@ -375,6 +398,7 @@ def draft_layer_backward(fwd, dY, X, U, Wq, Wk, Wv, Wo, s, a, B: int, hq: int, h
         dWk += dk2.T @ U[pt["pos"]]
         dWv += dv2.T @ U[pt["pos"]]
     dq2 = dq.reshape(Q, hq * d)
-    return {"dX": dq2 @ Wq, "dWq": dq2.T @ X, "dU": dU, "dWk": dWk, "dWv": dWv, "dWo": dWo,
+    dX += dq2 @ Wq
+    return {"dX": dX, "dWq": dq2.T @ X, "dU": dU, "dWk": dWk, "dWv": dWv, "dWo": dWo,
             "dbo": dbo, "do": do, "delta": dlt, "dq": dq}
 

@@ -12,15 +12,22 @@ import oracle
 from block_sparse_cross_amd import inputs
 
 
-def dense_layer(X, U, Wq, Wk, Wv, Wo, bo, s, a, B, hq, hkv, d, scale):
+def dense_layer(X, U, Wq, Wk, Wv, Wo, bo, s, a, B, hq, hkv, d, scale, own_blocks=False):
+    """Keys are the context rows U (and, for the whole mask, the query rows X
+    after them); row r of block i sees context positions [s_i, a_i) and, with
+    own_blocks, the B rows of its own block (Figure 1)."""
     Q, S = X.shape[0], U.shape[0]
     G = hq // hkv
+    KV = torch.cat([U, X], 0) if own_blocks else U
+    n = KV.shape[0]
     q = (X @ Wq.T).view(Q, hq, d).transpose(0, 1)                 # [hq, Q, d]
-    k = (U @ Wk.T).view(S, hkv, d).transpose(0, 1).repeat_interleave(G, 0)
-    v = (U @ Wv.T).view(S, hkv, d).transpose(0, 1).repeat_interleave(G, 0)
+    k = (KV @ Wk.T).view(n, hkv, d).transpose(0, 1).repeat_interleave(G, 0)
+    v = (KV @ Wv.T).view(n, hkv, d).transpose(0, 1).repeat_interleave(G, 0)
     blk = torch.arange(Q) // B
-    x = torch.arange(S)
-    mask = (x[None, :] >= s[blk][:, None]) & (x[None, :] < a[blk][:, None])   # [Q, S]
+    x = torch.arange(n)
+    mask = (x[None, :] >= s[blk][:, None]) & (x[None, :] < a[blk][:, None])   # [Q, n]
+    if own_blocks:
+        mask |= (x[None, :] >= S + blk[:, None] * B) & (x[None, :] < S + (blk[:, None] + 1) * B)
     z = (q @ k.transpose(1, 2)) * scale
     z = z.masked_fill(~mask[None], float("-inf"))
     p = torch.softmax(z, dim=-1)
@@ -43,17 +50,19 @@ def make_case(seed, P=4, J=2, m=16, B=4, hq=4, hkv=2, d=16, H=24):
     return s, a, B, hq, hkv, d, m, bundles, vals
 
 
+@pytest.mark.parametrize("own", [False, True])
 @pytest.mark.parametrize("seed", range(4))
-def test_split_kv_layer_equals_dense_layer_and_autograd(seed):
+def test_split_kv_layer_equals_dense_layer_and_autograd(seed, own):
     s, a, B, hq, hkv, d, m, bundles, v = make_case(seed)
     scale = d ** -0.5
     fwd = oracle.draft_layer_forward(v["X"], v["U"], v["Wq"], v["Wk"], v["Wv"], v["Wo"],
-                                     v["bo"], s, a, B, hq, hkv, d, scale, bundles, m)
+                                     v["bo"], s, a, B, hq, hkv, d, scale, bundles, m,
+                                     own_blocks=own)
     bwd = oracle.draft_layer_backward(fwd, v["dY"], v["X"], v["U"], v["Wq"], v["Wk"], v["Wv"],
                                       v["Wo"], s, a, B, hq, hkv, d, scale)
     T = {k: torch.tensor(x, dtype=torch.float64, requires_grad=k != "dY") for k, x in v.items()}
     Y = dense_layer(T["X"], T["U"], T["Wq"], T["Wk"], T["Wv"], T["Wo"], T["bo"],
-                    torch.tensor(s), torch.tensor(a), B, hq, hkv, d, scale)
+                    torch.tensor(s), torch.tensor(a), B, hq, hkv, d, scale, own_blocks=own)
     (Y * T["dY"]).sum().backward()
     np.testing.assert_allclose(fwd["Y"], Y.detach().numpy(), rtol=0, atol=1e-11)
     for ours, name in (("dX", "X"), ("dU", "U"), ("dWq", "Wq"), ("dWk", "Wk"), ("dWv", "Wv"),
