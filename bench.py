@@ -419,7 +419,8 @@ def layer_bench(args):
                                                first_row=int(j) * w.m) for j in b]))
          for b in bundles]
     cs = [dev(b.astype(np.int64) * w.m) for b in bundles]
-    layer = DraftLayer(sd, ad, w.B, w.hq, w.hkv, w.d, cs, w.m, Wq, Wk, Wv, Wo, bo)
+    layer = DraftLayer(sd, ad, w.B, w.hq, w.hkv, w.d, cs, w.m, Wq, Wk, Wv, Wo, bo,
+                       own_blocks=args.own_blocks)
     grads = None
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
@@ -453,6 +454,8 @@ def layer_bench(args):
             phase[j] += e[j].elapsed_time(e[j + 1])
     phase /= args.steps
     pairs = int(cost.sum())
+    if args.own_blocks:
+        pairs += w.N * w.B * w.B                  # every row also sees its block's B keys
     attn_flops = 14.0 * w.d * w.hq * pairs        # credited: 4 forward + 10 backward per pair
     gemm_flops = layer.gemm_flops()
     value = (attn_flops + gemm_flops) / (ms_step * 1e-3) / 1e12
@@ -463,8 +466,10 @@ def layer_bench(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {
             "workload": "%s with d_model=%d: Q=%d query rows, S=%d context rows, P=%d ranks x "
-                        "J=%d chunks of m=%d, Hq/Hkv/d=%d/%d/%d, all ranks emulated on one GPU"
-                        % (w.name, H, w.Q, w.S, w.P, w.J, w.m, w.hq, w.hkv, w.d),
+                        "J=%d chunks of m=%d, Hq/Hkv/d=%d/%d/%d, all ranks emulated on one GPU%s"
+                        % (w.name, H, w.Q, w.S, w.P, w.J, w.m, w.hq, w.hkv, w.d,
+                           ", whole mask (plus every block's own B keys)" if args.own_blocks
+                           else ""),
             "step": "plan + layer forward (QProj, per-rank KeyValueProj, attention, LSE "
                     "reduction, per-rank rescale and OProj summed with the bias once) + layer "
                     "backward (OProjBwd, Delta, attention backward, QProj/KeyValueProj backward)",

@@ -15,6 +15,13 @@ each rank's AttnBwd_p with the global lse and Delta adds its dq share and gives
 dk_p, dv_p; then dX = dq Wq, dWq = dq^T X, dU_p = dk_p Wk + dv_p Wv,
 dWk = sum_p dk_p^T U_p, dWv = sum_p dv_p^T U_p.
 
+With own_blocks, the whole mask of Figure 1: every block's rows also attend
+their block's B tokens, whose keys and values are the same projections of the
+block rows' hidden states (kb = X Wk^T, vb = X Wv^T). They form one more local
+segment (windows [iB, (i+1)B) over the block keys in block order) whose
+partial joins the merge and the output projection, and whose key and value
+gradients flow back through Wk, Wv into dX, dWk and dWv.
+
 Every step is a library call (argument marshalling only): the products run in
 splitkv_gemm, the attention in splitkv_attn_fwd / splitkv_attn_bwd, the merge
 halves in splitkv_lse_reduce / splitkv_lse_rescale, Delta in splitkv_delta.
@@ -41,7 +48,7 @@ class DraftLayer:
     def __init__(self, s: torch.Tensor, a: torch.Tensor, B: int, hq: int, hkv: int, d: int,
                  chunk_starts: Sequence[torch.Tensor], m: int, Wq: torch.Tensor,
                  Wk: torch.Tensor, Wv: torch.Tensor, Wo: torch.Tensor, bo: torch.Tensor,
-                 scale: Optional[float] = None):
+                 scale: Optional[float] = None, own_blocks: bool = False):
         self.s, self.a, self.B = s, a, B
         self.hq, self.hkv, self.d, self.m = hq, hkv, d, m
         self.cs = list(chunk_starts)
@@ -50,8 +57,11 @@ class DraftLayer:
         self.H = Wo.shape[0]
         self.scale = d ** -0.5 if scale is None else scale
         self.Q = s.numel() * B
+        self.own = own_blocks
         dev = s.device
-        Q, P = self.Q, self.P
+        Q = self.Q
+        P = self.P + (1 if own_blocks else 0)    # partials in the merge
+        self.n_parts = P
         bf, f32 = dict(dtype=torch.bfloat16, device=dev), dict(dtype=torch.float32, device=dev)
         self.q = torch.empty((Q, hq * d), **bf)
         self.o_parts = torch.empty((P, Q, hq, d), **bf)     # o_p, then obar_p in place
@@ -64,7 +74,9 @@ class DraftLayer:
         self.dq16 = torch.empty((Q, hq * d), **bf)
         self.ones = torch.ones((Q, 8), **bf)
         self.dbo8 = torch.empty((self.H, 8), **f32)
-        n_keys = [c.numel() * m for c in self.cs]
+        n_keys = [c.numel() * m for c in self.cs] + ([Q] if own_blocks else [])
+        if own_blocks:
+            self.bs, self.ba, self.bcs, self.blen = binding.own_block_local(s, B)
         self.k = [torch.empty((n, hkv * d), **bf) for n in n_keys]
         self.v = [torch.empty((n, hkv * d), **bf) for n in n_keys]
         self.dk = [torch.empty((n, hkv, d), **bf) for n in n_keys]
@@ -82,21 +94,29 @@ class DraftLayer:
         self.X, self.U = X, list(U)
         binding.splitkv_gemm(NT, X, self.Wq, out=self.q)
         q3 = self.q.view(Q, hq, d)
-        for p in range(self.P):
-            binding.splitkv_gemm(NT, self.U[p], self.Wk, out=self.k[p])
-            binding.splitkv_gemm(NT, self.U[p], self.Wv, out=self.v[p])
+        for p in range(self.n_parts):
+            src = self.U[p] if p < self.P else X      # the own-block keys come from X
+            binding.splitkv_gemm(NT, src, self.Wk, out=self.k[p])
+            binding.splitkv_gemm(NT, src, self.Wv, out=self.v[p])
             n = self.k[p].shape[0]
-            binding.splitkv_attn_fwd(self.s, self.a, self.B, self.cs[p], self.m, q3,
+            s, a, cs, m = self._segment(p)
+            binding.splitkv_attn_fwd(s, a, self.B, cs, m, q3,
                                      self.k[p].view(n, hkv, d), self.v[p].view(n, hkv, d),
                                      scale=self.scale, out=(self.o_parts[p], self.l_parts[p]),
                                      workspace=self.ws)
         binding.splitkv_lse_reduce(self.l_parts, out=self.lse)
-        for p in range(self.P):
+        for p in range(self.n_parts):
             binding.splitkv_lse_rescale(self.o_parts[p], self.l_parts[p], self.lse,
                                         out=self.o_parts[p])
             binding.splitkv_gemm(NT, self.o_parts[p].view(Q, hq * d), self.Wo, out=self.Y,
                                  bias=self.bo if p == 0 else None, accumulate=p > 0)
         return self.Y
+
+    def _segment(self, p: int):
+        """(windows s, a, chunk starts, chunk length) of partial p."""
+        if p < self.P:
+            return self.s, self.a, self.cs[p], self.m
+        return self.bs, self.ba, self.bcs, self.blen
 
     # ------------------------------------------------------------ backward --
     def backward(self, dY: torch.Tensor, grads: Optional[Dict[str, torch.Tensor]] = None
@@ -116,35 +136,38 @@ class DraftLayer:
         grads["dbo"] = self.dbo8[:, 0]
         binding.splitkv_gemm(NN, dY, self.Wo, out=self.do)
         do3 = self.do.view(Q, hq, d)
-        for p in range(self.P):
+        for p in range(self.n_parts):
             binding.splitkv_gemm(TN, dY, self.o_parts[p].view(Q, hq * d), out=grads["dWo"],
                                  accumulate=p > 0)
             binding.splitkv_delta(self.o_parts[p], do3, delta=self.delta, accumulate=p > 0)
         self.dq.zero_()
         q3 = self.q.view(Q, hq, d)
-        for p in range(self.P):
+        for p in range(self.n_parts):
             n = self.k[p].shape[0]
-            binding.splitkv_attn_bwd(self.s, self.a, self.B, self.cs[p], self.m, q3,
+            s, a, cs, m = self._segment(p)
+            binding.splitkv_attn_bwd(s, a, self.B, cs, m, q3,
                                      self.k[p].view(n, hkv, d), self.v[p].view(n, hkv, d), None,
                                      do3, self.lse, self.dq, scale=self.scale, delta=self.delta,
                                      out=(self.dk[p], self.dv[p]), workspace=self.ws)
         binding.splitkv_cast_bf16(self.dq, out=self.dq16)
         binding.splitkv_gemm(NN, self.dq16, self.Wq, out=grads["dX"])
         binding.splitkv_gemm(TN, self.dq16, self.X, out=grads["dWq"])
-        for p in range(self.P):
+        for p in range(self.n_parts):
             n = self.dk[p].shape[0]
             dk2, dv2 = self.dk[p].view(n, hkv * d), self.dv[p].view(n, hkv * d)
-            binding.splitkv_gemm(NN, dk2, self.Wk, out=grads["dU"][p])
-            binding.splitkv_gemm(NN, dv2, self.Wv, out=grads["dU"][p], accumulate=True)
-            binding.splitkv_gemm(TN, dk2, self.U[p], out=grads["dWk"], accumulate=p > 0)
-            binding.splitkv_gemm(TN, dv2, self.U[p], out=grads["dWv"], accumulate=p > 0)
+            # a rank's context rows get dU_p; the own-block keys' gradient goes to dX
+            dst, src = (grads["dU"][p], self.U[p]) if p < self.P else (grads["dX"], self.X)
+            binding.splitkv_gemm(NN, dk2, self.Wk, out=dst, accumulate=p >= self.P)
+            binding.splitkv_gemm(NN, dv2, self.Wv, out=dst, accumulate=True)
+            binding.splitkv_gemm(TN, dk2, src, out=grads["dWk"], accumulate=p > 0)
+            binding.splitkv_gemm(TN, dv2, src, out=grads["dWv"], accumulate=p > 0)
         return grads
 
     def gemm_flops(self) -> float:
         """Matrix-product FLOPs of one forward + backward."""
-        Q, H, P = self.Q, self.H, self.P
+        Q, H, P = self.Q, self.H, self.n_parts
         nq, nkv = self.hq * self.d, self.hkv * self.d
-        S_loc = sum(k.shape[0] for k in self.k)
+        S_loc = sum(k.shape[0] for k in self.k)     # every partial's key rows
         fwd = 2.0 * Q * H * nq + 2.0 * S_loc * H * 2 * nkv + P * 2.0 * Q * nq * H
         bwd = (2.0 * Q * H * nq                      # do
                + P * 2.0 * Q * H * nq                # dWo

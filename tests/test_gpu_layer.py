@@ -41,8 +41,9 @@ def build_case(seed, P=4, J=2, m=128, B=16, hq=4, hkv=2, d=64, H=192, L=512, A=6
     return s, a, B, hq, hkv, d, m, bundles, t, bo
 
 
+@pytest.mark.parametrize("own", [False, True])
 @pytest.mark.parametrize("seed", [0, 1])
-def test_layer_matches_oracle(seed):
+def test_layer_matches_oracle(seed, own):
     s, a, B, hq, hkv, d, m, bundles, t, bo = build_case(seed)
     dev = {k: to_dev(v) for k, v in t.items()}
     sd, ad = to_dev(s), to_dev(a)
@@ -50,13 +51,14 @@ def test_layer_matches_oracle(seed):
     U_parts = [dev["U"][torch.from_numpy(oracle.local_key_positions(b, m)).cuda()].contiguous()
                for b in bundles]
     layer = DraftLayer(sd, ad, B, hq, hkv, d, cs, m, dev["Wq"], dev["Wk"], dev["Wv"], dev["Wo"],
-                       to_dev(bo))
+                       to_dev(bo), own_blocks=own)
     Y = layer.forward(dev["X"], U_parts)
     g = layer.backward(dev["dY"])
     torch.cuda.synchronize()
     f64 = {k: vals64(v) for k, v in t.items()}
     fwd = oracle.draft_layer_forward(f64["X"], f64["U"], f64["Wq"], f64["Wk"], f64["Wv"],
-                                     f64["Wo"], bo, s, a, B, hq, hkv, d, d ** -0.5, bundles, m)
+                                     f64["Wo"], bo, s, a, B, hq, hkv, d, d ** -0.5, bundles, m,
+                                     own_blocks=own)
     bwd = oracle.draft_layer_backward(fwd, f64["dY"], f64["X"], f64["U"], f64["Wq"], f64["Wk"],
                                       f64["Wv"], f64["Wo"], s, a, B, hq, hkv, d, d ** -0.5)
     assert_layer_close(to_f64(Y), fwd["Y"], "Y")
