@@ -52,12 +52,10 @@ constexpr int kWM = 4;                      // waves along M (2 along N): 8 wave
 constexpr int kGemmThreads = 64 * 2 * kWM;
 constexpr int kMI = 256 / kWM / 32;         // 32-row blocks per wave (2)
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kStages = 2;                  // LDS ring of operand slices
 constexpr int kNSK = kBK / 8;               // 16-byte slots per k-major row
 constexpr int kKS = kBK / 16;               // 16-deep product steps per slice
 constexpr int kTileElems = kBM * kBK;       // both operand slices hold 256 x kBK elements
 constexpr int kPasses = kTileElems / 8 / kGemmThreads;  // 16-byte copies per thread per slice
-constexpr int kCopiesPerStage = 2 * kPasses;
 constexpr int kGroupRows = 8;               // tile-rows per group of the grid order
 constexpr int kXcds = 8;
 
@@ -239,13 +237,80 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// One K slice: wait for its copies (issued one slice earlier into `cur`),
+// pass the barrier, then run the slice's products while the copies of the next
+// full slice go out into `nxt`, spread one per fenced piece. The two stage
+// buffers are distinct arrays so the compiler can tell the transposing LDS
+// reads of `cur` from the copies landing in `nxt` (with one indexed array it
+// must assume they alias and drains every copy before each such read).
+template <int LAYOUT>
+__device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kMI][4], const bf16_t* A,
+                                           const bf16_t* B, int64_t M, int64_t N, int64_t K,
+                                           int64_t m0, int64_t n0, int kt, int kt_end,
+                                           int n_full, const uint32_t* aoff,
+                                           const uint32_t* boff, const bf16_t* ta,
+                                           const bf16_t* tb, bf16_t* ta_next, bf16_t* tb_next,
+                                           int tid, int lane, int wm, int wn) {
+  wait_async();  // this thread's copies of slice kt (and any zero-filling writes)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // slice kt visible to all; every wave is done with kt - 1
+  asm volatile("" ::: "memory");
+  const int kn = kt + 1;
+  const bool fast_next = kn < min(n_full, kt_end);
+  if (!fast_next && kn < kt_end) issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, kn, ta_next, tb_next, tid);
+  const int64_t kn0 = (int64_t)kn * kBK;
+  const char* a_next = reinterpret_cast<const char*>(Layout<LAYOUT>::A_KMAJOR ? A + kn0 : A + kn0 * M);
+  const char* b_next = reinterpret_cast<const char*>(Layout<LAYOUT>::B_KMAJOR ? B + kn0 : B + kn0 * N);
+  const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
+  // kKS 16-deep steps of 2 x 4 products, issued as fenced pieces of two
+  // products. A piece also issues at most one copy of the next slice and
+  // reads part of the next step's fragments (A_0 B_0, A_1 B_1, B_2, B_3 in
+  // the step's four pieces), so the LDS and memory pipes stay busy between
+  // the products instead of in bursts.
+  static_assert(kMI == 2 && 2 * kPasses <= 4 * kKS, "piece layout: 2 x 4 products per step");
+  bf16x8 a[2][kMI], b[2][4];
+#pragma unroll
+  for (int i = 0; i < kMI; ++i) a[0][i] = frag_a<LAYOUT>(ta, wm, i, 0, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[0][j] = frag_b<LAYOUT>(tb, wn, j, 0, lane);
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    const int c = ks & 1, nx = c ^ 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int piece = ks * 4 + q;
+      if (fast_next && piece < 2 * kPasses) {
+        const bool is_a = piece < kPasses;
+        const int pass = is_a ? piece : piece - kPasses;
+        uint32_t o = is_a ? aoff[pass] : boff[pass];
+        asm volatile("" : "+v"(o));
+        async_copy16((is_a ? a_next : b_next) + o,
+                     (is_a ? ta_next : tb_next) + pass * kGemmThreads * 8 + lds_off);
+      }
+      if (ks + 1 < kKS) {
+        if (q < kMI) a[nx][q] = frag_a<LAYOUT>(ta, wm, q, ks + 1, lane);
+        b[nx][q] = frag_b<LAYOUT>(tb, wn, q, ks + 1, lane);
+      }
+      const int i = q >> 1, j0 = 2 * (q & 1);
+#pragma unroll
+      for (int j = j0; j < j0 + 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 template <int LAYOUT, typename Tc>
 __global__ void __launch_bounds__(kGemmThreads, 1)
 gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
                  const bf16_t* __restrict__ B, Tc* __restrict__ Cm,
                  const float* __restrict__ bias, int accumulate, int splits,
                  int slices_per_split) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[kStages][2][kTileElems];  // [stage][A, B]
+  // two stage buffers (A and B slices each), declared apart
+  __shared__ __attribute__((aligned(16))) bf16_t lds_a0[kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_b0[kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_a1[kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_b1[kTileElems];
 
   // grid order: each XCD a contiguous run of (tile, K-split) items, tiles
   // grouped kGroupRows tile-rows
@@ -289,76 +354,18 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
     kmajor_offsets(N, K, n0, tid, boff);
   else
     mnmajor_offsets(N, n0, tid, boff);
-  // prologue: the first kStages - 1 slices in flight
-#pragma unroll
-  for (int s0 = 0; s0 < kStages - 1; ++s0) {
-    const int s = kt_begin + s0;
-    if (s < min(n_full, kt_end))
-      issue_stage_fast<LAYOUT>(A, B, M, N, s, aoff, boff, lds[s % kStages][0],
-                               lds[s % kStages][1], tid);
-    else if (s < kt_end)
-      issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, s, lds[s % kStages][0], lds[s % kStages][1],
-                          tid);
-  }
+  // slice kt_begin + r lands in buffer r mod 2
+  if (kt_begin < min(n_full, kt_end))
+    issue_stage_fast<LAYOUT>(A, B, M, N, kt_begin, aoff, boff, lds_a0, lds_b0, tid);
+  else if (kt_begin < kt_end)
+    issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, kt_begin, lds_a0, lds_b0, tid);
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    // Slice kt has landed once at most the copies of the slices issued after
-    // it are outstanding (they complete in issue order); the last slice may
-    // also have zero-filled part of its tile through LDS writes.
-    // A ragged last slice issues fewer copies (some slots are zero-filled
-    // instead), so while it is among the later slices everything is awaited.
-    if constexpr (kStages == 2) {
-      wait_async();
-    } else {
-      static_assert(kStages == 4, "waits below are written for 2 or 4 stages");
-      const int later = min(kStages - 2, kt_end - 1 - kt);
-      const bool ragged_later = (K % kBK != 0) && kt + later == n_k - 1;
-      if (ragged_later)
-        wait_async();
-      else if (later >= 2)
-        wait_vm<2 * kCopiesPerStage>();
-      else if (later == 1)
-        wait_vm<kCopiesPerStage>();
-      else
-        wait_async();
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // slice kt visible to all; every wave is done with kt - 1
-    asm volatile("" ::: "memory");
-    if (kt + kStages - 1 < min(n_full, kt_end)) {
-      const int s = (kt + kStages - 1) % kStages;
-      issue_stage_fast<LAYOUT>(A, B, M, N, kt + kStages - 1, aoff, boff, lds[s][0], lds[s][1],
-                               tid);
-    } else if (kt + kStages - 1 < kt_end) {
-      const int s = (kt + kStages - 1) % kStages;
-      issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, kt + kStages - 1, lds[s][0], lds[s][1], tid);
-    }
-    const bf16_t* ta = lds[kt % kStages][0];
-    const bf16_t* tb = lds[kt % kStages][1];
-    // kKS 16-deep steps; the fragments of step ks + 1 are read while the
-    // products of step ks run (fenced pieces keep the reads early).
-    bf16x8 a[2][kMI], b[2][4];
-#pragma unroll
-    for (int i = 0; i < kMI; ++i) a[0][i] = frag_a<LAYOUT>(ta, wm, i, 0, lane);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[0][j] = frag_b<LAYOUT>(tb, wn, j, 0, lane);
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      const int c = ks & 1, nx = c ^ 1;
-#pragma unroll
-      for (int i = 0; i < kMI; ++i) {
-        if (i == 0 && ks + 1 < kKS) {
-#pragma unroll
-          for (int i2 = 0; i2 < kMI; ++i2) a[nx][i2] = frag_a<LAYOUT>(ta, wm, i2, ks + 1, lane);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) b[nx][j] = frag_b<LAYOUT>(tb, wn, j, ks + 1, lane);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
+    gemm_slice<LAYOUT>(acc, A, B, M, N, K, m0, n0, kt, kt_end, n_full, aoff, boff, lds_a0,
+                       lds_b0, lds_a1, lds_b1, tid, lane, wm, wn);
+    if (kt + 1 < kt_end)
+      gemm_slice<LAYOUT>(acc, A, B, M, N, K, m0, n0, kt + 1, kt_end, n_full, aoff, boff, lds_a1,
+                         lds_b1, lds_a0, lds_b0, tid, lane, wm, wn);
   }
 
   // Epilogue: lane l of block (i, j) holds column 32 j + (l mod 32) of rows
