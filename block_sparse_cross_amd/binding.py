@@ -31,7 +31,8 @@ SPLITKV_BASELINE_NO_BALANCE, SPLITKV_BASELINE_ZIGZAG = 0, 1
 
 EXPORTED = ("splitkv_workspace_bytes", "splitkv_plan", "splitkv_plan_baseline",
             "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
-            "splitkv_delta", "splitkv_gemm", "splitkv_cast_bf16", "splitkv_attn_bwd",
+            "splitkv_delta", "splitkv_gemm", "splitkv_gemm_pair", "splitkv_cast_bf16",
+            "splitkv_attn_bwd",
             "splitkv_status_str")
 
 SPLITKV_GEMM_NT, SPLITKV_GEMM_NN, SPLITKV_GEMM_TN = 0, 1, 2
@@ -96,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.splitkv_gemm.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
         L.splitkv_gemm.restype = ctypes.c_int
+        L.splitkv_gemm_pair.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                        ctypes.c_int, vp]
+        L.splitkv_gemm_pair.restype = ctypes.c_int
         L.splitkv_cast_bf16.argtypes = [ctypes.c_int64, vp, vp, vp]
         L.splitkv_cast_bf16.restype = ctypes.c_int
         L.splitkv_attn_bwd.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -384,6 +389,45 @@ def splitkv_gemm(layout: int, A: torch.Tensor, B: torch.Tensor, out: Optional[to
     _check("splitkv_gemm", lib().splitkv_gemm(int(layout), int(M), int(N), int(K), _ptr(A), _ptr(B),
                                               _ptr(out), _dtype_code(out.dtype), _ptr(bias),
                                               int(bool(accumulate)), _stream(stream)))
+    return out
+
+
+def _gemm_shape(layout: int, A: torch.Tensor, B: torch.Tensor):
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16 or A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-d bf16")
+    if layout == SPLITKV_GEMM_NT:
+        (M, K), (N, K2) = A.shape, B.shape
+    elif layout == SPLITKV_GEMM_NN:
+        (M, K), (K2, N) = A.shape, B.shape
+    elif layout == SPLITKV_GEMM_TN:
+        (K, M), (K2, N) = A.shape, B.shape
+    else:
+        raise ValueError("unknown layout")
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    return M, N, K
+
+
+def splitkv_gemm_pair(layout: int, A1: torch.Tensor, B1: torch.Tensor, A2: torch.Tensor,
+                      B2: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      out_dtype: torch.dtype = torch.float32,
+                      bias: Optional[torch.Tensor] = None, accumulate: bool = False,
+                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """op(A1) op(B1) + op(A2) op(B2) in one pass (both pairs of the same shape)."""
+    M, N, K = _gemm_shape(layout, A1, B1)
+    if _gemm_shape(layout, A2, B2) != (M, N, K):
+        raise ValueError("the two products differ in shape")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs out")
+        out = torch.empty((M, N), dtype=out_dtype, device=A1.device)
+    if out.shape != (M, N):
+        raise ValueError("output shape disagrees")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N):
+        raise ValueError("bias must be fp32 [N]")
+    _check("splitkv_gemm_pair", lib().splitkv_gemm_pair(
+        int(layout), int(M), int(N), int(K), _ptr(A1), _ptr(B1), _ptr(A2), _ptr(B2), _ptr(out),
+        _dtype_code(out.dtype), _ptr(bias), int(bool(accumulate)), _stream(stream)))
     return out
 
 

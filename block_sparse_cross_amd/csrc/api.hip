@@ -248,8 +248,25 @@ int splitkv_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, con
   // tile count; the kernel addresses each operand with 32-bit byte offsets
   if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
   if (M * K >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
-  return hip_status(launch_gemm(layout, M, N, K, A, B, C, c_dtype, bias, accumulate != 0,
-                                static_cast<hipStream_t>(stream)));
+  return hip_status(launch_gemm(layout, M, N, K, A, B, nullptr, nullptr, C, c_dtype, bias,
+                                accumulate != 0, static_cast<hipStream_t>(stream)));
+}
+
+int splitkv_gemm_pair(int layout, int64_t M, int64_t N, int64_t K, const void* A1,
+                      const void* B1, const void* A2, const void* B2, void* C, int c_dtype,
+                      const float* bias, int accumulate, void* stream) {
+  if (layout != SPLITKV_GEMM_NT && layout != SPLITKV_GEMM_NN && layout != SPLITKV_GEMM_TN)
+    return SPLITKV_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 64 || M % 8 != 0 || N % 8 != 0 || K % 64 != 0)
+    return SPLITKV_ERR_INVALID_ARG;
+  if (c_dtype != SPLITKV_BF16 && c_dtype != SPLITKV_FP32) return SPLITKV_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return SPLITKV_OK;
+  if (A1 == nullptr || B1 == nullptr || A2 == nullptr || B2 == nullptr || C == nullptr)
+    return SPLITKV_ERR_INVALID_ARG;
+  if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  if (M * K >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  return hip_status(launch_gemm(layout, M, N, K, A1, B1, A2, B2, C, c_dtype, bias,
+                                accumulate != 0, static_cast<hipStream_t>(stream)));
 }
 
 int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,

@@ -27,6 +27,11 @@
 // 4 k-values per read, two per fragment); its slots are permuted by
 // 4 (row mod 4), so the 4 rows of a transposing read hit distinct banks.
 //
+// Paired products. C (+)= op(A1) op(B1) + op(A2) op(B2) with both pairs of the
+// same shape runs the second product's K slices after the first's in the same
+// accumulators (one output pass instead of a second read-modify-write): the
+// gradient of a rank's context rows is dk Wk + dv Wv.
+//
 // Split K. When the output has too few tiles to fill one round of the chip
 // (a rank's weight gradient 1024 x 5120 from K = 16384 rows is 80 tiles) and C
 // is fp32, K is cut into splits of at least 8 slices; each (tile, split) workgroup adds its
@@ -247,7 +252,8 @@ template <int LAYOUT>
 __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kMI][4], const bf16_t* A,
                                            const bf16_t* B, int64_t M, int64_t N, int64_t K,
                                            int64_t m0, int64_t n0, int kt, int kt_end,
-                                           int n_full, const uint32_t* aoff,
+                                           int n_full, const bf16_t* A2, const bf16_t* B2,
+                                           int n_k1, const uint32_t* aoff,
                                            const uint32_t* boff, const bf16_t* ta,
                                            const bf16_t* tb, bf16_t* ta_next, bf16_t* tb_next,
                                            int tid, int lane, int wm, int wn) {
@@ -256,11 +262,16 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kMI][4], const bf16_t* 
   __builtin_amdgcn_s_barrier();  // slice kt visible to all; every wave is done with kt - 1
   asm volatile("" ::: "memory");
   const int kn = kt + 1;
+  // slices past n_k1 belong to the second product of a pair
+  const bool second = kn >= n_k1;
+  const bf16_t* An = second ? A2 : A;
+  const bf16_t* Bn = second ? B2 : B;
+  const int kl = second ? kn - n_k1 : kn;
   const bool fast_next = kn < min(n_full, kt_end);
-  if (!fast_next && kn < kt_end) issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, kn, ta_next, tb_next, tid);
-  const int64_t kn0 = (int64_t)kn * kBK;
-  const char* a_next = reinterpret_cast<const char*>(Layout<LAYOUT>::A_KMAJOR ? A + kn0 : A + kn0 * M);
-  const char* b_next = reinterpret_cast<const char*>(Layout<LAYOUT>::B_KMAJOR ? B + kn0 : B + kn0 * N);
+  if (!fast_next && kn < kt_end) issue_stage<LAYOUT>(An, Bn, M, N, K, m0, n0, kl, ta_next, tb_next, tid);
+  const int64_t kn0 = (int64_t)kl * kBK;
+  const char* a_next = reinterpret_cast<const char*>(Layout<LAYOUT>::A_KMAJOR ? An + kn0 : An + kn0 * M);
+  const char* b_next = reinterpret_cast<const char*>(Layout<LAYOUT>::B_KMAJOR ? Bn + kn0 : Bn + kn0 * N);
   const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
   // kKS 16-deep steps of 2 x 4 products, issued as fenced pieces of two
   // products. A piece also issues at most one copy of the next slice and
@@ -303,7 +314,8 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kMI][4], const bf16_t* 
 template <int LAYOUT, typename Tc>
 __global__ void __launch_bounds__(kGemmThreads, 1)
 gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
-                 const bf16_t* __restrict__ B, Tc* __restrict__ Cm,
+                 const bf16_t* __restrict__ B, const bf16_t* __restrict__ A2,
+                 const bf16_t* __restrict__ B2, Tc* __restrict__ Cm,
                  const float* __restrict__ bias, int accumulate, int splits,
                  int slices_per_split) {
   // two stage buffers (A and B slices each), declared apart
@@ -340,8 +352,11 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int n_k = (int)((K + kBK - 1) / kBK);
-  const int n_full = (int)(K / kBK);  // slices wholly inside K
+  // With a second product (A2, B2; then K % kBK == 0) its slices follow the
+  // first product's n_k1 slices in the same accumulators.
+  const int n_k1 = (int)((K + kBK - 1) / kBK);
+  const int n_k = A2 != nullptr ? 2 * n_k1 : n_k1;
+  const int n_full = A2 != nullptr ? n_k : (int)(K / kBK);  // slices wholly inside K
   // this workgroup's K slices (all of them unless K is split)
   const int kt_begin = split * slices_per_split;
   const int kt_end = min(n_k, kt_begin + slices_per_split);
@@ -355,17 +370,23 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
   else
     mnmajor_offsets(N, n0, tid, boff);
   // slice kt_begin + r lands in buffer r mod 2
-  if (kt_begin < min(n_full, kt_end))
-    issue_stage_fast<LAYOUT>(A, B, M, N, kt_begin, aoff, boff, lds_a0, lds_b0, tid);
-  else if (kt_begin < kt_end)
-    issue_stage<LAYOUT>(A, B, M, N, K, m0, n0, kt_begin, lds_a0, lds_b0, tid);
+  {
+    const bool second = kt_begin >= n_k1;
+    const bf16_t* Ab = second ? A2 : A;
+    const bf16_t* Bb = second ? B2 : B;
+    const int kl = second ? kt_begin - n_k1 : kt_begin;
+    if (kt_begin < min(n_full, kt_end))
+      issue_stage_fast<LAYOUT>(Ab, Bb, M, N, kl, aoff, boff, lds_a0, lds_b0, tid);
+    else if (kt_begin < kt_end)
+      issue_stage<LAYOUT>(Ab, Bb, M, N, K, m0, n0, kl, lds_a0, lds_b0, tid);
+  }
 
   for (int kt = kt_begin; kt < kt_end; kt += 2) {
-    gemm_slice<LAYOUT>(acc, A, B, M, N, K, m0, n0, kt, kt_end, n_full, aoff, boff, lds_a0,
-                       lds_b0, lds_a1, lds_b1, tid, lane, wm, wn);
+    gemm_slice<LAYOUT>(acc, A, B, M, N, K, m0, n0, kt, kt_end, n_full, A2, B2, n_k1, aoff, boff,
+                       lds_a0, lds_b0, lds_a1, lds_b1, tid, lane, wm, wn);
     if (kt + 1 < kt_end)
-      gemm_slice<LAYOUT>(acc, A, B, M, N, K, m0, n0, kt + 1, kt_end, n_full, aoff, boff, lds_a1,
-                         lds_b1, lds_a0, lds_b0, tid, lane, wm, wn);
+      gemm_slice<LAYOUT>(acc, A, B, M, N, K, m0, n0, kt + 1, kt_end, n_full, A2, B2, n_k1, aoff,
+                         boff, lds_a1, lds_b1, lds_a0, lds_b0, tid, lane, wm, wn);
   }
 
   // Epilogue: lane l of block (i, j) holds column 32 j + (l mod 32) of rows
@@ -412,10 +433,11 @@ constexpr int kCus = 256;
 constexpr int kMinSlicesPerSplit = 8;
 
 template <int LAYOUT>
-hipError_t launch_gemm_l(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
-                         int c_dtype, const float* bias, int accumulate, hipStream_t stream) {
+hipError_t launch_gemm_l(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                         const void* A2, const void* B2, void* C, int c_dtype, const float* bias,
+                         int accumulate, hipStream_t stream) {
   const int64_t nb = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-  const int n_k = (int)((K + kBK - 1) / kBK);
+  const int n_k = (int)((K + kBK - 1) / kBK) * (A2 != nullptr ? 2 : 1);
   // Too few tiles to fill the chip: split K over workgroups (fp32 output only;
   // the splits add their partial products into C atomically).
   int splits = 1;
@@ -432,29 +454,34 @@ hipError_t launch_gemm_l(int64_t M, int64_t N, int64_t K, const void* A, const v
   }
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* b = static_cast<const bf16_t*>(B);
+  const bf16_t* a2 = static_cast<const bf16_t*>(A2);
+  const bf16_t* b2 = static_cast<const bf16_t*>(B2);
   const dim3 grid((unsigned)(nb * splits));
   if (c_dtype == SPLITKV_FP32)
     hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, float>), grid, dim3(kGemmThreads), 0, stream, M,
-                       N, K, a, b, static_cast<float*>(C), bias, accumulate, splits, sps);
+                       N, K, a, b, a2, b2, static_cast<float*>(C), bias, accumulate, splits, sps);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, bf16_t>), grid, dim3(kGemmThreads), 0, stream,
-                       M, N, K, a, b, static_cast<bf16_t*>(C), bias, accumulate, 1, n_k);
+                       M, N, K, a, b, a2, b2, static_cast<bf16_t*>(C), bias, accumulate, 1, n_k);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
-                       void* C, int c_dtype, const float* bias, int accumulate,
-                       hipStream_t stream) {
+                       const void* A2, const void* B2, void* C, int c_dtype, const float* bias,
+                       int accumulate, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   switch (layout) {
     case SPLITKV_GEMM_NT:
-      return launch_gemm_l<SPLITKV_GEMM_NT>(M, N, K, A, B, C, c_dtype, bias, accumulate, stream);
+      return launch_gemm_l<SPLITKV_GEMM_NT>(M, N, K, A, B, A2, B2, C, c_dtype, bias, accumulate,
+                                            stream);
     case SPLITKV_GEMM_NN:
-      return launch_gemm_l<SPLITKV_GEMM_NN>(M, N, K, A, B, C, c_dtype, bias, accumulate, stream);
+      return launch_gemm_l<SPLITKV_GEMM_NN>(M, N, K, A, B, A2, B2, C, c_dtype, bias, accumulate,
+                                            stream);
     default:
-      return launch_gemm_l<SPLITKV_GEMM_TN>(M, N, K, A, B, C, c_dtype, bias, accumulate, stream);
+      return launch_gemm_l<SPLITKV_GEMM_TN>(M, N, K, A, B, A2, B2, C, c_dtype, bias, accumulate,
+                                            stream);
   }
 }
 

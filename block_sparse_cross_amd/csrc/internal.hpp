@@ -71,8 +71,8 @@ hipError_t launch_delta(int64_t rows, int32_t d, const void* o, int o_dtype, con
 hipError_t launch_cast_bf16(int64_t n, const float* src, void* dst, hipStream_t stream);
 
 hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
-                       void* C, int c_dtype, const float* bias, int accumulate,
-                       hipStream_t stream);
+                       const void* A2, const void* B2, void* C, int c_dtype, const float* bias,
+                       int accumulate, hipStream_t stream);
 
 hipError_t launch_bwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
                       const int2* block_range, void* meta, void* chunk_range, const void* q,

@@ -23,7 +23,7 @@ partial joins the merge and the output projection, and whose key and value
 gradients flow back through Wk, Wv into dX, dWk and dWv.
 
 Every step is a library call (argument marshalling only): the products run in
-splitkv_gemm, the attention in splitkv_attn_fwd / splitkv_attn_bwd, the merge
+splitkv_gemm / splitkv_gemm_pair, the attention in splitkv_attn_fwd / splitkv_attn_bwd, the merge
 halves in splitkv_lse_reduce / splitkv_lse_rescale, Delta in splitkv_delta.
 Operands of the products are bf16; Y and the weight and input gradients fp32.
 """
@@ -155,10 +155,11 @@ class DraftLayer:
         for p in range(self.n_parts):
             n = self.dk[p].shape[0]
             dk2, dv2 = self.dk[p].view(n, hkv * d), self.dv[p].view(n, hkv * d)
-            # a rank's context rows get dU_p; the own-block keys' gradient goes to dX
+            # a rank's context rows get dU_p = dk Wk + dv Wv (one paired product);
+            # the own-block keys' gradient adds into dX
             dst, src = (grads["dU"][p], self.U[p]) if p < self.P else (grads["dX"], self.X)
-            binding.splitkv_gemm(NN, dk2, self.Wk, out=dst, accumulate=p >= self.P)
-            binding.splitkv_gemm(NN, dv2, self.Wv, out=dst, accumulate=True)
+            binding.splitkv_gemm_pair(NN, dk2, self.Wk, dv2, self.Wv, out=dst,
+                                      accumulate=p >= self.P)
             binding.splitkv_gemm(TN, dk2, src, out=grads["dWk"], accumulate=p > 0)
             binding.splitkv_gemm(TN, dv2, src, out=grads["dWv"], accumulate=p > 0)
         return grads

@@ -195,6 +195,14 @@ typedef enum {
 int splitkv_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                  void* C, int c_dtype, const float* bias, int accumulate, void* stream);
 
+/* Two products of the same layout and shape summed into one output:
+ *   C (+)= op(A1) op(B1) + op(A2) op(B2) (+ bias)
+ * in one pass over C (KeyValueProj's backward: dU_p = dk_p Wk + dv_p Wv).
+ * Same conventions as splitkv_gemm; additionally K % 64 == 0 and K >= 64. */
+int splitkv_gemm_pair(int layout, int64_t M, int64_t N, int64_t K, const void* A1,
+                      const void* B1, const void* A2, const void* B2, void* C, int c_dtype,
+                      const float* bias, int accumulate, void* stream);
+
 /* fp32 -> bf16 conversion (round to nearest even) of n elements, n % 8 == 0:
  * the rank-summed dq becomes the bf16 operand of QProj's backward products. */
 int splitkv_cast_bf16(int64_t n, const float* src, void* dst, void* stream);

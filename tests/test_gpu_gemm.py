@@ -102,3 +102,32 @@ def test_gemm_split_k(layout, M, N, K):
     torch.cuda.synchronize()
     assert_close_f32(to_f64(C), ref + bias[None, :], "split-K")
     assert_close_f32(to_f64(Ca), ref + C0, "split-K accumulate")
+
+
+@pytest.mark.parametrize("layout", [NT, NN, TN])
+@pytest.mark.parametrize("M,N,K", [(264, 520, 128), (1032, 512, 1024), (256, 256, 4096)])
+def test_gemm_pair(layout, M, N, K):
+    # op(A1) op(B1) + op(A2) op(B2) in one pass (incl. the split-K case 256 x 256)
+    A1, B1, r1 = operands(layout, M, N, K, seed=11 + M)
+    A2, B2, r2 = operands(layout, M, N, K, seed=12 + N)
+    bias = np.linspace(-1, 1, N).astype(np.float32)
+    C = binding.splitkv_gemm_pair(layout, to_dev(A1), to_dev(B1), to_dev(A2), to_dev(B2),
+                                  bias=to_dev(bias))
+    C0 = inputs.gen_matrix(M, N, 5, inputs.T_MAT, 1.0, dtype="fp32")
+    Ca = to_dev(C0)
+    binding.splitkv_gemm_pair(layout, to_dev(A1), to_dev(B1), to_dev(A2), to_dev(B2), out=Ca,
+                              accumulate=True)
+    torch.cuda.synchronize()
+    assert_close_f32(to_f64(C), r1 + r2 + bias[None, :], "pair")
+    assert_close_f32(to_f64(Ca), r1 + r2 + C0, "pair accumulate")
+
+
+def test_gemm_pair_rejects_k_not_multiple_of_64():
+    x = torch.zeros((16, 72), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((16, 16), 3.0, dtype=torch.float32, device="cuda")
+    st = binding.lib().splitkv_gemm_pair(NT, 16, 16, 72, x.data_ptr(), x.data_ptr(),
+                                         x.data_ptr(), x.data_ptr(), out.data_ptr(),
+                                         binding.SPLITKV_FP32, None, 0, None)
+    assert st == binding.SPLITKV_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (out == 3.0).all()
