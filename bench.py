@@ -31,12 +31,16 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-# Everything that decides the kernels' machine code: measured HBM traffic is
-# only reported while these files hash to the value recorded with it.
+# What decides the machine code and launch shapes of the kernels whose traffic
+# is recorded (plan, forward, merge, backward): their sources, the shared
+# device header, the compile-time constants of the internal header and the
+# build flags. Entry points, declarations and the C header only route calls
+# to them. Measured HBM traffic is reported only while this hash matches the
+# one recorded with it.
 KERNEL_SOURCES = ["block_sparse_cross_amd/csrc/" + f for f in
-                  ("api.hip", "attn_bwd.hip", "attn_fwd.hip", "merge.hip", "plan.hip",
-                   "common.hpp", "internal.hpp")] + ["block_sparse_cross_amd/build.py",
-                                                     "include/splitkv.h"]
+                  ("attn_bwd.hip", "attn_fwd.hip", "merge.hip", "plan.hip", "common.hpp")] + \
+    ["block_sparse_cross_amd/build.py"]
+CONSTANT_SOURCES = ["block_sparse_cross_amd/csrc/internal.hpp"]   # only its constexpr lines
 
 # The kernels one call of each entry point launches (names as in a trace).
 ENTRY_KERNELS = {
@@ -58,6 +62,12 @@ def sources_hash() -> str:
         h.update(f.encode())
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
+    for f in CONSTANT_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(ROOT, f)) as fh:
+            for line in fh:
+                if "constexpr" in line:
+                    h.update(line.encode())
     return h.hexdigest()[:16]
 
 
