@@ -111,12 +111,14 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
             raise SystemExit("no copy dispatch found for %s calibration" % counter)
         factors[counter] = COPY_CALIBRATION_BYTES / (big * 1024.0)
         for key, kernels in ENTRY_KERNELS.items():
-            tot = 0.0
+            tot, seen = 0.0, False
             for k in kernels:
                 ks = [v for name, vs in vals.items() if k in name for v in vs]
                 if ks:
                     tot += sum(ks) / len(ks)
-            out.setdefault(key, {})[counter] = tot * 1024.0 * factors[counter]
+                    seen = True
+            if seen:  # entry points the profiled run did not call are left out
+                out.setdefault(key, {})[counter] = tot * 1024.0 * factors[counter]
     rec = {"workload": workload, "sources_sha256": sources_hash(),
            "calibration": {"fetch_factor": round(factors["FETCH_SIZE"], 4),
                            "write_factor": round(factors["WRITE_SIZE"], 4)},
