@@ -122,7 +122,8 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
     rec = {"workload": workload, "sources_sha256": sources_hash(),
            "calibration": {"fetch_factor": round(factors["FETCH_SIZE"], 4),
                            "write_factor": round(factors["WRITE_SIZE"], 4)},
-           "per_launch_bytes": {k: {"fetch": round(v["FETCH_SIZE"]), "write": round(v["WRITE_SIZE"])}
+           "per_launch_bytes": {k: {"fetch": round(v.get("FETCH_SIZE", 0.0)),
+                                    "write": round(v.get("WRITE_SIZE", 0.0))}
                                 for k, v in out.items()}}
     lines = ["# HBM traffic per call: %s" % workload, "",
              "Commands (run from the repository root on one MI355X, one counter per pass):", "",
