@@ -131,3 +131,15 @@ def test_gemm_pair_rejects_k_not_multiple_of_64():
     assert st == binding.SPLITKV_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert (out == 3.0).all()
+
+
+@pytest.mark.parametrize("layout", [NT, NN, TN])
+def test_gemm_bf16_accumulate(layout):
+    # C bf16 read, added to, rounded once: C = bf16(C0 + A B)
+    M, N, K = 136, 264, 192
+    A, B, ref = operands(layout, M, N, K, seed=21)
+    C0 = inputs.gen_matrix(M, N, 22, inputs.T_MAT, 1.0)          # bf16 bits
+    Cd = to_dev(C0)
+    binding.splitkv_gemm(layout, to_dev(A), to_dev(B), out=Cd, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close_bf16_out(to_f64(Cd), ref + vals64(C0), "bf16 accumulate")
