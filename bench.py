@@ -383,6 +383,12 @@ def main():
         "setup_s": round(setup_s, 1),
     }
 
+    # Context measured on the same box after the timed steps: a dense bf16
+    # product through the vendor library and a plain 1 GiB device copy (the
+    # ceilings the attention and merge rates can be read against).
+    result["context"] = box_ceilings(torch, dev)
+    result["merge_frac_copy"] = round(merge_gbs / result["context"]["device_copy_gbs"], 4)
+
     if args.copy_calibration:
         x = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
         y = torch.empty_like(x)
@@ -394,6 +400,36 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, seed, s, a, bundles, load, q, locs, args)
     print(json.dumps(result), flush=True)
+
+
+def box_ceilings(torch, dev) -> dict:
+    """Dense bf16 8192^3 product (torch.matmul, the vendor library) and a 1 GiB
+    device-to-device copy, each the median of 5 timed runs after 2 warmups."""
+    def med_ms(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+    n = 8192
+    a = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    gemm_ms = med_ms(lambda: torch.matmul(a, b))
+    del a, b
+    x = torch.empty(1 << 29, dtype=torch.float16, device=dev)   # 1 GiB
+    y = torch.empty_like(x)
+    copy_ms = med_ms(lambda: y.copy_(x))
+    del x, y
+    return {"dense_bf16_gemm_tflops": round(2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "device_copy_gbs": round(2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+            "what": "torch.matmul bf16 8192^3 and a 1 GiB device copy (read + write bytes), "
+                    "medians of 5 after the timed steps"}
 
 
 def layer_bench(args):
