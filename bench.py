@@ -149,8 +149,9 @@ def parse():
     ap.add_argument("--workload", default="weak8")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1200,
-                    help="query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-blocks", type=int, default=24,
+                    help="blocks (of B query rows) in the oracle's timed forward + backward "
+                         "sample")
     ap.add_argument("--own-blocks", action="store_true",
                     help="whole mask: also the own-block partial of every block (its B "
                          "block keys), merged with the P context partials and in the backward")
@@ -536,8 +537,9 @@ def layer_bench(args):
 
 def cpu_baseline(w, seed, s, a, bundles, load, q, locs, args):
     """The oracle (fp64 C, OpenMP) timed on this host on a bounded sample of the
-    same workload: Eq. 3 partial attention for a few query rows (all heads)
-    against the max-loaded rank's local keys, FLOPs counted like the GPU's."""
+    same workload: the forward (Eq. 3) and the backward (Algorithm 1: Delta,
+    then dq, dk, dv) of a seeded subset of the blocks against the max-loaded
+    rank's local keys, FLOPs counted like the GPU's (14 d Hq per live pair)."""
     import oracle
     from block_sparse_cross_amd import inputs
 
@@ -548,22 +550,28 @@ def cpu_baseline(w, seed, s, a, bundles, load, q, locs, args):
     k = inputs.as_f32(inputs.gen_local_kv(w, seed, ids, "k")).astype(np.float64)
     v = inputs.as_f32(inputs.gen_local_kv(w, seed, ids, "v")).astype(np.float64)
     g = np.random.default_rng(seed + 12345)
-    rows = np.sort(g.choice(w.Q, size=min(args.cpu_rows, w.Q), replace=False))
-    qs = inputs.as_f32(inputs.gen_q(w, seed, blocks=rows // w.B)).reshape(
-        len(rows), w.B, w.hq, w.d)[np.arange(len(rows)), rows % w.B].astype(np.float64)
-    blk = rows // w.B
-    live = int(sum(((pos >= s[i]) & (pos < a[i])).sum() for i in blk))  # pairs per head
+    blocks = np.sort(g.choice(w.N, size=min(args.cpu_blocks, w.N), replace=False))
+    qs = inputs.as_f32(inputs.gen_q(w, seed, blocks=blocks)).astype(np.float64)
+    dos = inputs.as_f32(inputs.gen_do(w, seed, blocks=blocks)).astype(np.float64)
+    qs = qs.reshape(len(blocks) * w.B, w.hq, w.d)
+    dos = dos.reshape(len(blocks) * w.B, w.hq, w.d)
+    sb, ab = s[blocks], a[blocks]                  # the sample as its own set of blocks
+    rows = np.arange(len(blocks) * w.B)
+    live = int(sum(((pos >= sb[i]) & (pos < ab[i])).sum() for i in range(len(blocks)))) * w.B
+    scale = w.d ** -0.5
     t0 = time.perf_counter()
-    oracle.partial_attn(rows, w.B, s, a, qs, pos, k, v, w.d ** -0.5)
+    o, lse = oracle.partial_attn(rows, w.B, sb, ab, qs, pos, k, v, scale)
+    dlt = oracle.delta(o, dos)
+    oracle.attn_bwd(w.B, sb, ab, qs, dos, lse, dlt, pos, k, v, scale, rows, np.arange(len(pos)))
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.d * w.hq * live
+    flops = 14.0 * w.d * w.hq * live
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "fp64 partial attention (Eq. 3) of %d query rows x %d heads against "
-                      "rank %d's %d local keys (%d live pairs per head)"
-                      % (len(rows), w.hq, r, len(pos), live)}
-
+            "sample": "fp64 forward (Eq. 3) + backward (Algorithm 1: Delta, dq, dk, dv) of %d "
+                      "seeded blocks (%d query rows) x %d heads against rank %d's %d local keys "
+                      "(%d live pairs per head); FLOPs counted as 14 d Hq per live pair"
+                      % (len(blocks), len(rows), w.hq, r, len(pos), live)}
 
 if __name__ == "__main__":
     main()
