@@ -13,19 +13,23 @@
 // Work decomposition. A workgroup of 8 waves (two per SIMD) computes a
 // 256 x 256 tile of C; wave (wm, wn) owns 64 rows x 128 columns as 2 x 4
 // blocks of the 32x32x16 bf16 matrix-core product (128 fp32 accumulators per
-// lane). K advances 32 at a time through a ring of 4 LDS stages (32 KB each):
-// the A and B slices are copied global -> LDS with asynchronous 16-byte loads
-// three steps ahead of their use, each step waits only for its own slice
-// (vmcnt leaves the later slices in flight) and passes one barrier.
+// lane). K advances 64 at a time through two LDS stage buffers (A and B
+// slices, 64 KB per stage, declared as separate arrays): the A and B slices of
+// step k + 1 are copied global -> LDS with asynchronous 16-byte loads while
+// step k is multiplied, one copy per fenced piece of two products, from
+// per-lane 32-bit offsets fixed per workgroup plus a scalar slice base; one
+// barrier per step.
 //
 // Operand tiles in LDS. A slice whose rows run along K ("k-major": A in NT and
-// NN, B in NT) is stored [256][32], 64-byte rows, and read 8 k-values per
+// NN, B in NT) is stored [256][64], 128-byte rows, and read 8 k-values per
 // lane with one 16-byte LDS read; its 16-byte slots are XOR-permuted by
-// (row / 4) mod 4, so the 16 rows a quarter-wave reads land on 16 distinct
+// (row / 2) mod 8, so the 16 rows a quarter-wave reads land on 16 distinct
 // bank groups. A slice whose rows run along M or N ("mn-major": B in NN and
-// TN, A in TN) is stored [32][256] and read transposed (ds_read_b64_tr_b16,
+// TN, A in TN) is stored [64][256] and read transposed (ds_read_b64_tr_b16,
 // 4 k-values per read, two per fragment); its slots are permuted by
-// 4 (row mod 4), so the 4 rows of a transposing read hit distinct banks.
+// 4 (row mod 4), so the 4 rows of a transposing read hit distinct banks. The
+// fragments of the next 16-deep step are read behind the current step's
+// products.
 //
 // Paired products. C (+)= op(A1) op(B1) + op(A2) op(B2) with both pairs of the
 // same shape runs the second product's K slices after the first's in the same
@@ -232,14 +236,6 @@ __device__ __forceinline__ void issue_stage(const bf16_t* A, const bf16_t* B, in
     copy_step<LAYOUT, true>(A, B, M, N, K, m0, n0, k0, ta, tb, tid);
   else
     copy_step<LAYOUT, false>(A, B, M, N, K, m0, n0, k0, ta, tb, tid);
-}
-
-// s_waitcnt with vmcnt = N (6 bits: low 4 at bit 0, high 2 at bit 14) and the
-// other counters left free.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // One K slice: wait for its copies (issued one slice earlier into `cur`),
