@@ -473,19 +473,20 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
 }
 
-// dQ, query-outer (no atomics): a workgroup takes 128 consecutive query
+// dQ, query-outer (no atomics): a workgroup takes 256 consecutive query
 // vectors of one kv head (32 per wave, lane % 32 = the lane's vector) and
 // walks the 64-key tiles of their key intervals, like the forward kernel. With
 // the global lse the weights need no running statistics:
 //   S^T = K Q^T, dP^T = V dO^T, dS^T = P (dP - Delta), dQ^T += K^T dS^T,
 // the K^T fragments coming from the row-major K tile through the transposing
 // read. dq += scale * dQ once at the end (each (row, head) has one owner).
-constexpr int kDqThreads = 256;
-constexpr int kDqVecPerWG = 128;
+constexpr int kDqThreads = 512;  // 8 waves, two per SIMD
+constexpr int kDqWaves = kDqThreads / 64;
+constexpr int kDqVecPerWG = 32 * kDqWaves;
 constexpr int kDqKT = 64;
 
 template <int D>
-__global__ void __launch_bounds__(kDqThreads, 2)
+__global__ void __launch_bounds__(kDqThreads, 1)
 attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ delta,
@@ -496,12 +497,12 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16_t V0[kDqKT * D];
   __shared__ __attribute__((aligned(16))) bf16_t K1[kDqKT * D];
   __shared__ __attribute__((aligned(16))) bf16_t V1[kDqKT * D];
-  __shared__ int wave_lo[4], wave_hi[4];
+  __shared__ int wave_lo[kDqWaves], wave_hi[kDqWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int s16 = lane & 15;
-  const int g = blockIdx.x % hkv;
+  const int g = __builtin_amdgcn_readfirstlane(blockIdx.x % hkv);
   // vector groups in reverse (longest windows first), as in the forward
   const int64_t vec = (int64_t)((gridDim.x / hkv) - 1 - blockIdx.x / hkv) * kDqVecPerWG + wave * 32 + (lane & 31);
   const bool valid = vec < n_vec;
@@ -523,10 +524,11 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
   const bool live_lane = valid && qlo < qhi;
   const int64_t head_off = (row * hq + (int64_t)g * G + hh) * D;
-  const int wlo = wave_min_i(live_lane ? qlo : 0x7fffffff);
-  const int whi = wave_max_i(live_lane ? qhi : -1);
-  const int wall_lo = wave_max_i(live_lane ? qlo : 0x7fffffff);
-  const int wall_hi = wave_min_i(live_lane ? qhi : -1);
+  // (the same in every lane; readfirstlane keeps the tile tests scalar)
+  const int wlo = __builtin_amdgcn_readfirstlane(wave_min_i(live_lane ? qlo : 0x7fffffff));
+  const int whi = __builtin_amdgcn_readfirstlane(wave_max_i(live_lane ? qhi : -1));
+  const int wall_lo = __builtin_amdgcn_readfirstlane(wave_max_i(live_lane ? qlo : 0x7fffffff));
+  const int wall_hi = __builtin_amdgcn_readfirstlane(wave_min_i(live_lane ? qhi : -1));
   if (lane == 0) { wave_lo[wave] = wlo; wave_hi[wave] = whi; }
 
   // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T).
@@ -544,15 +546,17 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __syncthreads();
   int lo = 0x7fffffff, hi = -1;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) { lo = min(lo, wave_lo[w]); hi = max(hi, wave_hi[w]); }
+  for (int w = 0; w < kDqWaves; ++w) { lo = min(lo, wave_lo[w]); hi = max(hi, wave_hi[w]); }
   lo = __builtin_amdgcn_readfirstlane(lo);
   hi = __builtin_amdgcn_readfirstlane(hi);
 
+  const uint32_t k_off = tile_lane_offset<D, kDqThreads, kSwzBoth>((int64_t)hkv * D, tid);
+  const uint32_t v_off = tile_lane_offset<D, kDqThreads, kSwzRows>((int64_t)hkv * D, tid);
   auto issue_tile = [&](int k0, bf16_t* Kn, bf16_t* Vn) {
     if (k0 + kDqKT <= n_keys) {
       const int64_t first = ((int64_t)k0 * hkv + g) * D;
-      issue_tile_async<D, kDqKT, kDqThreads, kSwzBoth>(k + first, (int64_t)hkv * D, Kn, tid);
-      issue_tile_async<D, kDqKT, kDqThreads, kSwzRows>(v + first, (int64_t)hkv * D, Vn, tid);
+      issue_tile_async_off<D, kDqKT, kDqThreads>(k + first, (int64_t)hkv * D, k_off, Kn, tid);
+      issue_tile_async_off<D, kDqKT, kDqThreads>(v + first, (int64_t)hkv * D, v_off, Vn, tid);
     } else {
       issue_rows_async<D, kDqKT, kDqThreads, kSwzBoth>(k, hkv, g, k0, n_keys, Kn, tid);
       issue_rows_async<D, kDqKT, kDqThreads, kSwzRows>(v, hkv, g, k0, n_keys, Vn, tid);

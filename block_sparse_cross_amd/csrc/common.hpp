@@ -151,42 +151,17 @@ __device__ __forceinline__ void issue_rows_async(const bf16_t* __restrict__ src,
   }
 }
 
-// The same copy for a tile that lies wholly inside the buffer, with the
-// addressing split into a wave-uniform part (the tile's first row and the
-// per-pass steps, scalar) and a per-lane byte offset within the tile (row r at
-// r * row_stride elements, its 16-byte slot permuted by the swizzle KIND).
-// Rows of pass p sit p * THREADS / NS rows below those of pass 0, a multiple
-// of 16, and the swizzles depend on the row modulo 16 only, so one per-lane
-// offset serves every pass. The offset is recomputed from the thread index at
-// each call (a few integer operations) rather than kept live across the tile
-// loop: under register pressure the compiler would otherwise spill it, and a
-// scratch reload waits on the same counter as the asynchronous copies.
-// Kernels with registers to spare pass RECOMPUTE = false and let the compiler
-// hoist the offsets out of the loop.
-template <int D, int ROWS, int THREADS, int KIND, bool RECOMPUTE = true>
-__device__ __forceinline__ void issue_tile_async(const bf16_t* first, int64_t row_stride,
-                                                 bf16_t* tile, int tid) {
-  constexpr int NS = D / 8;
-  constexpr int PASSES = ROWS * NS / THREADS;
-  constexpr int ROWS_PER_PASS = THREADS / NS;
-  static_assert(PASSES * THREADS == ROWS * NS, "tile must split evenly over the threads");
-  static_assert(ROWS_PER_PASS % 16 == 0, "pass step must keep the swizzle");
-  int t = tid;
-  if constexpr (RECOMPUTE) asm volatile("" : "+v"(t));  // opaque: keep the offset computation here
-  const int row = t / NS, phys = t % NS;
-  const uint32_t off = (uint32_t)(row * (uint32_t)row_stride * 2u + (phys ^ swz<NS, KIND>(row)) * 16);
-  const uint32_t step = (uint32_t)(ROWS_PER_PASS * row_stride * 2);  // uniform
-  const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
-  const char* base = reinterpret_cast<const char*>(first);
-#pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass)
-    async_copy16((base + (size_t)pass * step) + off, tile + pass * THREADS * 8 + lds_off);
-}
-
-// The same copy with the lane's byte offset computed once by the caller
-// (tile_lane_offset) and kept in one register: a kernel with registers to
-// spare saves the per-call offset arithmetic. The offset is made opaque at
-// each call so that the compiler does not hoist a 64-bit address per pass.
+// The same copy for a tile that lies wholly inside the buffer. Row r of the
+// tile sits r * row_stride elements after `first`, its 16-byte slot permuted
+// by the swizzle KIND; rows of pass p sit p * THREADS / NS rows below those
+// of pass 0, a multiple of 16, and the swizzles depend on the row modulo 16
+// only, so one per-lane byte offset (tile_lane_offset, computed once by the
+// caller and kept in one register) serves every pass. The tile's first address is
+// the same in every lane; it is read from the first lane into scalar
+// registers and each pass adds its step there, so the copies take the
+// scalar-base form with the lane offset as their only vector operand and a
+// pass costs no vector instruction. The offset is made opaque at each call so
+// that the compiler does not fold it into a 64-bit vector address per pass.
 template <int D, int THREADS, int KIND>
 __device__ __forceinline__ uint32_t tile_lane_offset(int64_t row_stride, int tid) {
   constexpr int NS = D / 8;
@@ -203,12 +178,20 @@ __device__ __forceinline__ void issue_tile_async_off(const bf16_t* first, int64_
   static_assert(ROWS_PER_PASS % 16 == 0, "pass step must keep the swizzle");
   uint32_t off = lane_off;
   asm volatile("" : "+v"(off));
-  const uint32_t step = (uint32_t)(ROWS_PER_PASS * row_stride * 2);  // uniform
+  const uint64_t a = reinterpret_cast<uint64_t>(first);
+  // (readfirstlane returns a signed int: each half goes through uint32_t so
+  // that it is zero-extended)
+  const uint32_t a_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t a_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t base = ((uint64_t)a_hi << 32) | (uint64_t)a_lo;
+  const uint64_t step = (uint64_t)ROWS_PER_PASS * (uint64_t)row_stride * 2u;
   const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
-  const char* base = reinterpret_cast<const char*>(first);
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass)
-    async_copy16((base + (size_t)pass * step) + off, tile + pass * THREADS * 8 + lds_off);
+  for (int pass = 0; pass < PASSES; ++pass) {
+    uint64_t b = base + pass * step;
+    asm volatile("" : "+s"(b));  // the pass address stays in scalar registers
+    async_copy16(reinterpret_cast<const char*>(b) + off, tile + pass * THREADS * 8 + lds_off);
+  }
 }
 
 // Local (per-rank) key range of one block. The local buffer holds the rank's
