@@ -149,11 +149,16 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   constexpr int NW = kBwdThreads / 64;
   // Double buffers as distinct arrays: the chunk loop is unrolled by two so
   // the compiler can tell the next chunk's asynchronous LDS writes from the
-  // current chunk's reads (and does not wait for the copies to land).
-  __shared__ __attribute__((aligned(16))) bf16_t Qs0[kQC * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Qs1[kQC * D];
-  __shared__ __attribute__((aligned(16))) bf16_t dOs0[kQC * D];
-  __shared__ __attribute__((aligned(16))) bf16_t dOs1[kQC * D];
+  // current chunk's reads (and does not wait for the copies to land). The Q
+  // and dO tiles of one stage share an array (dO 16 KB after Q), so one
+  // per-lane read offset serves both with an immediate displacement; with
+  // four arrays the compiler kept a register per (array, offset) and spilled.
+  __shared__ __attribute__((aligned(16))) bf16_t QD0[2 * kQC * D];
+  __shared__ __attribute__((aligned(16))) bf16_t QD1[2 * kQC * D];
+  bf16_t* const Qs0 = QD0;
+  bf16_t* const dOs0 = QD0 + kQC * D;
+  bf16_t* const Qs1 = QD1;
+  bf16_t* const dOs1 = QD1 + kQC * D;
   __shared__ __attribute__((aligned(16))) float Ms0[4 * kQC];
   __shared__ __attribute__((aligned(16))) float Ms1[4 * kQC];
   __shared__ int list[kListCap];
