@@ -29,7 +29,8 @@ SPLITKV_OP_PLAN, SPLITKV_OP_FWD, SPLITKV_OP_BWD, SPLITKV_OP_MERGE = 0, 1, 2, 3
 
 SPLITKV_BASELINE_NO_BALANCE, SPLITKV_BASELINE_ZIGZAG = 0, 1
 
-EXPORTED = ("splitkv_workspace_bytes", "splitkv_plan", "splitkv_plan_baseline",
+EXPORTED = ("splitkv_workspace_bytes", "splitkv_validate_anchors", "splitkv_plan",
+            "splitkv_plan_baseline",
             "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
             "splitkv_delta", "splitkv_gemm", "splitkv_gemm_pair", "splitkv_cast_bf16",
             "splitkv_attn_bwd",
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
         A, H, Lc = ctypes.POINTER(Anchors), ctypes.POINTER(Heads), ctypes.POINTER(Local)
         L.splitkv_workspace_bytes.argtypes = [ctypes.c_int, A, H, Lc]
         L.splitkv_workspace_bytes.restype = sz
+        L.splitkv_validate_anchors.argtypes = [A, ctypes.c_int64, vp, vp]
+        L.splitkv_validate_anchors.restype = ctypes.c_int
         L.splitkv_plan.argtypes = [A, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_int32, vp, vp, vp, vp, vp]
         L.splitkv_plan.restype = ctypes.c_int
@@ -210,6 +213,20 @@ def splitkv_plan(s: torch.Tensor, a: torch.Tensor, block_size: int, S: int, m: i
 def baseline_range_count(strategy: int, n_samples: int, P: int) -> int:
     """Number of ranges splitkv_plan_baseline prices (P, or 2P per sample)."""
     return P if strategy == SPLITKV_BASELINE_NO_BALANCE else 2 * P * n_samples
+
+
+def splitkv_validate_anchors(s: torch.Tensor, a: torch.Tensor, block_size: int, S: int,
+                             out: Optional[torch.Tensor] = None,
+                             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Device-side check that every window [s_i, a_i) lies in [0, S) (empty
+    windows allowed). Returns a device int64 tensor [2]: the number of invalid
+    blocks and the index of the first one (-1 if none)."""
+    if out is None:
+        out = torch.empty(2, dtype=torch.int64, device=s.device)
+    an = make_anchors(s, a, block_size)
+    _check("splitkv_validate_anchors",
+           lib().splitkv_validate_anchors(ctypes.byref(an), int(S), _ptr(out), _stream(stream)))
+    return out
 
 
 def splitkv_plan_baseline(strategy: int, s: torch.Tensor, a: torch.Tensor, block_size: int,

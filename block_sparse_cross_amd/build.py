@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsplitkv.so")
-SOURCES = ["api.hip", "plan.hip", "merge.hip", "attn_fwd.hip", "attn_bwd.hip", "gemm.hip"]
+SOURCES = ["api.hip", "anchors.hip", "plan.hip", "merge.hip", "attn_fwd.hip", "attn_bwd.hip",
+           "gemm.hip"]
 ARCH = os.environ.get("SPLITKV_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

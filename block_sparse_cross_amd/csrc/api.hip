@@ -101,6 +101,14 @@ size_t splitkv_workspace_bytes(int op, const splitkv_anchors* an, const splitkv_
   }
 }
 
+int splitkv_validate_anchors(const splitkv_anchors* an, int64_t S, int64_t* result, void* stream) {
+  int st = check_anchors(an);
+  if (st != SPLITKV_OK) return st;
+  if (S < 0 || result == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  return hip_status(launch_validate_anchors(an->s, an->a, an->n_blocks, S, result,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int32_t J,
                  int64_t* chunk_cost, int32_t* chunk_owner, int32_t* rank_chunks,
                  int64_t* rank_load, void* stream) {

@@ -46,6 +46,9 @@ hipError_t launch_plan_baseline(int strategy, const int64_t* s, const int64_t* a
                                 int32_t P, int64_t S, int64_t* range_cost, int64_t* rank_load,
                                 hipStream_t stream);
 
+hipError_t launch_validate_anchors(const int64_t* s, const int64_t* a, int64_t n_blocks,
+                                   int64_t S, int64_t* result, hipStream_t stream);
+
 hipError_t launch_block_ranges(const int64_t* s, const int64_t* a, int64_t n_blocks,
                                const int64_t* chunk_start, int32_t n_chunks, int64_t m,
                                int2* block_range, hipStream_t stream);

@@ -86,6 +86,15 @@ typedef struct {
 size_t splitkv_workspace_bytes(int op, const splitkv_anchors* an, const splitkv_heads* hd,
                                const splitkv_local* loc);
 
+/* Device-side check of the anchor metadata (a debugging aid; no other entry
+ * point reads anchors on the host). Block i's rows attend [s_i, a_i) of their
+ * own sample (§3.1, Figure 1), so block i is valid when
+ *   0 <= s[i] <= a[i] <= S     (an empty window, s[i] == a[i], is valid).
+ * result: device int64 [2], overwritten with the number of invalid blocks and
+ * the index of the first one (-1 if none); read it once the stream has reached
+ * the call. Requires S >= 0 and result != NULL; n_blocks == 0 gives {0, -1}. */
+int splitkv_validate_anchors(const splitkv_anchors* an, int64_t S, int64_t* result, void* stream);
+
 /* Chunk pricing (Eq. 6) and cost-aware LPT (§4.2).
  *   cost[j]  = B * sum_i ( min(a_i, j*m + m) - max(s_i, j*m) )^+, j < P*J   (int64)
  *   Chunks are taken by cost, highest first (equal costs: lower j first); each

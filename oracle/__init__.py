@@ -46,6 +46,7 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(_LIB):
             build(force=True)
         L = ctypes.CDLL(_LIB)
+        L.oracle_validate_anchors.argtypes = [ctypes.c_int64, i64p, i64p, ctypes.c_int64, i64p]
         L.oracle_anchor_profile.argtypes = [ctypes.c_int64, i64p, i64p, ctypes.c_int64,
                                             ctypes.c_int64, i64p]
         for name in ("oracle_chunk_costs", "oracle_chunk_costs_prefix"):
@@ -100,6 +101,18 @@ def _f64(x) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- planner --
+def validate_anchors(s, a, S: int) -> Tuple[int, int]:
+    """(number of blocks whose window [s_i, a_i) is not inside [0, S), index of
+    the first such block or -1): §3.1 / Figure 1 of the Split-KV paper."""
+    s, a = _i64(s), _i64(a)
+    if len(s) != len(a):
+        raise ValueError("s and a differ in length")
+    out = np.zeros(2, np.int64)
+    lib().oracle_validate_anchors(len(s), _p(s, ctypes.c_int64), _p(a, ctypes.c_int64), int(S),
+                                  _p(out, ctypes.c_int64))
+    return int(out[0]), int(out[1])
+
+
 def anchor_profile(s, a, B: int, S: int) -> np.ndarray:
     s, a = _i64(s), _i64(a)
     out = np.zeros(S, dtype=np.int64)

@@ -17,6 +17,7 @@
  *   §4.2 (balance)      D = (N/P) B^2, W_p = C_p + D, rho = max W / mean W
  *   §3.3, Figure 5(b)   Zigzag: 2P chunks per sample, rank p gets p and 2P-1-p
  *   §4.1, Algorithm 1   MERGE in per-rank form: LSE reduction, then rescaling
+ *   §3.1, Figure 1      a valid anchor window lies inside the packed context
  *
  * Floating point is fp64 throughout, inputs included: the tests widen the exact
  * bf16/fp32 values the GPU consumed to fp64 before calling in.
@@ -32,6 +33,25 @@
 
 static int64_t max64(int64_t x, int64_t y) { return x > y ? x : y; }
 static int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
+
+/* ------------------------------------------------------------------------- */
+/* §3.1, Figure 1: block i's rows see the context window [s_i, a_i) of their   */
+/* sample, a sub-interval of the packed context [0, S) (empty allowed).        */
+/* out = {number of blocks violating 0 <= s_i <= a_i <= S, first such i or -1}. */
+/* ------------------------------------------------------------------------- */
+EXPORT void oracle_validate_anchors(int64_t n_blocks, const int64_t* s, const int64_t* a,
+                                    int64_t S, int64_t* out) {
+    int64_t bad = 0, first = -1;
+    for (int64_t i = 0; i < n_blocks; ++i) {
+        int ok = 0 <= s[i] && s[i] <= a[i] && a[i] <= S;
+        if (!ok) {
+            if (first < 0) first = i;
+            bad += 1;
+        }
+    }
+    out[0] = bad;
+    out[1] = first;
+}
 
 /* ------------------------------------------------------------------------- */
 /* Eq. 2: c(x) = B * #{ i : s_i <= x < a_i }, x in [0, S). Brute force.       */
