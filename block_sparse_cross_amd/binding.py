@@ -30,7 +30,7 @@ SPLITKV_OP_PLAN, SPLITKV_OP_FWD, SPLITKV_OP_BWD, SPLITKV_OP_MERGE = 0, 1, 2, 3
 SPLITKV_BASELINE_NO_BALANCE, SPLITKV_BASELINE_ZIGZAG = 0, 1
 
 EXPORTED = ("splitkv_workspace_bytes", "splitkv_validate_anchors", "splitkv_plan",
-            "splitkv_plan_baseline",
+            "splitkv_locality_match", "splitkv_plan_baseline",
             "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
             "splitkv_delta", "splitkv_gemm", "splitkv_gemm_pair", "splitkv_cast_bf16",
             "splitkv_attn_bwd",
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.splitkv_workspace_bytes.restype = sz
         L.splitkv_validate_anchors.argtypes = [A, ctypes.c_int64, vp, vp]
         L.splitkv_validate_anchors.restype = ctypes.c_int
+        L.splitkv_locality_match.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                             vp, vp, vp, vp]
+        L.splitkv_locality_match.restype = ctypes.c_int
         L.splitkv_plan.argtypes = [A, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_int32, vp, vp, vp, vp, vp]
         L.splitkv_plan.restype = ctypes.c_int
@@ -226,6 +229,28 @@ def splitkv_validate_anchors(s: torch.Tensor, a: torch.Tensor, block_size: int, 
     an = make_anchors(s, a, block_size)
     _check("splitkv_validate_anchors",
            lib().splitkv_validate_anchors(ctypes.byref(an), int(S), _ptr(out), _stream(stream)))
+    return out
+
+
+def splitkv_locality_match(rank_chunks: torch.Tensor, m: int,
+                           out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                           stream: Optional[torch.cuda.Stream] = None):
+    """Place a plan's bundles (device int32 [P][J], as splitkv_plan returns them)
+    on physical ranks keeping the most context rows in place (§4.2). Returns
+    device tensors (phys_rank int32 [P], send_rows int64 [P][P], kept_moved
+    int64 [2])."""
+    if rank_chunks.dim() != 2 or rank_chunks.dtype != torch.int32 or not rank_chunks.is_contiguous():
+        raise ValueError("rank_chunks must be a contiguous int32 [P][J] tensor")
+    P, J = rank_chunks.shape
+    dev = rank_chunks.device
+    if out is None:
+        out = (torch.empty(P, dtype=torch.int32, device=dev),
+               torch.empty((P, P), dtype=torch.int64, device=dev),
+               torch.empty(2, dtype=torch.int64, device=dev))
+    perm, send, km = out
+    _check("splitkv_locality_match",
+           lib().splitkv_locality_match(_ptr(rank_chunks), int(P), int(J), int(m), _ptr(perm),
+                                        _ptr(send), _ptr(km), _stream(stream)))
     return out
 
 

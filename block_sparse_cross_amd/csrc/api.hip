@@ -128,6 +128,19 @@ int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int
                                 static_cast<hipStream_t>(stream)));
 }
 
+int splitkv_locality_match(const int32_t* rank_chunks, int32_t P, int32_t J, int64_t m,
+                           int32_t* phys_rank, int64_t* send_rows, int64_t* kept_moved,
+                           void* stream) {
+  if (P < 1 || J < 1 || m < 1) return SPLITKV_ERR_INVALID_ARG;
+  if (rank_chunks == nullptr || phys_rank == nullptr || send_rows == nullptr ||
+      kept_moved == nullptr)
+    return SPLITKV_ERR_INVALID_ARG;
+  if (P > kMaxMatchRanks || (int64_t)P * J > kMaxPlanChunks) return SPLITKV_ERR_UNSUPPORTED;
+  if ((__int128)P * J * m >= ((__int128)1 << 62)) return SPLITKV_ERR_UNSUPPORTED;
+  return hip_status(launch_locality_match(rank_chunks, P, J, m, phys_rank, send_rows, kept_moved,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int splitkv_plan_baseline(int strategy, const splitkv_anchors* an, int32_t n_samples,
                           const int64_t* sample_start, const int64_t* sample_len, int32_t P,
                           int64_t* range_cost, int64_t* rank_load, void* stream) {

@@ -15,6 +15,7 @@ constexpr int kMaxPlanRanks = 1024;
 constexpr int kMaxPlanChunks = 4096;
 constexpr int kBwdChunk = 64;  // query vectors per chunk of the dK/dV kernel
 constexpr int kMaxBaselineSamples = 128;
+constexpr int kMaxMatchRanks = 256;  // ranks of a locality matching
 
 // Packed sample table of a position-based assignment, passed by value.
 struct BaselineSamples {
@@ -45,6 +46,10 @@ hipError_t launch_plan_baseline(int strategy, const int64_t* s, const int64_t* a
                                 int64_t n_blocks, int32_t B, const BaselineSamples& samples,
                                 int32_t P, int64_t S, int64_t* range_cost, int64_t* rank_load,
                                 hipStream_t stream);
+
+hipError_t launch_locality_match(const int32_t* rank_chunks, int32_t P, int32_t J, int64_t m,
+                                 int32_t* phys_rank, int64_t* send_rows, int64_t* kept_moved,
+                                 hipStream_t stream);
 
 hipError_t launch_validate_anchors(const int64_t* s, const int64_t* a, int64_t n_blocks,
                                    int64_t S, int64_t* result, hipStream_t stream);

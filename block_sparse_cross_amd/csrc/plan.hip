@@ -266,7 +266,146 @@ lpt_kernel(const int64_t* __restrict__ cost, int n_chunks, int P, int J,
   for (int t = threadIdx.x; t < n_chunks; t += blockDim.x) rank_chunks[t] = idx[t];
 }
 
+// Locality matching (§4.2): the bundles of a plan are placed on physical
+// ranks without changing any load, keeping as many context rows where they
+// already are as possible. Before the step's all-to-all, physical rank r holds
+// the r-th of P equal contiguous parts of [0, S) (S = P J m), i.e. chunks
+// r J .. r J + J - 1; placing bundle b on rank r keeps
+//   keep(b, r) = m * #{ chunks of b whose home is r }
+// rows. The best placement is a linear assignment problem, solved exactly by
+// the Hungarian method: row (bundle) and column (rank) potentials on the cost
+// -keep, bundles entering one at a time along a shortest augmenting path. One
+// workgroup; thread t owns column t (column 0 is the virtual start column).
+// Each step scans the free columns in parallel and takes the smallest reduced
+// cost, the lowest column on ties (wave shuffles, then the wave minima in
+// LDS), so the result is unique. Chunk ids outside [0, P J) count as neither
+// kept nor sent.
+constexpr int kMatchThreads = 512;
+static_assert(kMatchThreads > kMaxMatchRanks, "one thread per column plus the virtual one");
+
+__global__ void __launch_bounds__(kMatchThreads)
+locality_match_kernel(const int32_t* __restrict__ bundles, int P, int J, int64_t m,
+                      int32_t* __restrict__ perm, int64_t* __restrict__ send,
+                      int64_t* __restrict__ kept_moved) {
+  __shared__ int32_t bl[kMaxPlanChunks];
+  __shared__ int64_t u[kMaxMatchRanks + 1], v[kMaxMatchRanks + 1], minv[kMaxMatchRanks + 1];
+  __shared__ int32_t match[kMaxMatchRanks + 1], way[kMaxMatchRanks + 1];
+  __shared__ int32_t used[kMaxMatchRanks + 1];
+  __shared__ int32_t placed[kMaxMatchRanks];
+  __shared__ long long wbest[kMatchThreads / kWave];
+  __shared__ int32_t wcol[kMatchThreads / kWave];
+  __shared__ long long s_delta;
+  __shared__ int32_t s_col;
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int PJ = P * J;
+  const long long kInf = INT64_MAX / 4;
+  for (int x = t; x < PJ; x += kMatchThreads) bl[x] = bundles[x];
+  if (t <= P) { u[t] = 0; v[t] = 0; match[t] = 0; way[t] = 0; }
+  if (t < P) placed[t] = t;
+  __syncthreads();
+  auto keep = [&](int b, int r) -> long long {
+    long long n = 0;
+    for (int k = 0; k < J; ++k) {
+      const int j = bl[b * J + k];
+      n += (j >= 0 && j < PJ && j / J == r) ? 1 : 0;
+    }
+    return n * m;
+  };
+
+  for (int i = 1; i <= P; ++i) {
+    if (t <= P) { minv[t] = kInf; used[t] = 0; }
+    if (t == 0) match[0] = i;
+    int j0 = 0;
+    __syncthreads();
+    // at most P steps: every step uses up one more of the P real columns
+    for (int step = 0; step <= P; ++step) {
+      if (t == 0) used[j0] = 1;
+      __syncthreads();
+      const int i0 = match[j0];
+      long long best = kInf;
+      int col = 0x7fffffff;
+      if (t >= 1 && t <= P && !used[t]) {
+        const long long cur = -keep(i0 - 1, t - 1) - u[i0] - v[t];
+        if (cur < minv[t]) { minv[t] = cur; way[t] = j0; }
+        best = minv[t];
+        col = t;
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        const long long ob = __shfl_xor(best, off);
+        const int oc = __shfl_xor(col, off);
+        if (ob < best || (ob == best && oc < col)) { best = ob; col = oc; }
+      }
+      if (lane == 0) { wbest[wave] = best; wcol[wave] = col; }
+      __syncthreads();
+      if (t == 0) {
+        long long b = wbest[0];
+        int c = wcol[0];
+        for (int w = 1; w < kMatchThreads / kWave; ++w)
+          if (wbest[w] < b || (wbest[w] == b && wcol[w] < c)) { b = wbest[w]; c = wcol[w]; }
+        s_delta = b;
+        s_col = c;
+      }
+      __syncthreads();
+      const long long delta = s_delta;
+      const int j1 = s_col;
+      if (t <= P) {
+        if (used[t]) { u[match[t]] += delta; v[t] -= delta; }
+        else minv[t] -= delta;
+      }
+      __syncthreads();
+      j0 = j1;
+      if (j0 > P || match[j0] == 0) break;
+    }
+    if (t == 0) {  // flip the augmenting path back to column 0
+      for (int step = 0; step <= P && j0 != 0 && j0 <= P; ++step) {
+        const int j1 = way[j0];
+        match[j0] = match[j1];
+        j0 = j1;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (t >= 1 && t <= P) {
+    const int b = match[t] - 1;  // the matching is perfect: every bundle is placed once
+    if (b >= 0 && b < P) placed[b] = t - 1;
+  }
+  for (int x = t; x < P * P; x += kMatchThreads) send[x] = 0;
+  __syncthreads();
+  if (t < P) perm[t] = placed[t];
+  long long kept = 0;
+  if (t < P) {
+    const int dst = placed[t];
+    kept = keep(t, dst);
+    for (int k = 0; k < J; ++k) {  // the rank that receives bundle t owns send[.][dst]
+      const int j = bl[t * J + k];
+      if (j < 0 || j >= PJ) continue;
+      const int src = j / J;
+      if (src != dst) send[(int64_t)src * P + dst] += m;
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) kept += __shfl_xor(kept, off);
+  if (lane == 0) wbest[wave] = kept;
+  __syncthreads();
+  if (t == 0) {
+    long long total = 0;
+    for (int w = 0; w < kMatchThreads / kWave; ++w) total += wbest[w];
+    kept_moved[0] = total;
+    kept_moved[1] = (long long)PJ * m - total;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_locality_match(const int32_t* rank_chunks, int32_t P, int32_t J, int64_t m,
+                                 int32_t* phys_rank, int64_t* send_rows, int64_t* kept_moved,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(locality_match_kernel, dim3(1), dim3(kMatchThreads), 0, stream, rank_chunks,
+                     P, J, m, phys_rank, send_rows, kept_moved);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan_baseline(int strategy, const int64_t* s, const int64_t* a,
                                 int64_t n_blocks, int32_t B, const BaselineSamples& samples,

@@ -110,6 +110,24 @@ int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int
                  int64_t* chunk_cost, int32_t* chunk_owner, int32_t* rank_chunks,
                  int64_t* rank_load, void* stream);
 
+/* Locality matching (§4.2): places the plan's bundles (rank_chunks of
+ * splitkv_plan: device int32 [P][J] chunk ids) on physical ranks without
+ * changing any load, so that the step's all-to-all moves as few context rows
+ * as possible. Before the all-to-all, physical rank r holds the r-th of P
+ * equal contiguous parts of [0, S), S = P*J*m (chunks r*J .. r*J + J - 1);
+ * placing bundle b on rank r keeps m * #{chunks of b whose home is r} rows in
+ * place. The placement maximises the rows kept (a linear assignment, solved
+ * exactly; of equally good choices the one the Hungarian method reaches with
+ * lowest-index tie-breaks, so the result is unique).
+ * Outputs (device): phys_rank int32 [P] (bundle b runs on rank phys_rank[b]),
+ *   send_rows int64 [P][P] (rows rank src sends to rank dst, zero diagonal),
+ *   kept_moved int64 [2] = {rows kept in place, rows moved}.
+ * Requires P <= 256, P*J <= 4096. Chunk ids outside [0, P*J) count as neither
+ * kept nor sent. Integer only. */
+int splitkv_locality_match(const int32_t* rank_chunks, int32_t P, int32_t J, int64_t m,
+                           int32_t* phys_rank, int64_t* send_rows, int64_t* kept_moved,
+                           void* stream);
+
 /* The two position-based assignments the cost-aware plan is measured against
  * (§3.3 and Figure 5(b) for Zigzag; §5.5 and Figure 9 for No balance). */
 typedef enum {

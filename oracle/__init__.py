@@ -47,6 +47,9 @@ def lib() -> ctypes.CDLL:
             build(force=True)
         L = ctypes.CDLL(_LIB)
         L.oracle_validate_anchors.argtypes = [ctypes.c_int64, i64p, i64p, ctypes.c_int64, i64p]
+        L.oracle_locality_match.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            i32p, i64p, i64p]
+        L.oracle_locality_match.restype = ctypes.c_int
         L.oracle_anchor_profile.argtypes = [ctypes.c_int64, i64p, i64p, ctypes.c_int64,
                                             ctypes.c_int64, i64p]
         for name in ("oracle_chunk_costs", "oracle_chunk_costs_prefix"):
@@ -148,6 +151,24 @@ def plan(s, a, B: int, S: int, m: int, P: int, J: int):
     cost = chunk_costs(s, a, B, S // m, m)
     owner, bundles, load = lpt(cost, P, J)
     return cost, owner, bundles, load
+
+
+def locality_match(bundles, m: int):
+    """Locality matching of §4.2: place the LPT bundles (int [P][J] chunk ids)
+    on physical ranks keeping the most context rows in place, where rank r
+    first holds chunks r*J .. r*J + J - 1. Returns (perm [P]: bundle -> rank,
+    send int64 [P][P]: rows rank src sends to rank dst, kept, moved)."""
+    b = np.ascontiguousarray(bundles, dtype=np.int32)
+    P, J = b.shape
+    perm = np.zeros(P, np.int32)
+    send = np.zeros((P, P), np.int64)
+    km = np.zeros(2, np.int64)
+    rc = lib().oracle_locality_match(_p(b, ctypes.c_int32), P, J, int(m),
+                                     _p(perm, ctypes.c_int32), _p(send, ctypes.c_int64),
+                                     _p(km, ctypes.c_int64))
+    if rc != 0:
+        raise ValueError("oracle_locality_match: invalid arguments")
+    return perm, send, int(km[0]), int(km[1])
 
 
 def zigzag_loads(sample_start, sample_len, prof, P: int) -> np.ndarray:

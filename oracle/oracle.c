@@ -18,6 +18,7 @@
  *   §3.3, Figure 5(b)   Zigzag: 2P chunks per sample, rank p gets p and 2P-1-p
  *   §4.1, Algorithm 1   MERGE in per-rank form: LSE reduction, then rescaling
  *   §3.1, Figure 1      a valid anchor window lies inside the packed context
+ *   §4.2 (placement)    locality matching of the LPT bundles to physical ranks
  *
  * Floating point is fp64 throughout, inputs included: the tests widen the exact
  * bf16/fp32 values the GPU consumed to fp64 before calling in.
@@ -147,6 +148,87 @@ EXPORT int oracle_lpt(int64_t n_chunks, const int64_t* cost, int32_t P, int32_t 
     }
     free(order);
     free(count);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Locality matching (§4.2): the LPT bundles are placed on physical ranks     */
+/* without changing their loads, keeping as many context rows in place as     */
+/* possible. Reading: before the step's all-to-all, physical rank r holds the */
+/* r-th of P equal contiguous parts of [0, S), S = P*J*m, so chunk j starts   */
+/* on rank j / J. keep[b][r] = m * #{ chunks j of bundle b : j / J == r }.    */
+/* The placement maximises sum_b keep[b][perm[b]]: a linear assignment       */
+/* problem, solved exactly by the Hungarian method with row and column        */
+/* potentials on the cost -keep (rows = bundles, columns = ranks; each row    */
+/* enters by a shortest augmenting path; of equal reduced costs the lowest    */
+/* column is taken). Outputs: perm[b] = physical rank of bundle b; send[src*P */
+/* + dst] = rows rank src sends to rank dst (m per chunk of the bundle placed */
+/* on dst whose home is src != dst); kept_moved = {rows in place, S - kept}.  */
+/* Chunk ids outside [0, P*J) count as neither kept nor sent.                 */
+/* ------------------------------------------------------------------------- */
+static int64_t keep_rows(const int32_t* bundles, int32_t J, int64_t m, int32_t PJ, int32_t b,
+                         int32_t r) {
+    int64_t n = 0;
+    for (int32_t k = 0; k < J; ++k) {
+        int32_t j = bundles[(int64_t)b * J + k];
+        if (j >= 0 && j < PJ && j / J == r) n += 1;
+    }
+    return n * m;
+}
+
+EXPORT int oracle_locality_match(const int32_t* bundles, int32_t P, int32_t J, int64_t m,
+                                 int32_t* perm, int64_t* send, int64_t* kept_moved) {
+    if (P <= 0 || J <= 0 || m <= 0) return -1;
+    const int32_t PJ = P * J;
+    const int64_t INF = INT64_MAX / 4;
+    int64_t* u = (int64_t*)calloc(P + 1, sizeof(int64_t));
+    int64_t* v = (int64_t*)calloc(P + 1, sizeof(int64_t));
+    int64_t* minv = (int64_t*)malloc(sizeof(int64_t) * (P + 1));
+    int32_t* match = (int32_t*)calloc(P + 1, sizeof(int32_t)); /* column -> row, 0 = free */
+    int32_t* way = (int32_t*)calloc(P + 1, sizeof(int32_t));
+    char* used = (char*)malloc(P + 1);
+    for (int32_t i = 1; i <= P; ++i) {
+        match[0] = i;
+        int32_t j0 = 0;
+        for (int32_t j = 0; j <= P; ++j) { minv[j] = INF; used[j] = 0; }
+        do {
+            used[j0] = 1;
+            int32_t i0 = match[j0], j1 = 0;
+            int64_t delta = INF;
+            for (int32_t j = 1; j <= P; ++j) {
+                if (used[j]) continue;
+                int64_t cur = -keep_rows(bundles, J, m, PJ, i0 - 1, j - 1) - u[i0] - v[j];
+                if (cur < minv[j]) { minv[j] = cur; way[j] = j0; }
+                if (minv[j] < delta) { delta = minv[j]; j1 = j; }
+            }
+            for (int32_t j = 0; j <= P; ++j) {
+                if (used[j]) { u[match[j]] += delta; v[j] -= delta; }
+                else minv[j] -= delta;
+            }
+            j0 = j1;
+        } while (match[j0] != 0);
+        do {
+            int32_t j1 = way[j0];
+            match[j0] = match[j1];
+            j0 = j1;
+        } while (j0 != 0);
+    }
+    for (int32_t j = 1; j <= P; ++j) perm[match[j] - 1] = j - 1;
+    for (int64_t x = 0; x < (int64_t)P * P; ++x) send[x] = 0;
+    int64_t kept = 0;
+    for (int32_t b = 0; b < P; ++b) {
+        int32_t dst = perm[b];
+        kept += keep_rows(bundles, J, m, PJ, b, dst);
+        for (int32_t k = 0; k < J; ++k) {
+            int32_t j = bundles[(int64_t)b * J + k];
+            if (j < 0 || j >= PJ) continue;
+            int32_t src = j / J;
+            if (src != dst) send[(int64_t)src * P + dst] += m;
+        }
+    }
+    kept_moved[0] = kept;
+    kept_moved[1] = (int64_t)PJ * m - kept;
+    free(u); free(v); free(minv); free(match); free(way); free(used);
     return 0;
 }
 

@@ -1,0 +1,64 @@
+"""splitkv_locality_match (placement of the LPT bundles on physical ranks,
+§4.2) against the oracle: the same Hungarian tie rule makes the placement
+unique, so perm, send rows and kept/moved must agree bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_cross_amd import binding, inputs
+from tests.helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_match(bundles, m):
+    perm, send, km = binding.splitkv_locality_match(to_dev(np.asarray(bundles, np.int32)), m)
+    torch.cuda.synchronize()
+    return perm.cpu().numpy(), send.cpu().numpy(), km.cpu().numpy()
+
+
+def assert_same(bundles, m):
+    perm, send, km = gpu_match(bundles, m)
+    p_ref, s_ref, kept, moved = oracle.locality_match(bundles, m)
+    np.testing.assert_array_equal(perm, p_ref)
+    np.testing.assert_array_equal(send, s_ref)
+    assert km.tolist() == [kept, moved]
+
+
+@pytest.mark.parametrize("P,J", [(1, 1), (2, 2), (3, 5), (8, 4), (16, 8), (64, 8), (256, 16)])
+def test_random_bundles(P, J):
+    g = np.random.default_rng(P * 100 + J)
+    for trial in range(3):
+        b = g.permutation(P * J).reshape(P, J)
+        if trial == 1:
+            b = np.arange(P * J).reshape(P, J)[g.permutation(P)]  # a permuted home layout
+        assert_same(b, 4096)
+
+
+def test_ids_outside_the_plan_are_ignored():
+    b = np.arange(24).reshape(6, 4)
+    b[1, 2], b[4, 0] = -1, 10_000
+    assert_same(b, 7)
+
+
+@pytest.mark.parametrize("name,P,J", [("weak8", 8, 4), ("cp64", 64, 8), ("cp16", 16, 8)])
+def test_lpt_plans(name, P, J):
+    if name == "weak8":
+        w = inputs.WORKLOADS["weak8"]
+    else:   # the CP-size study workloads of §5.5: 4 samples x 256k
+        w = inputs.Workload(name, b=4, L=262144, A=512, B=16, hq=32, hkv=8, d=128,
+                            dtype="bf16", scale=1.0, P=P, m=(4 * 262144) // (P * J))
+    s, a = inputs.workload_anchors(w, 0)
+    _, _, bundles, _ = binding.splitkv_plan(to_dev(s), to_dev(a), w.B, w.S, w.m, P, J)
+    torch.cuda.synchronize()
+    assert_same(bundles.cpu().numpy(), w.m)
+
+
+def test_invalid_arguments():
+    with pytest.raises(binding.SplitKVError):
+        binding.splitkv_locality_match(torch.zeros((257, 1), dtype=torch.int32, device="cuda"), 8)
+    with pytest.raises(binding.SplitKVError):
+        binding.splitkv_locality_match(torch.zeros((4, 2), dtype=torch.int32, device="cuda"), 0)
+    with pytest.raises(ValueError):
+        binding.splitkv_locality_match(torch.zeros((4, 2), dtype=torch.int64, device="cuda"), 8)
