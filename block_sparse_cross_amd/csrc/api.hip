@@ -136,7 +136,8 @@ int splitkv_locality_match(const int32_t* rank_chunks, int32_t P, int32_t J, int
       kept_moved == nullptr)
     return SPLITKV_ERR_INVALID_ARG;
   if (P > kMaxMatchRanks || (int64_t)P * J > kMaxPlanChunks) return SPLITKV_ERR_UNSUPPORTED;
-  if ((__int128)P * J * m >= ((__int128)1 << 62)) return SPLITKV_ERR_UNSUPPORTED;
+  // slacks stay below (P + 1) * J * m and are packed above 9 column bits
+  if ((__int128)(P + 1) * P * J * m >= ((__int128)1 << 54)) return SPLITKV_ERR_UNSUPPORTED;
   return hip_status(launch_locality_match(rank_chunks, P, J, m, phys_rank, send_rows, kept_moved,
                                           static_cast<hipStream_t>(stream)));
 }

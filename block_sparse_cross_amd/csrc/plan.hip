@@ -274,112 +274,137 @@ lpt_kernel(const int64_t* __restrict__ cost, int n_chunks, int P, int J,
 //   keep(b, r) = m * #{ chunks of b whose home is r }
 // rows. The best placement is a linear assignment problem, solved exactly by
 // the Hungarian method: row (bundle) and column (rank) potentials on the cost
-// -keep, bundles entering one at a time along a shortest augmenting path. One
-// workgroup; thread t owns column t (column 0 is the virtual start column).
-// Each step scans the free columns in parallel and takes the smallest reduced
-// cost, the lowest column on ties (wave shuffles, then the wave minima in
-// LDS), so the result is unique. Chunk ids outside [0, P J) count as neither
-// kept nor sent.
-constexpr int kMatchThreads = 512;
-static_assert(kMatchThreads > kMaxMatchRanks, "one thread per column plus the virtual one");
+// J m - keep >= 0 (the constant leaves the best placement unchanged, and with
+// non-negative costs every slack stays >= 0), bundles entering one at a time
+// along a shortest augmenting path.
+//
+// One wave. Lane l keeps, in registers, column l + 1 + 64 k and row
+// l + 1 + 64 k (k < kMatchSlots): the column's potential, slack (minv),
+// predecessor (way), used flag and matched row, and the row's potential and
+// tree flag (a row is in the tree once the column it is matched to is used;
+// those rows take + delta, the used columns - delta). The keep counts sit in
+// LDS as a [P][P] table. A step scans the lane's free columns (ascending, so
+// ties keep the lowest) and packs (slack, column) into one 64-bit key whose
+// wave minimum (DPP steps and four lane reads, no LDS) is the smallest slack
+// at the lowest column: the result is unique. Single values of other lanes are read with readlane at a uniform
+// lane. Chunk ids outside [0, P J) count as neither kept nor sent.
+constexpr int kMatchThreads = kWave;
+constexpr int kMatchSlots = kMaxMatchRanks / kWave;
+constexpr int kColBits = 9;  // columns 1 .. 256 in the low bits of a wave-minimum key
+static_assert(kMaxMatchRanks < (1 << kColBits), "column must fit its key bits");
 
 __global__ void __launch_bounds__(kMatchThreads)
 locality_match_kernel(const int32_t* __restrict__ bundles, int P, int J, int64_t m,
                       int32_t* __restrict__ perm, int64_t* __restrict__ send,
                       int64_t* __restrict__ kept_moved) {
   __shared__ int32_t bl[kMaxPlanChunks];
-  __shared__ int64_t u[kMaxMatchRanks + 1], v[kMaxMatchRanks + 1], minv[kMaxMatchRanks + 1];
-  __shared__ int32_t match[kMaxMatchRanks + 1], way[kMaxMatchRanks + 1];
-  __shared__ int32_t used[kMaxMatchRanks + 1];
+  __shared__ uint16_t keepc[kMaxMatchRanks * kMaxMatchRanks];  // [bundle][home rank] chunk counts
   __shared__ int32_t placed[kMaxMatchRanks];
-  __shared__ long long wbest[kMatchThreads / kWave];
-  __shared__ int32_t wcol[kMatchThreads / kWave];
-  __shared__ long long s_delta;
-  __shared__ int32_t s_col;
-  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int lane = threadIdx.x;
   const int PJ = P * J;
   const long long kInf = INT64_MAX / 4;
-  for (int x = t; x < PJ; x += kMatchThreads) bl[x] = bundles[x];
-  if (t <= P) { u[t] = 0; v[t] = 0; match[t] = 0; way[t] = 0; }
-  if (t < P) placed[t] = t;
+  for (int x = lane; x < PJ; x += kMatchThreads) bl[x] = bundles[x];
+  for (int x = lane; x < P * P; x += kMatchThreads) keepc[x] = 0;
+  for (int x = lane; x < P; x += kMatchThreads) placed[x] = x;
   __syncthreads();
-  auto keep = [&](int b, int r) -> long long {
-    long long n = 0;
+  for (int bb = lane; bb < P; bb += kMatchThreads)  // lane owns row bb of the table
     for (int k = 0; k < J; ++k) {
-      const int j = bl[b * J + k];
-      n += (j >= 0 && j < PJ && j / J == r) ? 1 : 0;
+      const int j = bl[bb * J + k];
+      if (j >= 0 && j < PJ) keepc[bb * P + j / J] += 1;
     }
-    return n * m;
+  __syncthreads();
+
+  long long v[kMatchSlots], minv[kMatchSlots], u[kMatchSlots];
+  int way[kMatchSlots], match[kMatchSlots];
+  bool used[kMatchSlots], tree[kMatchSlots];
+#pragma unroll
+  for (int k = 0; k < kMatchSlots; ++k) { v[k] = 0; u[k] = 0; match[k] = 0; way[k] = 0; }
+  // value of register array x for global index g (1-based), read from its lane
+  auto lane_of = [](int g) { return (g - 1) % kWave; };
+  auto slot_of = [](int g) { return (g - 1) / kWave; };
+  auto read_i = [&](const int (&x)[kMatchSlots], int g) {
+    const int k = slot_of(g);
+    int val = x[0];
+#pragma unroll
+    for (int q = 1; q < kMatchSlots; ++q) val = (k == q) ? x[q] : val;
+    return __builtin_amdgcn_readlane(val, lane_of(g));
+  };
+  auto read_l = [&](const long long (&x)[kMatchSlots], int g) {
+    const int k = slot_of(g);
+    long long val = x[0];
+#pragma unroll
+    for (int q = 1; q < kMatchSlots; ++q) val = (k == q) ? x[q] : val;
+    const int lo = __builtin_amdgcn_readlane((int)(val & 0xffffffffll), lane_of(g));
+    const int hi = __builtin_amdgcn_readlane((int)(val >> 32), lane_of(g));
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
   };
 
   for (int i = 1; i <= P; ++i) {
-    if (t <= P) { minv[t] = kInf; used[t] = 0; }
-    if (t == 0) match[0] = i;
+#pragma unroll
+    for (int k = 0; k < kMatchSlots; ++k) { minv[k] = kInf; used[k] = false; tree[k] = false; }
     int j0 = 0;
-    __syncthreads();
     // at most P steps: every step uses up one more of the P real columns
     for (int step = 0; step <= P; ++step) {
-      if (t == 0) used[j0] = 1;
-      __syncthreads();
-      const int i0 = match[j0];
+      const int i0 = j0 == 0 ? i : read_i(match, j0);
+#pragma unroll
+      for (int k = 0; k < kMatchSlots; ++k) {
+        if (j0 != 0 && lane == lane_of(j0) && k == slot_of(j0)) used[k] = true;
+        if (lane == lane_of(i0) && k == slot_of(i0)) tree[k] = true;
+      }
+      const long long ui0 = read_l(u, i0);
       long long best = kInf;
       int col = 0x7fffffff;
-      if (t >= 1 && t <= P && !used[t]) {
-        const long long cur = -keep(i0 - 1, t - 1) - u[i0] - v[t];
-        if (cur < minv[t]) { minv[t] = cur; way[t] = j0; }
-        best = minv[t];
-        col = t;
-      }
 #pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        const long long ob = __shfl_xor(best, off);
-        const int oc = __shfl_xor(col, off);
-        if (ob < best || (ob == best && oc < col)) { best = ob; col = oc; }
+      for (int k = 0; k < kMatchSlots; ++k) {
+        const int c = lane + 1 + kWave * k;
+        if (c > P || used[k]) continue;
+        const long long cur = (long long)(J - keepc[(i0 - 1) * P + (c - 1)]) * m - ui0 - v[k];
+        if (cur < minv[k]) { minv[k] = cur; way[k] = j0; }
+        if (minv[k] < best) { best = minv[k]; col = c; }
       }
-      if (lane == 0) { wbest[wave] = best; wcol[wave] = col; }
-      __syncthreads();
-      if (t == 0) {
-        long long b = wbest[0];
-        int c = wcol[0];
-        for (int w = 1; w < kMatchThreads / kWave; ++w)
-          if (wbest[w] < b || (wbest[w] == b && wcol[w] < c)) { b = wbest[w]; c = wcol[w]; }
-        s_delta = b;
-        s_col = c;
+      const unsigned long long key =
+          col > P ? kNoKey : (((unsigned long long)best << kColBits) | (unsigned)col);
+      const unsigned long long wkey = wave_min_key(key);
+      const long long delta = (long long)(wkey >> kColBits);
+      col = wkey == kNoKey ? 0x7fffffff : (int)(wkey & ((1u << kColBits) - 1));
+#pragma unroll
+      for (int k = 0; k < kMatchSlots; ++k) {
+        const int c = lane + 1 + kWave * k;
+        if (c <= P) {
+          if (used[k]) v[k] -= delta;
+          else minv[k] -= delta;
+          if (tree[k]) u[k] += delta;
+        }
       }
-      __syncthreads();
-      const long long delta = s_delta;
-      const int j1 = s_col;
-      if (t <= P) {
-        if (used[t]) { u[match[t]] += delta; v[t] -= delta; }
-        else minv[t] -= delta;
-      }
-      __syncthreads();
+      j0 = col;
+      if (j0 > P || read_i(match, j0) == 0) break;
+    }
+    // flip the augmenting path back to column 0: p[j0] = p[way[j0]]
+    for (int step = 0; step <= P && j0 >= 1 && j0 <= P; ++step) {
+      const int j1 = read_i(way, j0);
+      const int row = j1 == 0 ? i : read_i(match, j1);
+#pragma unroll
+      for (int k = 0; k < kMatchSlots; ++k)
+        if (lane == lane_of(j0) && k == slot_of(j0)) match[k] = row;
       j0 = j1;
-      if (j0 > P || match[j0] == 0) break;
     }
-    if (t == 0) {  // flip the augmenting path back to column 0
-      for (int step = 0; step <= P && j0 != 0 && j0 <= P; ++step) {
-        const int j1 = way[j0];
-        match[j0] = match[j1];
-        j0 = j1;
-      }
-    }
-    __syncthreads();
   }
 
-  if (t >= 1 && t <= P) {
-    const int b = match[t] - 1;  // the matching is perfect: every bundle is placed once
-    if (b >= 0 && b < P) placed[b] = t - 1;
+#pragma unroll
+  for (int k = 0; k < kMatchSlots; ++k) {
+    const int c = lane + 1 + kWave * k;
+    const int b = match[k] - 1;  // the matching is perfect: every bundle is placed once
+    if (c <= P && b >= 0 && b < P) placed[b] = c - 1;
   }
-  for (int x = t; x < P * P; x += kMatchThreads) send[x] = 0;
+  for (int x = lane; x < P * P; x += kMatchThreads) send[x] = 0;
   __syncthreads();
-  if (t < P) perm[t] = placed[t];
   long long kept = 0;
-  if (t < P) {
-    const int dst = placed[t];
-    kept = keep(t, dst);
-    for (int k = 0; k < J; ++k) {  // the rank that receives bundle t owns send[.][dst]
-      const int j = bl[t * J + k];
+  for (int b = lane; b < P; b += kMatchThreads) {
+    const int dst = placed[b];
+    perm[b] = dst;
+    kept += (long long)keepc[b * P + dst] * m;
+    for (int k = 0; k < J; ++k) {  // the lane placing bundle b owns column dst of send
+      const int j = bl[b * J + k];
       if (j < 0 || j >= PJ) continue;
       const int src = j / J;
       if (src != dst) send[(int64_t)src * P + dst] += m;
@@ -387,13 +412,9 @@ locality_match_kernel(const int32_t* __restrict__ bundles, int P, int J, int64_t
   }
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) kept += __shfl_xor(kept, off);
-  if (lane == 0) wbest[wave] = kept;
-  __syncthreads();
-  if (t == 0) {
-    long long total = 0;
-    for (int w = 0; w < kMatchThreads / kWave; ++w) total += wbest[w];
-    kept_moved[0] = total;
-    kept_moved[1] = (long long)PJ * m - total;
+  if (lane == 0) {
+    kept_moved[0] = kept;
+    kept_moved[1] = (long long)PJ * m - kept;
   }
 }
 

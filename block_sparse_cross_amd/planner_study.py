@@ -3,7 +3,9 @@ cost-aware LPT plan, on the GPU, over the load-balancing workloads of the
 Split-KV paper's §5.5 (Figures 9 and 10) and a sweep of the chunks per rank J.
 
 Every assignment is computed by the library (`splitkv_plan` for LPT,
-`splitkv_plan_baseline` for the two position-based rules). This module builds
+`splitkv_plan_baseline` for the two position-based rules), and the LPT bundles
+are placed on physical ranks by `splitkv_locality_match` (the step's
+all-to-all volume is reported with and without that placement). This module builds
 the seeded anchors, times each call with HIP events on the stream it runs on,
 and turns the rank loads C_p into the imbalance 100(rho - 1) of §4.2, with
 W_p = C_p + D and D = (N/P) B^2.
@@ -94,6 +96,19 @@ def run_case(L: int, P: int, J: int, seed: int, reps: int) -> Dict:
         load = res[-1].cpu().numpy()
         out[name] = imbalance_pct(load, w.N, w.B)
         out[name + "_us"] = _time_call(fn, reps) if reps > 0 else None
+    # the step's all-to-all: context rows that leave their first holder, with
+    # LPT bundle p on rank p and with the locality matching of §4.2
+    bundles = lpt_out[2]
+    match_out = (torch.empty(P, dtype=torch.int32, device=dev),
+                 torch.empty((P, P), **i64), torch.empty(2, **i64))
+    match = lambda: binding.splitkv_locality_match(bundles, w.m, out=match_out)
+    match()
+    torch.cuda.synchronize()
+    b = bundles.cpu().numpy()
+    in_place = int((b // J == np.arange(P)[:, None]).sum()) * w.m
+    out["moved_plan_order"] = 100.0 * (w.S - in_place) / w.S
+    out["moved_matched"] = 100.0 * int(match_out[2][1].item()) / w.S
+    out["match_us"] = _time_call(match, reps) if reps > 0 else None
     return out
 
 
@@ -113,6 +128,9 @@ def study(seeds: int, reps: int, log=sys.stderr) -> Dict:
         for k in ("no_balance", "zigzag", "lpt"):
             row[k] = float(np.mean([r[k] for r in per_seed]))
             row[k + "_us"] = per_seed[0][k + "_us"]
+        for k in ("moved_plan_order", "moved_matched"):
+            row[k] = float(np.mean([r[k] for r in per_seed]))
+        row["match_us"] = per_seed[0]["match_us"]
         rows[group].append(row)
         print("planner study: %s L=%d P=%d J=%d done in %.1f s" % (group, L, P, J, time.time() - t0),
               file=log, flush=True)
@@ -147,6 +165,18 @@ def to_markdown(res: Dict) -> str:
                 group, r["L"], r["P"], r["J"], r["m"], r["no_balance"], r["zigzag"], r["lpt"],
                 *["%.1f" % r[k + "_us"] if r[k + "_us"] is not None else "-"
                   for k in ("no_balance", "zigzag", "lpt")]))
+    out.append("")
+    out.append("LPT's all-to-all (§4.2): context rows that leave the rank first holding them "
+               "(rank r holds the r-th contiguous part of the packed context), % of S, with "
+               "bundle p on rank p and after the locality matching; GPU time of one "
+               "`splitkv_locality_match` call:\n")
+    out.append("| study | per-sample L | P | J | moved, plan order | moved, matched | match us |")
+    out.append("|---|---:|---:|---:|---:|---:|---:|")
+    for group in ("context", "cp", "j_sweep"):
+        for r in res["rows"][group]:
+            out.append("| %s | %d | %d | %d | %.1f | %.1f | %s |" % (
+                group, r["L"], r["P"], r["J"], r["moved_plan_order"], r["moved_matched"],
+                "%.1f" % r["match_us"] if r["match_us"] is not None else "-"))
     return "\n".join(out) + "\n"
 
 

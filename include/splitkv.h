@@ -122,8 +122,8 @@ int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int
  * Outputs (device): phys_rank int32 [P] (bundle b runs on rank phys_rank[b]),
  *   send_rows int64 [P][P] (rows rank src sends to rank dst, zero diagonal),
  *   kept_moved int64 [2] = {rows kept in place, rows moved}.
- * Requires P <= 256, P*J <= 4096. Chunk ids outside [0, P*J) count as neither
- * kept nor sent. Integer only. */
+ * Requires P <= 256, P*J <= 4096, (P+1)*P*J*m < 2^54. Chunk ids outside
+ * [0, P*J) count as neither kept nor sent. Integer only. */
 int splitkv_locality_match(const int32_t* rank_chunks, int32_t P, int32_t J, int64_t m,
                            int32_t* phys_rank, int64_t* send_rows, int64_t* kept_moved,
                            void* stream);

@@ -159,7 +159,8 @@ EXPORT int oracle_lpt(int64_t n_chunks, const int64_t* cost, int32_t P, int32_t 
 /* on rank j / J. keep[b][r] = m * #{ chunks j of bundle b : j / J == r }.    */
 /* The placement maximises sum_b keep[b][perm[b]]: a linear assignment       */
 /* problem, solved exactly by the Hungarian method with row and column        */
-/* potentials on the cost -keep (rows = bundles, columns = ranks; each row    */
+/* potentials on the cost J*m - keep >= 0 (rows = bundles, columns = ranks;   */
+/* the constant leaves the best placement unchanged; each row                 */
 /* enters by a shortest augmenting path; of equal reduced costs the lowest    */
 /* column is taken). Outputs: perm[b] = physical rank of bundle b; send[src*P */
 /* + dst] = rows rank src sends to rank dst (m per chunk of the bundle placed */
@@ -197,7 +198,7 @@ EXPORT int oracle_locality_match(const int32_t* bundles, int32_t P, int32_t J, i
             int64_t delta = INF;
             for (int32_t j = 1; j <= P; ++j) {
                 if (used[j]) continue;
-                int64_t cur = -keep_rows(bundles, J, m, PJ, i0 - 1, j - 1) - u[i0] - v[j];
+                int64_t cur = (int64_t)J * m - keep_rows(bundles, J, m, PJ, i0 - 1, j - 1) - u[i0] - v[j];
                 if (cur < minv[j]) { minv[j] = cur; way[j] = j0; }
                 if (minv[j] < delta) { delta = minv[j]; j1 = j; }
             }

@@ -20,8 +20,10 @@ def oracle_imbalances(L, P, J, seed):
     for k, strategy in (("no_balance", 0), ("zigzag", 1)):
         _, load = oracle.baseline_plan(strategy, st, ln, prof, P)
         out[k] = 100.0 * (oracle.imbalance(load, w.N, w.B) - 1.0)
-    _, _, _, load = oracle.plan(s, a, w.B, w.S, w.m, P, J)
+    _, _, bundles, load = oracle.plan(s, a, w.B, w.S, w.m, P, J)
     out["lpt"] = 100.0 * (oracle.imbalance(load, w.N, w.B) - 1.0)
+    _, _, _, moved = oracle.locality_match(bundles, w.m)
+    out["moved_matched"] = 100.0 * moved / w.S
     return out
 
 
@@ -32,6 +34,8 @@ def test_case_matches_oracle(L, P, J):
     for k in ("no_balance", "zigzag", "lpt"):
         assert got[k] == pytest.approx(want[k], rel=1e-12, abs=1e-12), k
         assert got[k + "_us"] > 0
+    assert got["moved_matched"] == pytest.approx(want["moved_matched"], rel=1e-12, abs=1e-12)
+    assert got["moved_matched"] <= got["moved_plan_order"] and got["match_us"] > 0
 
 
 def test_study_runs_and_orders_the_rules():
@@ -40,4 +44,4 @@ def test_study_runs_and_orders_the_rules():
     for group in ("context", "cp"):
         assert s[group + "_lpt"][0] < s[group + "_zigzag"][0] < s[group + "_no_balance"][0]
     md = ps.to_markdown(res)
-    assert md.count("\n| j_sweep |") == 2 * len(ps.J_SWEEP)
+    assert md.count("\n| j_sweep |") == 2 * 2 * len(ps.J_SWEEP)   # imbalance and all-to-all tables
