@@ -303,6 +303,7 @@ def main():
             phase[j] += e[j].elapsed_time(e[j + 1])
     phase /= args.steps                      # ms per step: plan, fwd (P calls), merge, bwd (P calls)
     ms_step = wall * 1e3 / args.steps
+    step_gpu = sorted(e[0].elapsed_time(e[4]) for e in events)   # GPU time of each timed step
 
     pairs = int(cost.sum())                  # sum over ranks of live (row, key) pairs per head
     D = (w.N // w.P) * w.B * w.B             # own-block pairs per rank (Section 4.2's D)
@@ -337,6 +338,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3),
+        "step_gpu_ms": {"median": round(float(np.median(step_gpu)), 3),
+                        "min": round(step_gpu[0], 3)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -566,8 +569,24 @@ def cpu_baseline(w, seed, s, a, bundles, load, q, locs, args):
     dt = time.perf_counter() - t0
     flops = 14.0 * w.d * w.hq * live
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    # the plan (Eq. 6 + LPT) of the whole workload, and the Eq. 4 merge of the
+    # P partials over a sample of rows, bytes counted as for the GPU's merge
+    t0 = time.perf_counter()
+    oracle.plan(s, a, w.B, w.S, w.m, w.P, w.J)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    mrows = 32768
+    o_parts = g.standard_normal((w.P, mrows, w.d))
+    l_parts = g.standard_normal((w.P, mrows))
+    t0 = time.perf_counter()
+    oracle.merge(o_parts, l_parts)
+    merge_s = time.perf_counter() - t0
+    merge_bytes = w.P * mrows * (w.d * 2 + 4) + mrows * (w.d * 2 + 4)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(dt, 2),
+            "plan_ms": round(plan_ms, 3),
+            "merge_gbs": round(merge_bytes / merge_s / 1e9, 3),
+            "merge_sample": "%d partials x %d rows of d=%d (bytes as the GPU's bf16 merge)"
+                            % (w.P, mrows, w.d),
             "sample": "fp64 forward (Eq. 3) + backward (Algorithm 1: Delta, dq, dk, dv) of %d "
                       "seeded blocks (%d query rows) x %d heads against rank %d's %d local keys "
                       "(%d live pairs per head); FLOPs counted as 14 d Hq per live pair"
