@@ -36,12 +36,16 @@
 // accumulators (one output pass instead of a second read-modify-write): the
 // gradient of a rank's context rows is dk Wk + dv Wv.
 //
-// Split K. When the output has too few tiles to fill one round of the chip
-// (a rank's weight gradient 1024 x 5120 from K = 16384 rows is 80 tiles) and C
-// is fp32, K is cut into splits of at least 8 slices; each (tile, split) workgroup adds its
-// partial product into C with atomic fp32 adds (C zeroed first unless the call
-// accumulates; the bias comes with split 0). The order of those adds varies
-// from run to run, so such results are reproducible to rounding only.
+// Split K. When C is fp32 and the tiles leave a round of the chip part-filled,
+// the tiles of that last round have K cut into splits of at least 8 slices;
+// each (tile, split) workgroup adds its partial product into C with atomic
+// fp32 adds (C zeroed first unless the call accumulates; the bias comes with
+// split 0), while the tiles of the full rounds before it keep all of K and a
+// plain store. With fewer tiles than one round (a rank's weight gradient
+// 1024 x 5120 from K = 16384 rows is 80 tiles) every tile is split; with 320
+// tiles (5120 x 4096) the last 64 take four splits each, so the launch lasts
+// 1.25 tile-times instead of 2. The order of the atomic adds varies from run
+// to run, so split tiles are reproducible to rounding only.
 //
 // Edges. M and N need not be multiples of the tile: rows and columns past the
 // end are read from the last valid row or 8-column group (finite filler) and
@@ -312,7 +316,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
 gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
                  const bf16_t* __restrict__ B, const bf16_t* __restrict__ A2,
                  const bf16_t* __restrict__ B2, Tc* __restrict__ Cm,
-                 const float* __restrict__ bias, int accumulate, int splits,
+                 const float* __restrict__ bias, int accumulate, int full_tiles, int splits,
                  int slices_per_split) {
   // two stage buffers (A and B slices each), declared apart
   __shared__ __attribute__((aligned(16))) bf16_t lds_a0[kTileElems];
@@ -320,15 +324,24 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
   __shared__ __attribute__((aligned(16))) bf16_t lds_a1[kTileElems];
   __shared__ __attribute__((aligned(16))) bf16_t lds_b1[kTileElems];
 
-  // grid order: each XCD a contiguous run of (tile, K-split) items, tiles
-  // grouped kGroupRows tile-rows
+  // Items 0 .. full_tiles - 1 are whole tiles (all of K); each later tile is
+  // `splits` items, one per K split. Grid order: the whole tiles first, then
+  // the split items; within each part every XCD (workgroups are dealt to the
+  // XCDs round-robin) takes a contiguous run of items, tiles grouped
+  // kGroupRows tile-rows, so each XCD gets its share of both parts.
   const int n_tm = (int)((M + kBM - 1) / kBM), n_tn = (int)((N + kBN - 1) / kBN);
   const int nb = n_tm * n_tn;
-  const int total = nb * splits;
+  const int total = full_tiles + (nb - full_tiles) * splits;
   int item = blockIdx.x;
-  if (total % kXcds == 0) item = (item % kXcds) * (total / kXcds) + item / kXcds;
-  const int split = item % splits;
-  const int bid = item / splits;
+  if (item < full_tiles) {
+    if (full_tiles % kXcds == 0) item = (item % kXcds) * (full_tiles / kXcds) + item / kXcds;
+  } else if ((total - full_tiles) % kXcds == 0 && full_tiles % kXcds == 0) {
+    const int r = item - full_tiles, part = (total - full_tiles) / kXcds;
+    item = full_tiles + (r % kXcds) * part + r / kXcds;
+  }
+  const bool split_tile = item >= full_tiles && splits > 1;
+  const int split = item < full_tiles ? 0 : (item - full_tiles) % splits;
+  const int bid = item < full_tiles ? item : full_tiles + (item - full_tiles) / splits;
   const int group = bid / (kGroupRows * n_tn);
   const int first = group * kGroupRows;
   const int rows_in_group = min(n_tm - first, kGroupRows);
@@ -353,9 +366,9 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
   const int n_k1 = (int)((K + kBK - 1) / kBK);
   const int n_k = A2 != nullptr ? 2 * n_k1 : n_k1;
   const int n_full = A2 != nullptr ? n_k : (int)(K / kBK);  // slices wholly inside K
-  // this workgroup's K slices (all of them unless K is split)
-  const int kt_begin = split * slices_per_split;
-  const int kt_end = min(n_k, kt_begin + slices_per_split);
+  // this workgroup's K slices (all of them unless its tile is split)
+  const int kt_begin = split_tile ? split * slices_per_split : 0;
+  const int kt_end = split_tile ? min(n_k, kt_begin + slices_per_split) : n_k;
   uint32_t aoff[kPasses], boff[kPasses];
   if constexpr (Layout<LAYOUT>::A_KMAJOR)
     kmajor_offsets(M, K, m0, tid, aoff);
@@ -401,7 +414,7 @@ gemm_bf16_kernel(int64_t M, int64_t N, int64_t K, const bf16_t* __restrict__ A,
           Tc* p = Cm + m * N + n;
           float x = acc[i][j][e] + bn;
           if constexpr (sizeof(Tc) == 4) {
-            if (splits > 1) {  // K split: the partial sums meet in C (zeroed first if needed)
+            if (split_tile) {  // K split: the partial sums meet in C (zeroed first if needed)
               atomicAdd(reinterpret_cast<float*>(p), x);
               continue;
             }
@@ -420,11 +433,13 @@ zero_f32_kernel(int64_t n4, float4* __restrict__ p) {
   if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// K is split only when the tiles fill less than one round of the 256 CUs, into
-// as many splits as still fit in that round (measured on the per-rank weight
-// gradient 1024 x 5120 from K = 16384, 80 tiles: 3 splits 241 us, 2: 280 us,
-// 13: 442 us, none: 483 us; with more tiles the atomic adds cost more than the
-// fuller rounds save). A split keeps at least 8 slices.
+// K is split only for the tiles of a part-filled last round of the 256 CUs,
+// into as many splits as fill that round (at least 8 slices each). Measured on
+// the per-rank weight gradient 1024 x 5120 from K = 16384 (80 tiles, all in
+// the last round): 3 splits 241 us, 2: 280 us, 13: 442 us, none: 483 us.
+// Splitting every tile of a larger output cost more in atomic adds than the
+// fuller round saved; splitting only the last round's tiles keeps the atomic
+// traffic to those tiles.
 constexpr int kCus = 256;
 constexpr int kMinSlicesPerSplit = 8;
 
@@ -434,13 +449,19 @@ hipError_t launch_gemm_l(int64_t M, int64_t N, int64_t K, const void* A, const v
                          int accumulate, hipStream_t stream) {
   const int64_t nb = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int n_k = (int)((K + kBK - 1) / kBK) * (A2 != nullptr ? 2 : 1);
-  // Too few tiles to fill the chip: split K over workgroups (fp32 output only;
-  // the splits add their partial products into C atomically).
+  // tiles of the full rounds keep all of K; the rest (fp32 output only) split it
+  int64_t full = nb;
   int splits = 1;
-  if (c_dtype == SPLITKV_FP32 && nb < kCus / 2)
-    splits = max(1, min((int)(kCus / nb), n_k / kMinSlicesPerSplit));
+  if (c_dtype == SPLITKV_FP32) {
+    const int64_t tail = nb % kCus;
+    if (tail != 0 && (nb < kCus / 2 || nb > kCus)) {
+      full = nb - tail;
+      splits = max(1, min((int)(kCus / tail), n_k / kMinSlicesPerSplit));
+    }
+  }
   const int sps = (n_k + splits - 1) / splits;
   splits = (n_k + sps - 1) / sps;
+  if (splits == 1) full = nb;
   if (splits > 1 && !accumulate) {
     const int64_t n4 = M * N / 4;  // N % 8 == 0
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
@@ -452,13 +473,15 @@ hipError_t launch_gemm_l(int64_t M, int64_t N, int64_t K, const void* A, const v
   const bf16_t* b = static_cast<const bf16_t*>(B);
   const bf16_t* a2 = static_cast<const bf16_t*>(A2);
   const bf16_t* b2 = static_cast<const bf16_t*>(B2);
-  const dim3 grid((unsigned)(nb * splits));
+  const dim3 grid((unsigned)(full + (nb - full) * splits));
   if (c_dtype == SPLITKV_FP32)
     hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, float>), grid, dim3(kGemmThreads), 0, stream, M,
-                       N, K, a, b, a2, b2, static_cast<float*>(C), bias, accumulate, splits, sps);
+                       N, K, a, b, a2, b2, static_cast<float*>(C), bias, accumulate, (int)full,
+                       splits, sps);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<LAYOUT, bf16_t>), grid, dim3(kGemmThreads), 0, stream,
-                       M, N, K, a, b, a2, b2, static_cast<bf16_t*>(C), bias, accumulate, 1, n_k);
+                       M, N, K, a, b, a2, b2, static_cast<bf16_t*>(C), bias, accumulate, (int)nb, 1,
+                       n_k);
   return hipGetLastError();
 }
 

@@ -104,6 +104,24 @@ def test_gemm_split_k(layout, M, N, K):
     assert_close_f32(to_f64(Ca), ref + C0, "split-K accumulate")
 
 
+# More tiles than one round of the chip with a part-filled last round: the
+# tiles of the full rounds keep all of K (plain stores), the last round's tiles
+# split K (atomic adds), in one launch. 257 tiles: one tail tile in 4 splits;
+# 320 tiles (the per-rank dWo shape with a shorter K): 64 tail tiles in 4.
+@pytest.mark.parametrize("layout", [NT, NN, TN])
+@pytest.mark.parametrize("M,N,K", [(256 * 257, 256, 2048), (5120, 4096, 2048), (3000, 5904, 1088)])
+def test_gemm_tail_split(layout, M, N, K):
+    A, B, ref = operands(layout, M, N, K, seed=M + K + layout)
+    bias = np.random.default_rng(4).standard_normal(N).astype(np.float32)
+    C = binding.splitkv_gemm(layout, to_dev(A), to_dev(B), bias=to_dev(bias))
+    C0 = inputs.gen_matrix(M, N, 7, inputs.T_MAT, 1.0, dtype="fp32")
+    Ca = to_dev(C0)
+    binding.splitkv_gemm(layout, to_dev(A), to_dev(B), out=Ca, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close_f32(to_f64(C), ref + bias[None, :], "tail split")
+    assert_close_f32(to_f64(Ca), ref + C0, "tail split accumulate")
+
+
 @pytest.mark.parametrize("layout", [NT, NN, TN])
 @pytest.mark.parametrize("M,N,K", [(264, 520, 128), (1032, 512, 1024), (256, 256, 4096)])
 def test_gemm_pair(layout, M, N, K):
