@@ -44,7 +44,7 @@
 // plain store. With fewer tiles than one round (a rank's weight gradient
 // 1024 x 5120 from K = 16384 rows is 80 tiles) every tile is split; with 320
 // tiles (5120 x 4096) the last 64 take four splits each, so the launch lasts
-// 1.25 tile-times instead of 2. The order of the atomic adds varies from run
+// 1.25 tile-times instead of 2 (the launcher's rule says when it pays). The order of the atomic adds varies from run
 // to run, so split tiles are reproducible to rounding only.
 //
 // Edges. M and N need not be multiples of the tile: rows and columns past the
@@ -438,8 +438,11 @@ zero_f32_kernel(int64_t n4, float4* __restrict__ p) {
 // the per-rank weight gradient 1024 x 5120 from K = 16384 (80 tiles, all in
 // the last round): 3 splits 241 us, 2: 280 us, 13: 442 us, none: 483 us.
 // Splitting every tile of a larger output cost more in atomic adds than the
-// fuller round saved; splitting only the last round's tiles keeps the atomic
-// traffic to those tiles.
+// fuller round saved. With more than one round, the last round's tiles are
+// split when that round is at most a quarter full (320 tiles, 5120 x 4096 from
+// K = 8192: 389 -> 350 us, accumulating 462 -> 383 us), or half full when C is
+// accumulated (640 tiles, 8192 x 5120 from K = 4096: 511 -> 480 us; without
+// accumulation the zeroing pass made it 342 -> 390 us, so it stays whole).
 constexpr int kCus = 256;
 constexpr int kMinSlicesPerSplit = 8;
 
@@ -453,8 +456,12 @@ hipError_t launch_gemm_l(int64_t M, int64_t N, int64_t K, const void* A, const v
   int64_t full = nb;
   int splits = 1;
   if (c_dtype == SPLITKV_FP32) {
+    // a last round at most a quarter full (half full when C is accumulated
+    // anyway): the split's zeroing pass and atomic adds cost less than the
+    // idle part of that round
     const int64_t tail = nb % kCus;
-    if (tail != 0 && (nb < kCus / 2 || nb > kCus)) {
+    const bool split_tail = nb > kCus && (4 * tail <= kCus || (accumulate && 2 * tail <= kCus));
+    if (tail != 0 && (nb < kCus / 2 || split_tail)) {
       full = nb - tail;
       splits = max(1, min((int)(kCus / tail), n_k / kMinSlicesPerSplit));
     }
