@@ -83,7 +83,7 @@ def test_fwd_full_size_sampled_rows(name):
     assert np.isfinite(got_l[~empty]).all()
 
 
-@pytest.mark.parametrize("name", ["strong8", "qs32", "weak64"])
+@pytest.mark.parametrize("name", ["weak8", "strong8", "qs4", "qs32", "weak64"])
 def test_bwd_full_size_sampled(name):
     sh = share(name)
     w = sh.w
