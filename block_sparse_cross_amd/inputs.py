@@ -11,7 +11,7 @@ prompt-to-response ratio, diffusion block size B=16, an anchor budget A per
 sample, micro-batch b packed into S = b*L context positions and Q = b*A*B
 query rows; head layouts from Table 2 (n_q=32, n_kv=8, d_h=128).
 
-Readings of points the paper leaves open (each is listed in the design doc):
+Readings of points the paper leaves open:
   * s_i is the packed start of anchor i's sample (§3.1, Figure 1).
   * anchors are distinct positions drawn uniformly from the sample's response
     span [s + L/4, s + L), sorted ascending, blocks ordered sample-major.
