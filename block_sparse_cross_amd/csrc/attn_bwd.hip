@@ -12,7 +12,7 @@
 //     a record {lse * log2 e, Delta, lo, hi} with the row's local key interval
 //     (lse = -inf becomes +inf so that P = exp2(. - inf) = 0), laid out per
 //     (kv head, 64-vector chunk) as four 64-wide arrays.
-//  2. chunk_range_kernel: per 64-vector query chunk, the union of its
+//  2. chunk_range_kernel: per 64-vector query chunk (one wave), the union of its
 //     intervals and the interval that every vector of the chunk covers.
 //  3. attn_bwd_dkdv_kernel: a workgroup owns 128 local keys of one kv head (32
 //     per wave; K and V fragments and the dK, dV accumulators in registers)
@@ -118,23 +118,27 @@ bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
   rec[3 * kQC] = __int_as_float(r.y);
 }
 
-// Per 32-vector chunk c: {min lo, max hi} over its non-empty vectors (union),
-// {max lo, min hi} over all 32 slots (what every vector covers; vectors past
-// the end count as empty).
-__global__ void chunk_range_kernel(const int2* __restrict__ block_range, int64_t n_vec, int G,
-                                   int B, int64_t n_qc, int4* __restrict__ out) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= n_qc) return;
-  int ulo = 0x7fffffff, uhi = -1, clo = -1, chi = 0x7fffffff;
-  for (int t = 0; t < kQC; ++t) {
-    const int64_t vec = c * kQC + t;
-    int2 r = make_int2(0, 0);
-    if (vec < n_vec) r = block_range[(vec / G) / B];
-    if (r.x < r.y) { ulo = min(ulo, r.x); uhi = max(uhi, r.y); }
-    clo = max(clo, r.x);
-    chi = min(chi, r.y);
-  }
-  out[c] = uhi < 0 ? make_int4(0, 0, 0, 0) : make_int4(ulo, uhi, clo, chi);
+// Per 64-vector chunk c: {min lo, max hi} over its non-empty vectors (union),
+// {max lo, min hi} over all 64 slots (what every vector covers; vectors past
+// the end count as empty). One wave per chunk, lane t = vector 64 c + t, the
+// four extremes by wave reductions.
+constexpr int kRangeThreads = 256;
+__global__ void __launch_bounds__(kRangeThreads)
+chunk_range_kernel(const int2* __restrict__ block_range, int64_t n_vec, int G, int B,
+                   int64_t n_qc, int4* __restrict__ out) {
+  static_assert(kQC == kWave, "one lane per vector of a chunk");
+  const int64_t c = ((int64_t)blockIdx.x * kRangeThreads + threadIdx.x) / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (c >= n_qc) return;  // whole waves: c is the same in every lane of a wave
+  const int64_t vec = c * kQC + lane;
+  int2 r = make_int2(0, 0);
+  if (vec < n_vec) r = block_range[(vec / G) / B];
+  const bool live = r.x < r.y;
+  const int ulo = wave_min_i(live ? r.x : 0x7fffffff);
+  const int uhi = wave_max_i(live ? r.y : -1);
+  const int clo = wave_max_i(r.x);
+  const int chi = wave_min_i(r.y);
+  if (lane == 0) out[c] = uhi < 0 ? make_int4(0, 0, 0, 0) : make_int4(ulo, uhi, clo, chi);
 }
 
 template <int D>
@@ -778,8 +782,10 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
                          static_cast<const bf16_t*>(dout), lse, delta, block_range, meta, n_vec,
                          n_qc, G, gshift, hd.hq, hd.hkv, an.block_size);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      hipLaunchKernelGGL(chunk_range_kernel, dim3((unsigned)((n_qc + 255) / 256)), dim3(256), 0,
-                         stream, block_range, n_vec, G, an.block_size, n_qc, chunk_range);
+      const int64_t per_wg = kRangeThreads / kWave;  // chunks per workgroup
+      hipLaunchKernelGGL(chunk_range_kernel, dim3((unsigned)((n_qc + per_wg - 1) / per_wg)),
+                         dim3(kRangeThreads), 0, stream, block_range, n_vec, G, an.block_size,
+                         n_qc, chunk_range);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (n_keys == 0) return hipSuccess;
