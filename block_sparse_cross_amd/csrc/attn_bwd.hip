@@ -54,18 +54,20 @@ delta_kernel(const T* __restrict__ o, const T* __restrict__ dout, float* __restr
   delta[t] = acc;
 }
 
-// bf16 path: one record slot per (kv head g, 32-vector chunk c, t < 32); D/8
-// lanes per slot (16-byte loads, shuffle reduction). The records are laid out
-// as [g][c][field][t] with fields {lse * log2 e, Delta, lo, hi}, so that one
-// 512-byte copy stages a chunk's records as four 32-wide arrays. Slots past
-// the last vector are dead (lse = +inf: P = 0; empty interval).
-template <int D>
+// bf16 path: one record slot per (kv head g, 64-vector chunk c, t < 64); D/8
+// lanes per slot when Delta comes from o and do (16-byte loads, shuffle
+// reduction), one when it is given. The records are laid out as
+// [g][c][field][t] with fields {lse * log2 e, Delta, lo, hi}, so that one
+// 1 KB copy stages a chunk's records as four 64-wide arrays. Slots past the
+// last vector are dead (lse = +inf: P = 0; empty interval).
+template <int D, int L>
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
                 const float* __restrict__ lse, float* __restrict__ delta,
                 const int2* __restrict__ block_range, float* __restrict__ meta, int64_t n_vec,
                 int64_t n_qc, int G, int gshift, int hq, int hkv, int B) {
-  constexpr int L = D / 8;  // lanes per slot (8 or 16), a divisor of 64
+  // L lanes per slot: D / 8 (8 or 16, a divisor of 64) when Delta is taken
+  // from o and do, 1 when it is given
   const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t slot = gt / L;
   const int part = (int)(gt % L);
@@ -776,11 +778,18 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
     const int gshift = (G & (G - 1)) == 0 ? __builtin_ctz(G) : -1;
     int4* chunk_range = static_cast<int4*>(chunk_ws);
     if (n_rh > 0) {
-      const int64_t threads = (int64_t)hd.hkv * n_qc * kQC * (D / 8);
-      hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                         0, stream, static_cast<const bf16_t*>(o),
-                         static_cast<const bf16_t*>(dout), lse, delta, block_range, meta, n_vec,
-                         n_qc, G, gshift, hd.hq, hd.hkv, an.block_size);
+      const int64_t slots = (int64_t)hd.hkv * n_qc * kQC;
+      if (o != nullptr)
+        hipLaunchKernelGGL((bwd_prep_kernel<D, D / 8>),
+                           dim3((unsigned)((slots * (D / 8) + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), lse,
+                           delta, block_range, meta, n_vec, n_qc, G, gshift, hd.hq, hd.hkv,
+                           an.block_size);
+      else  // Delta given: one lane per slot
+        hipLaunchKernelGGL((bwd_prep_kernel<D, 1>), dim3((unsigned)((slots + 255) / 256)),
+                           dim3(256), 0, stream, static_cast<const bf16_t*>(nullptr),
+                           static_cast<const bf16_t*>(dout), lse, delta, block_range, meta, n_vec,
+                           n_qc, G, gshift, hd.hq, hd.hkv, an.block_size);
       if ((err = hipGetLastError()) != hipSuccess) return err;
       const int64_t per_wg = kRangeThreads / kWave;  // chunks per workgroup
       hipLaunchKernelGGL(chunk_range_kernel, dim3((unsigned)((n_qc + per_wg - 1) / per_wg)),
