@@ -68,6 +68,9 @@ int check_attn_common(const splitkv_anchors* an, const splitkv_heads* hd, const 
   if ((st = check_local(loc)) != SPLITKV_OK) return st;
   const int64_t Q = an->n_blocks * (int64_t)an->block_size;
   if (Q * hd->hq >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  // a 64-row tile of q or k (all heads) must span less than 2^32 bytes (the
+  // kernels copy tiles through 32-bit buffer ranges)
+  if ((int64_t)hd->hq * hd->d >= (int64_t(1) << 25)) return SPLITKV_ERR_UNSUPPORTED;
   return SPLITKV_OK;
 }
 

@@ -223,15 +223,17 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   auto issue_chunk = [&](int64_t c, bf16_t* Qd, bf16_t* Dd, float* Md) {
     const int64_t vec0 = c * kQC;
     if (fast_chunks && vec0 + kQC <= n_vec) {
+      // the chunk's kQC / G rows of all hq heads, as buffer resources
       const int64_t first = ((vec0 >> gshift) * hq + (int64_t)g * G) * D;
-      const char* qb = reinterpret_cast<const char*>(q + first);
-      const char* db = reinterpret_cast<const char*>(dout + first);
+      const uint32_t span = (uint32_t)((kQC >> gshift) * (int64_t)hq * D * 2);
+      const __amdgpu_buffer_rsrc_t qr = make_rsrc(uniform_ptr(q + first), span);
+      const __amdgpu_buffer_rsrc_t dr = make_rsrc(uniform_ptr(dout + first), span);
 #pragma unroll
       for (int pp = 0; pp < QPASSES; ++pp) {
         const int r0 = RPP * pp;
         const uint32_t step = (uint32_t)((((int64_t)(r0 >> gshift)) * hq + (r0 & (G - 1))) * D * 2);
-        async_copy16(qb + (lane_off + step), Qd + pp * kBwdThreads * 8 + lds_wave);
-        async_copy16(db + (lane_off + step), Dd + pp * kBwdThreads * 8 + lds_wave);
+        async_copy16_buf(qr, lane_off, step, Qd + pp * kBwdThreads * 8 + lds_wave);
+        async_copy16_buf(dr, lane_off, step, Dd + pp * kBwdThreads * 8 + lds_wave);
       }
       if (wave == NW - 1 && lane < kQC)
         async_copy16(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);

@@ -151,17 +151,42 @@ __device__ __forceinline__ void issue_rows_async(const bf16_t* __restrict__ src,
   }
 }
 
+// The same copy through a buffer resource: buffer_load_dwordx4 ... lds, with
+// a scalar base and a 32-bit range (`bytes`; a raw buffer, byte offsets,
+// loads past the range read zero), a per-lane offset and a scalar offset.
+// As fast as the global form in the attention kernels (0-2% faster), and the
+// hardware checks every load against the tile's range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: the raw-buffer format of the gfx9 family
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ void async_copy16_buf(__amdgpu_buffer_rsrc_t r, uint32_t lane_off,
+                                                 uint32_t scalar_off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, lane_off,
+                                           scalar_off, 0, 0);
+}
+// A 64-bit address that is the same in every lane, read from the first lane
+// into scalar registers (readfirstlane returns a signed int: each half goes
+// through uint32_t so that it is zero-extended).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 // The same copy for a tile that lies wholly inside the buffer. Row r of the
 // tile sits r * row_stride elements after `first`, its 16-byte slot permuted
 // by the swizzle KIND; rows of pass p sit p * THREADS / NS rows below those
 // of pass 0, a multiple of 16, and the swizzles depend on the row modulo 16
 // only, so one per-lane byte offset (tile_lane_offset, computed once by the
-// caller and kept in one register) serves every pass. The tile's first address is
-// the same in every lane; it is read from the first lane into scalar
-// registers and each pass adds its step there, so the copies take the
-// scalar-base form with the lane offset as their only vector operand and a
-// pass costs no vector instruction. The offset is made opaque at each call so
-// that the compiler does not fold it into a 64-bit vector address per pass.
+// caller and kept in one register) serves every pass. The tile's first
+// address is the same in every lane and becomes a buffer resource over the
+// tile's ROWS rows (ROWS * row_stride * 2 bytes, below 2^32); each pass adds
+// its step as the scalar offset, so a pass costs no vector instruction. The
+// lane offset is made opaque at each call so that the compiler keeps it in
+// one register.
 template <int D, int THREADS, int KIND>
 __device__ __forceinline__ uint32_t tile_lane_offset(int64_t row_stride, int tid) {
   constexpr int NS = D / 8;
@@ -178,20 +203,12 @@ __device__ __forceinline__ void issue_tile_async_off(const bf16_t* first, int64_
   static_assert(ROWS_PER_PASS % 16 == 0, "pass step must keep the swizzle");
   uint32_t off = lane_off;
   asm volatile("" : "+v"(off));
-  const uint64_t a = reinterpret_cast<uint64_t>(first);
-  // (readfirstlane returns a signed int: each half goes through uint32_t so
-  // that it is zero-extended)
-  const uint32_t a_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t a_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint64_t base = ((uint64_t)a_hi << 32) | (uint64_t)a_lo;
-  const uint64_t step = (uint64_t)ROWS_PER_PASS * (uint64_t)row_stride * 2u;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(first), (uint32_t)(ROWS * row_stride * 2));
+  const uint32_t step = (uint32_t)(ROWS_PER_PASS * row_stride * 2);
   const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
-    uint64_t b = base + pass * step;
-    asm volatile("" : "+s"(b));  // the pass address stays in scalar registers
-    async_copy16(reinterpret_cast<const char*>(b) + off, tile + pass * THREADS * 8 + lds_off);
-  }
+  for (int pass = 0; pass < PASSES; ++pass)
+    async_copy16_buf(r, off, pass * step, tile + pass * THREADS * 8 + lds_off);
 }
 
 // Local (per-rank) key range of one block. The local buffer holds the rank's

@@ -24,7 +24,7 @@
  *   - LSE values are natural logarithms. A (row, head) with no live key gets
  *     lse = -inf and o = 0.
  *   - Supported: d in {64, 128}; hq % hkv == 0; q/k/v dtype bf16 (matrix-core
- *     path) or fp32; J*m < 2^31; N*B*hq < 2^31.
+ *     path) or fp32; J*m < 2^31; N*B*hq < 2^31; hq*d < 2^25.
  */
 #ifndef SPLITKV_H
 #define SPLITKV_H
