@@ -185,6 +185,10 @@ def test_tiny_fp32_workload_partials_merge_and_backward():
     (8, 5000, 128, "fp32", "fp32"),
     (64, 4096, 128, "bf16", "bf16"),
     (7, 129, 8, "fp32", "bf16"),
+    (9, 777, 128, "bf16", "bf16"),      # partials taken in groups of 8: one full group + 1
+    (17, 300, 64, "fp32", "fp32"),      # the third group is reloaded into the first buffer
+    (24, 257, 128, "bf16", "fp32"),
+    (33, 100, 16, "fp32", "bf16"),
 ])
 def test_merge(P, rows, d, in_dt, out_dt):
     o_parts, lse_parts = inputs.gen_partials(P, rows, d, seed=P * 1000 + rows, dtype=in_dt)
@@ -199,6 +203,24 @@ def test_merge(P, rows, d, in_dt, out_dt):
     else:
         assert_close_bf16(got, o_ref, "merge")
     assert (got[np.isneginf(l_ref)] == 0).all()
+
+
+@pytest.mark.parametrize("P", [3, 8, 11, 20, 40])
+def test_merge_one_live_partial_per_row(P):
+    """Row r sees only partial r mod P: its weight is exp(0) = 1, so the merged
+    row must be exactly that partial's row and lse its lse_p (fp32 in and out).
+    A wrong partial index, group offset or buffer turn picks another row."""
+    rows, d = 3 * P + 5, 32
+    _, lse_parts = inputs.gen_partials(P, rows, d, seed=P, dtype="fp32")
+    # every (partial, row) distinct and nonzero, so a wrong pick cannot match
+    o_parts = (np.arange(P * rows * d, dtype=np.float32).reshape(P, rows, d) % 65521.0) + 1.0
+    live = np.arange(rows) % P
+    lse_parts[:] = -np.inf
+    lse_parts[live, np.arange(rows)] = np.linspace(-30.0, 30.0, rows, dtype=np.float32)
+    om, lm = binding.splitkv_lse_merge(to_dev(o_parts), to_dev(lse_parts))
+    torch.cuda.synchronize()
+    assert np.array_equal(lm.cpu().numpy(), lse_parts[live, np.arange(rows)])
+    assert np.array_equal(om.cpu().numpy(), o_parts[live, np.arange(rows)])
 
 
 def test_merge_all_empty_and_permutation():
