@@ -146,7 +146,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="weak8")
+    ap.add_argument("--workload", default="strong8",
+                    help="strong8 (default: the largest fwd+bwd share on one GPU), weak8, "
+                         "qs4/qs8/qs16/qs32, weak64 or tiny")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=24,
@@ -568,7 +570,12 @@ def cpu_baseline(w, seed, s, a, bundles, load, q, locs, args):
     oracle.attn_bwd(w.B, sb, ab, qs, dos, lse, dlt, pos, k, v, scale, rows, np.arange(len(pos)))
     dt = time.perf_counter() - t0
     flops = 14.0 * w.d * w.hq * live
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    cores = oracle.omp_threads()
+    # the oracle's work is proportional to the live pairs it visits, so its time
+    # for the max-loaded rank's whole share (every block) and for the whole
+    # step (every rank) follows from the sample by that ratio
+    rank_pairs = int(load[r])
+    all_pairs = int(load.sum())
     # the plan (Eq. 6 + LPT) of the whole workload, and the Eq. 4 merge of the
     # P partials over a sample of rows, bytes counted as for the GPU's merge
     t0 = time.perf_counter()
@@ -582,7 +589,15 @@ def cpu_baseline(w, seed, s, a, bundles, load, q, locs, args):
     merge_s = time.perf_counter() - t0
     merge_bytes = w.P * mrows * (w.d * 2 + 4) + mrows * (w.d * 2 + 4)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "cpu_model": cpu_model(),
             "kind": "oracle", "seconds": round(dt, 2),
+            "sample_live_pairs_per_head": live,
+            "extrapolated": {
+                "rank_share_s": round(dt * rank_pairs / live, 1),
+                "step_s": round(dt * all_pairs / live, 1),
+                "how": "measured seconds x (live pairs of rank %d's whole share, or of all %d "
+                       "ranks) / live pairs of the sample; labelled as an extrapolation, not "
+                       "measured" % (r, w.P)},
             "plan_ms": round(plan_ms, 3),
             "merge_gbs": round(merge_bytes / merge_s / 1e9, 3),
             "merge_sample": "%d partials x %d rows of d=%d (bytes as the GPU's bf16 merge)"
@@ -591,6 +606,19 @@ def cpu_baseline(w, seed, s, a, bundles, load, q, locs, args):
                       "seeded blocks (%d query rows) x %d heads against rank %d's %d local keys "
                       "(%d live pairs per head); FLOPs counted as 14 d Hq per live pair"
                       % (len(blocks), len(rows), w.hq, r, len(pos), live)}
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
 
 if __name__ == "__main__":
     main()

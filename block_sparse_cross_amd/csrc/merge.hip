@@ -205,9 +205,10 @@ lse_reduce_kernel(int P, int64_t rows, const float* __restrict__ lse_parts,
 // partial is empty (lse_p = -inf). One thread per 8 consecutive elements.
 template <typename Tin, typename Tout>
 __global__ void __launch_bounds__(kMergeThreads)
-lse_rescale_kernel(int64_t rows, int d, const Tin* __restrict__ o_part,
-                   const float* __restrict__ lse_part, const float* __restrict__ lse,
-                   Tout* __restrict__ o_bar) {
+lse_rescale_kernel(int64_t rows, int d, const Tin* o_part, const float* __restrict__ lse_part,
+                   const float* __restrict__ lse, Tout* o_bar) {
+  // o_bar may alias o_part (in place): each thread loads its 8 elements
+  // before it stores them, and no other thread touches them
   const int segs = d / 8;
   const int64_t unit = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
   if (unit >= rows * segs) return;

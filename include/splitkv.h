@@ -117,8 +117,9 @@ int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int
  * equal contiguous parts of [0, S), S = P*J*m (chunks r*J .. r*J + J - 1);
  * placing bundle b on rank r keeps m * #{chunks of b whose home is r} rows in
  * place. The placement maximises the rows kept (a linear assignment, solved
- * exactly; of equally good choices the one the Hungarian method reaches with
- * lowest-index tie-breaks, so the result is unique).
+ * exactly). Several placements often keep the same number of rows; which of
+ * them is returned is not specified (the same input gives the same one), and
+ * send_rows and kept_moved always describe the placement returned.
  * Outputs (device): phys_rank int32 [P] (bundle b runs on rank phys_rank[b]),
  *   send_rows int64 [P][P] (rows rank src sends to rank dst, zero diagonal),
  *   kept_moved int64 [2] = {rows kept in place, rows moved}.

@@ -50,6 +50,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_locality_match.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             i32p, i64p, i64p]
         L.oracle_locality_match.restype = ctypes.c_int
+        L.oracle_placement_rows.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            i32p, i64p, i64p]
+        L.oracle_placement_rows.restype = ctypes.c_int
+        L.oracle_omp_threads.argtypes = []
+        L.oracle_omp_threads.restype = ctypes.c_int
         L.oracle_anchor_profile.argtypes = [ctypes.c_int64, i64p, i64p, ctypes.c_int64,
                                             ctypes.c_int64, i64p]
         for name in ("oracle_chunk_costs", "oracle_chunk_costs_prefix"):
@@ -169,6 +174,30 @@ def locality_match(bundles, m: int):
     if rc != 0:
         raise ValueError("oracle_locality_match: invalid arguments")
     return perm, send, int(km[0]), int(km[1])
+
+
+def omp_threads() -> int:
+    """Threads the oracle's parallel loops use on this host."""
+    return int(lib().oracle_omp_threads())
+
+
+def placement_rows(bundles, perm, m: int):
+    """The all-to-all that one placement of the bundles implies (§4.2): chunk j
+    of bundle b moves from its home rank j // J to rank perm[b]. Returns (send
+    int64 [P][P]: rows rank src sends to rank dst, kept, moved). Raises if perm
+    is not a permutation."""
+    b = np.ascontiguousarray(bundles, dtype=np.int32)
+    P, J = b.shape
+    pm = np.ascontiguousarray(perm, dtype=np.int32)
+    if pm.shape != (P,):
+        raise ValueError("perm must have one entry per bundle")
+    send = np.zeros((P, P), np.int64)
+    km = np.zeros(2, np.int64)
+    rc = lib().oracle_placement_rows(_p(b, ctypes.c_int32), P, J, int(m), _p(pm, ctypes.c_int32),
+                                     _p(send, ctypes.c_int64), _p(km, ctypes.c_int64))
+    if rc != 0:
+        raise ValueError("oracle_placement_rows: perm is not a permutation")
+    return send, int(km[0]), int(km[1])
 
 
 def zigzag_loads(sample_start, sample_len, prof, P: int) -> np.ndarray:

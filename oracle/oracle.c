@@ -30,7 +30,20 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 #define EXPORT __attribute__((visibility("default")))
+
+/* Threads the parallel loops below use (1 without OpenMP). */
+EXPORT int oracle_omp_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 static int64_t max64(int64_t x, int64_t y) { return x > y ? x : y; }
 static int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
@@ -177,6 +190,41 @@ static int64_t keep_rows(const int32_t* bundles, int32_t J, int64_t m, int32_t P
     return n * m;
 }
 
+/* The all-to-all of one placement (any permutation perm: bundle b runs on   */
+/* physical rank perm[b]), by the definition: every chunk j of bundle b lives  */
+/* on rank j / J before the step and on rank perm[b] after it, so its m rows   */
+/* stay in place when the two agree and are sent from j / J to perm[b]        */
+/* otherwise. send[src*P + dst] = rows sent from src to dst (zero diagonal);   */
+/* kept_moved = {rows in place, P*J*m - rows in place}. Chunk ids outside     */
+/* [0, P*J) count as neither kept nor sent. Returns -1 when perm is not a     */
+/* permutation of 0 .. P-1.                                                   */
+EXPORT int oracle_placement_rows(const int32_t* bundles, int32_t P, int32_t J, int64_t m,
+                                 const int32_t* perm, int64_t* send, int64_t* kept_moved) {
+    if (P <= 0 || J <= 0 || m <= 0) return -1;
+    char* seen = (char*)calloc(P, 1);
+    for (int32_t b = 0; b < P; ++b) {
+        if (perm[b] < 0 || perm[b] >= P || seen[perm[b]]) { free(seen); return -1; }
+        seen[perm[b]] = 1;
+    }
+    free(seen);
+    const int32_t PJ = P * J;
+    for (int64_t x = 0; x < (int64_t)P * P; ++x) send[x] = 0;
+    int64_t kept = 0;
+    for (int32_t b = 0; b < P; ++b) {
+        int32_t dst = perm[b];
+        for (int32_t k = 0; k < J; ++k) {
+            int32_t j = bundles[(int64_t)b * J + k];
+            if (j < 0 || j >= PJ) continue;
+            int32_t src = j / J;
+            if (src == dst) kept += m;
+            else send[(int64_t)src * P + dst] += m;
+        }
+    }
+    kept_moved[0] = kept;
+    kept_moved[1] = (int64_t)PJ * m - kept;
+    return 0;
+}
+
 EXPORT int oracle_locality_match(const int32_t* bundles, int32_t P, int32_t J, int64_t m,
                                  int32_t* perm, int64_t* send, int64_t* kept_moved) {
     if (P <= 0 || J <= 0 || m <= 0) return -1;
@@ -215,22 +263,8 @@ EXPORT int oracle_locality_match(const int32_t* bundles, int32_t P, int32_t J, i
         } while (j0 != 0);
     }
     for (int32_t j = 1; j <= P; ++j) perm[match[j] - 1] = j - 1;
-    for (int64_t x = 0; x < (int64_t)P * P; ++x) send[x] = 0;
-    int64_t kept = 0;
-    for (int32_t b = 0; b < P; ++b) {
-        int32_t dst = perm[b];
-        kept += keep_rows(bundles, J, m, PJ, b, dst);
-        for (int32_t k = 0; k < J; ++k) {
-            int32_t j = bundles[(int64_t)b * J + k];
-            if (j < 0 || j >= PJ) continue;
-            int32_t src = j / J;
-            if (src != dst) send[(int64_t)src * P + dst] += m;
-        }
-    }
-    kept_moved[0] = kept;
-    kept_moved[1] = (int64_t)PJ * m - kept;
     free(u); free(v); free(minv); free(match); free(way); free(used);
-    return 0;
+    return oracle_placement_rows(bundles, P, J, m, perm, send, kept_moved);
 }
 
 /* ------------------------------------------------------------------------- */

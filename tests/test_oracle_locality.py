@@ -82,3 +82,63 @@ def test_never_worse_than_keeping_plan_order(name):
     keep = keep_matrix(np.asarray(bundles), w.m)
     assert kept >= int(np.trace(keep))       # bundle b on rank b
     check_invariants(np.asarray(bundles), w.m, perm, send, kept, moved)
+
+
+def rows_by_position(b, perm, m):
+    """The all-to-all of a placement counted one context position at a time:
+    position x sits in chunk x // m, which starts on rank x // (J m) and must
+    end on the rank its bundle is placed on."""
+    P, J = b.shape
+    owner = np.full(P * J, -1)
+    for i in range(P):
+        for j in b[i]:
+            if 0 <= j < P * J:
+                owner[j] = i
+    send = np.zeros((P, P), np.int64)
+    kept = 0
+    for x in range(P * J * m):
+        j = x // m
+        if owner[j] < 0:
+            continue
+        src, dst = x // (J * m), perm[owner[j]]
+        if src == dst:
+            kept += 1
+        else:
+            send[src, dst] += 1
+    return send, kept
+
+
+@pytest.mark.parametrize("P,J,m", [(1, 1, 3), (2, 3, 2), (4, 2, 5), (5, 3, 1), (7, 2, 3)])
+def test_placement_rows_by_position(P, J, m):
+    g = np.random.default_rng(P * 7 + J)
+    for trial in range(10):
+        b = g.permutation(P * J).reshape(P, J)
+        if trial == 0:
+            b[0, 0] = -1          # ids outside the plan are neither kept nor sent
+        perm = g.permutation(P)
+        send, kept, moved = oracle.placement_rows(b, perm, m)
+        s_ref, k_ref = rows_by_position(b, perm, m)
+        np.testing.assert_array_equal(send, s_ref)
+        assert kept == k_ref and moved == P * J * m - kept
+
+
+def test_placement_rows_of_the_matching_and_of_home():
+    g = np.random.default_rng(5)
+    b = g.permutation(40).reshape(8, 5)
+    perm, send, kept, moved = oracle.locality_match(b, 16)
+    s2, k2, m2 = oracle.placement_rows(b, perm, 16)
+    np.testing.assert_array_equal(send, s2)
+    assert (kept, moved) == (k2, m2)
+    home = np.arange(40).reshape(8, 5)
+    s3, k3, m3 = oracle.placement_rows(home, np.arange(8), 16)
+    assert not s3.any() and k3 == 8 * 5 * 16 and m3 == 0
+    # every bundle placed one rank further: all rows move
+    s4, k4, m4 = oracle.placement_rows(home, (np.arange(8) + 1) % 8, 16)
+    assert k4 == 0 and m4 == 640 and s4[np.arange(8), (np.arange(8) + 1) % 8].tolist() == [80] * 8
+
+
+def test_placement_rows_rejects_non_permutations():
+    b = np.arange(6).reshape(3, 2)
+    for bad in ([0, 0, 1], [0, 1, 3], [-1, 0, 1]):
+        with pytest.raises(ValueError):
+            oracle.placement_rows(b, np.array(bad), 4)
