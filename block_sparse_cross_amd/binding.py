@@ -111,6 +111,9 @@ def lib() -> ctypes.CDLL:
         L.splitkv_cast_bf16.restype = ctypes.c_int
         L.splitkv_attn_bwd.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.splitkv_attn_bwd.restype = ctypes.c_int
+        L.splitkv_attn_bwd_noalloc.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp]
+        L.splitkv_attn_bwd_noalloc.restype = ctypes.c_int
         L.splitkv_status_str.argtypes = [ctypes.c_int]
         L.splitkv_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -487,16 +490,9 @@ def splitkv_cast_bf16(src: torch.Tensor, out: Optional[torch.Tensor] = None,
     return out
 
 
-def splitkv_attn_bwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v, o, dout, lse,
-                     dq: torch.Tensor, scale: Optional[float] = None,
-                     delta: Optional[torch.Tensor] = None,
-                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-                     workspace: Optional[torch.Tensor] = None,
-                     stream: Optional[torch.cuda.Stream] = None):
-    """Backward of the local partial with the global lse (and Delta = <do, o>).
-
-    dq (fp32 [Q, hq, d]) is accumulated in place. Pass o=None and delta=... to
-    supply Delta directly. Returns (dk, dv, delta)."""
+def _bwd_args(s, a, block_size, chunk_start, chunk_len, q, k, v, o, dout, lse, dq, scale, delta,
+              out):
+    """Checks and outputs shared by the two backward entry points."""
     Q, hq, d = q.shape
     hkv = k.shape[1]
     if dout.shape != q.shape or dout.dtype != q.dtype:
@@ -518,10 +514,44 @@ def splitkv_attn_bwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v
     dk, dv = out
     an, hd, loc = make_anchors(s, a, block_size), make_heads(hq, hkv, d, q.dtype, scale), \
         make_local(chunk_start, chunk_len)
+    return an, hd, loc, delta, dk, dv
+
+
+def splitkv_attn_bwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v, o, dout, lse,
+                     dq: torch.Tensor, scale: Optional[float] = None,
+                     delta: Optional[torch.Tensor] = None,
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None):
+    """Backward of the local partial with the global lse (and Delta = <do, o>).
+
+    dq (fp32 [Q, hq, d]) is accumulated in place. Pass o=None and delta=... to
+    supply Delta directly. Returns (dk, dv, delta)."""
+    an, hd, loc, delta, dk, dv = _bwd_args(s, a, block_size, chunk_start, chunk_len, q, k, v, o,
+                                           dout, lse, dq, scale, delta, out)
     nbytes = splitkv_workspace_bytes(SPLITKV_OP_BWD, an, hd, loc)
     ws_ptr, ws_bytes = _workspace(nbytes, q.device, workspace)
     _check("splitkv_attn_bwd", lib().splitkv_attn_bwd(
         ctypes.byref(an), ctypes.byref(hd), ctypes.byref(loc), _ptr(q), _ptr(k), _ptr(v),
         _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
         ws_ptr, ws_bytes, _stream(stream)))
+    return dk, dv, delta
+
+
+def splitkv_attn_bwd_noalloc(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v, o,
+                             dout, lse, dq: torch.Tensor, scale: Optional[float] = None,
+                             delta: torch.Tensor = None,
+                             out: Tuple[torch.Tensor, torch.Tensor] = None,
+                             stream: Optional[torch.cuda.Stream] = None):
+    """splitkv_attn_bwd on the library's fixed per-device scratch: no workspace.
+    Allocates nothing, so delta and out (dk, dv) must be given. Returns (dk,
+    dv, delta)."""
+    if delta is None or out is None:
+        raise ValueError("the no-allocation backward needs delta and out=(dk, dv)")
+    an, hd, loc, delta, dk, dv = _bwd_args(s, a, block_size, chunk_start, chunk_len, q, k, v, o,
+                                           dout, lse, dq, scale, delta, out)
+    _check("splitkv_attn_bwd_noalloc", lib().splitkv_attn_bwd_noalloc(
+        ctypes.byref(an), ctypes.byref(hd), ctypes.byref(loc), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+        _stream(stream)))
     return dk, dv, delta

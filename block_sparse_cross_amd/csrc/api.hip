@@ -1,6 +1,8 @@
 // C ABI of the Split-KV per-device hot path (declared in include/splitkv.h).
 // Validates every scalar on the host, sizes the workspace, and enqueues the
 // kernels on the caller's stream. Nothing is enqueued when validation fails.
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -71,6 +73,64 @@ int check_attn_common(const splitkv_anchors* an, const splitkv_heads* hd, const 
   // a 64-row tile of q or k (all heads) must span less than 2^32 bytes (the
   // kernels copy tiles through 32-bit buffer ranges)
   if ((int64_t)hd->hq * hd->d >= (int64_t(1) << 25)) return SPLITKV_ERR_UNSUPPORTED;
+  return SPLITKV_OK;
+}
+
+int check_bwd_args(const splitkv_anchors* an, const splitkv_heads* hd, const splitkv_local* loc,
+                   const void* q, const void* k, const void* v, const void* dout,
+                   const float* lse, const float* delta, const float* dq, const void* dk,
+                   const void* dv) {
+  int st = check_attn_common(an, hd, loc);
+  if (st != SPLITKV_OK) return st;
+  const int64_t n_keys = (int64_t)loc->n_chunks * loc->chunk_len;
+  const int64_t Q = an->n_blocks * (int64_t)an->block_size;
+  if (Q > 0 && (q == nullptr || dout == nullptr || lse == nullptr || delta == nullptr ||
+                dq == nullptr))
+    return SPLITKV_ERR_INVALID_ARG;
+  if (n_keys > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return SPLITKV_ERR_INVALID_ARG;
+  return SPLITKV_OK;
+}
+
+// The backward's kernels on a workspace laid out as `ws` at `base` (device).
+int run_bwd(const splitkv_anchors* an, const splitkv_heads* hd, const splitkv_local* loc,
+            const void* q, const void* k, const void* v, const void* o, const void* dout,
+            const float* lse, float* delta, float* dq, void* dk, void* dv, char* base,
+            const BwdWorkspace& ws, hipStream_t s) {
+  const int64_t n_keys = (int64_t)loc->n_chunks * loc->chunk_len;
+  int2* block_range = reinterpret_cast<int2*>(base + ws.block_range);
+  hipError_t e = launch_block_ranges(an->s, an->a, an->n_blocks, loc->chunk_start, loc->n_chunks,
+                                     loc->chunk_len, block_range, s);
+  if (e != hipSuccess) return SPLITKV_ERR_HIP;
+  return hip_status(launch_bwd(*an, *hd, n_keys, block_range, base + ws.meta,
+                               base + ws.chunk_range, q, k, v, o, dout, lse, delta, dq, dk, dv,
+                               s));
+}
+
+// Fixed device scratch of splitkv_attn_bwd_noalloc, for callers that cannot
+// allocate. Each device that loads the library holds its own copy until the
+// process ends. Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol): the device address is looked up
+// once per device with that device current and kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[SPLITKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+char* scratch_addr[kMaxScratchDevices] = {};
+
+// The scratch address on the current device (looked up on the first call).
+int device_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SPLITKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return SPLITKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return SPLITKV_ERR_HIP;
+    scratch_addr[dev] = static_cast<char*>(p);
+  }
+  *out = scratch_addr[dev];
   return SPLITKV_OK;
 }
 
@@ -298,27 +358,27 @@ int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
                      const splitkv_local* loc, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, float* delta, float* dq,
                      void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_attn_common(an, hd, loc);
+  int st = check_bwd_args(an, hd, loc, q, k, v, dout, lse, delta, dq, dk, dv);
   if (st != SPLITKV_OK) return st;
-  const int64_t n_keys = (int64_t)loc->n_chunks * loc->chunk_len;
-  const int64_t Q = an->n_blocks * (int64_t)an->block_size;
-  if (Q > 0 && (q == nullptr || dout == nullptr || lse == nullptr || delta == nullptr ||
-                dq == nullptr))
-    return SPLITKV_ERR_INVALID_ARG;
-  if (n_keys > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
-    return SPLITKV_ERR_INVALID_ARG;
   const BwdWorkspace ws = bwd_workspace_layout(an->n_blocks, an->block_size, hd->hq, hd->hkv);
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total))
     return SPLITKV_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* base = static_cast<char*>(workspace);
-  int2* block_range = reinterpret_cast<int2*>(base + ws.block_range);
-  hipError_t e = launch_block_ranges(an->s, an->a, an->n_blocks, loc->chunk_start, loc->n_chunks,
-                                     loc->chunk_len, block_range, s);
-  if (e != hipSuccess) return SPLITKV_ERR_HIP;
-  return hip_status(launch_bwd(*an, *hd, n_keys, block_range, base + ws.meta,
-                               base + ws.chunk_range, q, k, v, o, dout, lse, delta, dq, dk, dv,
-                               s));
+  return run_bwd(an, hd, loc, q, k, v, o, dout, lse, delta, dq, dk, dv,
+                 static_cast<char*>(workspace), ws, static_cast<hipStream_t>(stream));
+}
+
+int splitkv_attn_bwd_noalloc(const splitkv_anchors* an, const splitkv_heads* hd,
+                             const splitkv_local* loc, const void* q, const void* k,
+                             const void* v, const void* o, const void* dout, const float* lse,
+                             float* delta, float* dq, void* dk, void* dv, void* stream) {
+  int st = check_bwd_args(an, hd, loc, q, k, v, dout, lse, delta, dq, dk, dv);
+  if (st != SPLITKV_OK) return st;
+  const BwdWorkspace ws = bwd_workspace_layout(an->n_blocks, an->block_size, hd->hq, hd->hkv);
+  if (ws.total > SPLITKV_NOALLOC_SCRATCH_BYTES) return SPLITKV_ERR_WORKSPACE;
+  char* base = nullptr;
+  if ((st = device_scratch(&base)) != SPLITKV_OK) return st;
+  return run_bwd(an, hd, loc, q, k, v, o, dout, lse, delta, dq, dk, dv, base, ws,
+                 static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -252,6 +252,26 @@ int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
                      float* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The backward above without a workspace argument, for callers that cannot
+ * allocate device memory at all (code under stream capture, tight serving
+ * loops, harnesses that forbid allocation). Same arguments, results and
+ * kernels as splitkv_attn_bwd; its scratch (the per-block key ranges, the
+ * per-vector records and the per-chunk ranges of the workspace) lives in a
+ * fixed device array of SPLITKV_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends. The call allocates and
+ * frees nothing. Inputs larger than the array can hold (when
+ * splitkv_workspace_bytes(SPLITKV_OP_BWD, ...) exceeds it; about 16 bytes per
+ * query row and head) return SPLITKV_ERR_WORKSPACE with nothing enqueued.
+ * The array is the current device's (hipGetDevice), so `stream` must belong
+ * to the current device. Every call on one device shares that device's
+ * array: calls that overlap in time on one device (several streams or host
+ * threads) race; serialise them. No state carries over between calls. */
+#define SPLITKV_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+int splitkv_attn_bwd_noalloc(const splitkv_anchors* an, const splitkv_heads* hd,
+                             const splitkv_local* loc, const void* q, const void* k,
+                             const void* v, const void* o, const void* dout, const float* lse,
+                             float* delta, float* dq, void* dk, void* dv, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* splitkv_status_str(int status);
 
