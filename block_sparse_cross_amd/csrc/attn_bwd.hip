@@ -544,7 +544,9 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int wall_hi = __builtin_amdgcn_readfirstlane(wave_min_i(live_lane ? qhi : -1));
   if (lane == 0) { wave_lo[wave] = wlo; wave_hi[wave] = whi; }
 
-  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T).
+  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T). The Q
+  // fragment is taken times scale * log2 e (rounded to bf16), so the product
+  // gives the exponent of P directly.
   bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -553,9 +555,20 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       a = *reinterpret_cast<const u32x4*>(q + head_off + ks * 16 + half * 8);
       b = *reinterpret_cast<const u32x4*>(dout + head_off + ks * 16 + half * 8);
     }
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      a[w] = pack_bf16x2_hw(__uint_as_float(a[w] << 16) * scale_log2,
+                            __uint_as_float(a[w] & 0xffff0000u) * scale_log2);
     qf[ks] = as_bf16x8(a);
     df[ks] = as_bf16x8(b);
   }
+  // Accumulator starts: S^T from -lse log2 e (so P = exp2 of the product;
+  // -inf for a row without live keys gives P = 0) and dP^T from -Delta (so
+  // dS = P times the product). A lane's 16 accumulator values all belong to
+  // its own query vector.
+  f32x16 s_init, p_init;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { s_init[r] = -lse2; p_init[r] = -dl; }
   __syncthreads();
   int lo = 0x7fffffff, hi = -1;
 #pragma unroll
@@ -564,7 +577,9 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   hi = __builtin_amdgcn_readfirstlane(hi);
 
   const uint32_t k_off = tile_lane_offset<D, kDqThreads, kSwzBoth>((int64_t)hkv * D, tid);
-  const uint32_t v_off = tile_lane_offset<D, kDqThreads, kSwzRows>((int64_t)hkv * D, tid);
+  // V takes K's swizzle, so one per-lane offset table serves the row-major
+  // reads of both
+  const uint32_t v_off = tile_lane_offset<D, kDqThreads, kSwzBoth>((int64_t)hkv * D, tid);
   auto issue_tile = [&](int k0, bf16_t* Kn, bf16_t* Vn) {
     if (k0 + kDqKT <= n_keys) {
       const int64_t first = ((int64_t)k0 * hkv + g) * D;
@@ -572,7 +587,7 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       issue_tile_async_off<D, kDqKT, kDqThreads>(v + first, (int64_t)hkv * D, v_off, Vn, tid);
     } else {
       issue_rows_async<D, kDqKT, kDqThreads, kSwzBoth>(k, hkv, g, k0, n_keys, Kn, tid);
-      issue_rows_async<D, kDqKT, kDqThreads, kSwzRows>(v, hkv, g, k0, n_keys, Vn, tid);
+      issue_rows_async<D, kDqKT, kDqThreads, kSwzBoth>(v, hkv, g, k0, n_keys, Vn, tid);
     }
   };
 
@@ -596,6 +611,17 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     asm volatile("" : "+v"(tr_off[dt][0]), "+v"(tr_off[dt][1]));
   }
 
+  // Element offsets of this lane's row-major reads of K and V (key row
+  // lane % 32 of a 32-key half, d-step ks); the swizzle depends on the row
+  // modulo 16 only, so the second half adds 32 D. Opaque, like tr_off.
+  int kro[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int kr = lane & 31;
+    kro[ks] = kr * D + (((2 * ks + half) ^ swz_both<NS>(kr)) * 8);
+    asm volatile("" : "+v"(kro[ks]));
+  }
+
   auto tile_step = [&](int k0, const bf16_t* Kt, const bf16_t* Vt, bf16_t* Kn, bf16_t* Vn) {
     wait_async();
     __syncthreads();
@@ -607,30 +633,29 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     // live at a time.
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int kr = mt * 32 + (lane & 31);
-      f32x16 sacc, pacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+      const int hb = mt * 32 * D;
+      f32x16 sacc = s_init, pacc = p_init;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Kt[kr * D + (((2 * ks + half) ^ swz_both<NS>(kr)) * 8)]);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(&Vt[kr * D + (((2 * ks + half) ^ swz_rows<NS>(kr)) * 8)]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&Kt[hb + kro[ks]]);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&Vt[hb + kro[ks]]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b), df[ks], pacc, 0, 0, 0);
       }
-      // dS^T = P (dP - Delta); the per-key test only on tiles that cut some
+      // dS^T = P (dP - Delta) (both already in the accumulators: the exponent
+      // of P and dP - Delta); the per-key test only on tiles that cut some
       // lane's interval (a separate copy of the loop, so the common case has
       // no per-element branches)
       auto weights = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(sacc[r], scale_log2, -lse2));
+          float p = fast_exp2(sacc[r]);
           if constexpr (MASKED) {
             const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
             p = (key >= qlo && key < qhi) ? p : 0.f;
           }
-          sacc[r] = p * (pacc[r] - dl);
+          sacc[r] = p * pacc[r];
         }
       };
       if (tile_masked)
