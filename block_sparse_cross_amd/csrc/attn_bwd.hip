@@ -9,9 +9,9 @@
 //
 // bf16 path, four kernels:
 //  1. bwd_prep_kernel: Delta (from o and do, or given) and, per query vector,
-//     a record {lse * log2 e, Delta, lo, hi} with the row's local key interval
-//     (lse = -inf becomes +inf so that P = exp2(. - inf) = 0), laid out per
-//     (kv head, 64-vector chunk) as four 64-wide arrays.
+//     a record {-lse * log2 e, -Delta, lo, hi} with the row's local key
+//     interval (lse = -inf stays -inf so that P = exp2(. - inf) = 0), laid out
+//     per (kv head, 64-vector chunk) as four 64-wide arrays.
 //  2. chunk_range_kernel: per 64-vector query chunk (one wave), the union of its
 //     intervals and the interval that every vector of the chunk covers.
 //  3. attn_bwd_dkdv_kernel: a workgroup owns 128 local keys of one kv head (32
@@ -57,9 +57,11 @@ delta_kernel(const T* __restrict__ o, const T* __restrict__ dout, float* __restr
 // bf16 path: one record slot per (kv head g, 64-vector chunk c, t < 64); D/8
 // lanes per slot when Delta comes from o and do (16-byte loads, shuffle
 // reduction), one when it is given. The records are laid out as
-// [g][c][field][t] with fields {lse * log2 e, Delta, lo, hi}, so that one
-// 1 KB copy stages a chunk's records as four 64-wide arrays. Slots past the
-// last vector are dead (lse = +inf: P = 0; empty interval).
+// [g][c][field][t] with fields {-lse * log2 e, -Delta, lo, hi} (the starting
+// values of the S and dP accumulators of the dK/dV kernel), so that one 1 KB
+// copy stages a chunk's records as four 64-wide arrays. Rows without live keys
+// and slots past the last vector start S at -inf (P = 0); dead slots have an
+// empty interval.
 template <int D, int L>
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
@@ -99,7 +101,7 @@ bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
   if (!ok || part != 0) return;
   float* rec = meta + (slot / kQC) * (4 * kQC) + slot % kQC;
   if (item < 0) {
-    rec[0] = INFINITY;
+    rec[0] = -INFINITY;
     rec[kQC] = 0.f;
     rec[2 * kQC] = __int_as_float(0);
     rec[3 * kQC] = __int_as_float(0);
@@ -114,8 +116,8 @@ bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
   }
   const float l = lse[item];
   const int2 r = block_range[rw / B];
-  rec[0] = l == -INFINITY ? INFINITY : l * kLog2e;
-  rec[kQC] = dl;
+  rec[0] = l == -INFINITY ? -INFINITY : -l * kLog2e;
+  rec[kQC] = -dl;
   rec[2 * kQC] = __int_as_float(r.x);
   rec[3 * kQC] = __int_as_float(r.y);
 }
@@ -191,6 +193,11 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       a = *reinterpret_cast<const u32x4*>(k + off);
       b = *reinterpret_cast<const u32x4*>(v + off);
     }
+    // K times scale * log2 e (rounded to bf16): S is then the exponent of P
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      a[w] = pack_bf16x2_hw(__uint_as_float(a[w] << 16) * scale_log2,
+                            __uint_as_float(a[w] & 0xffff0000u) * scale_log2);
     kf[ks] = as_bf16x8(a);
     vf[ks] = as_bf16x8(b);
   }
@@ -297,8 +304,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     // operands of a piece (two products), up to two pieces ahead: Q and dO
     // rows for S / dP, dO^T and Q^T fragments for dV^T / dK^T
     u32x4 opa[3], opb[3];
-    float4 ml[2], md[2];     // lse log2 e, Delta of 4 vectors (per 8-vector group jj)
-    int4 mlo[2], mhi[2];     // their key intervals (masked chunks only)
+    int4 mlo[2], mhi[2];     // key intervals of 4 vectors (masked chunks only)
     u32x4 pu, su;            // P and dS of the current 16-vector step, bf16
 
     auto load_sd = [&](int hv, int ks, int b) {
@@ -313,14 +319,26 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       opa[b] = u32x4{d0.x, d0.y, d1.x, d1.y};
       opb[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
     };
+    // The accumulators of S and dP of half hv start from the records'
+    // -lse log2 e and -Delta (element r of a lane is vector 8 (r / 4) +
+    // 4 half + r % 4 of the half), so that P = exp2(S) and dS = P dP after
+    // the products.
+    auto load_init = [&](int hv) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int q0 = hv * 32 + 8 * jj + rec_off;
+        const float4 l = *reinterpret_cast<const float4*>(&Mb[q0]);
+        const float4 d = *reinterpret_cast<const float4*>(&Mb[kQC + q0]);
+        sacc[hv][4 * jj + 0] = l.x; sacc[hv][4 * jj + 1] = l.y;
+        sacc[hv][4 * jj + 2] = l.z; sacc[hv][4 * jj + 3] = l.w;
+        pacc[hv][4 * jj + 0] = d.x; pacc[hv][4 * jj + 1] = d.y;
+        pacc[hv][4 * jj + 2] = d.z; pacc[hv][4 * jj + 3] = d.w;
+      }
+    };
     auto load_meta = [&](int hv, int jj) {
       const int q0 = hv * 32 + 8 * jj + rec_off, b = jj & 1;
-      ml[b] = *reinterpret_cast<const float4*>(&Mb[q0]);
-      md[b] = *reinterpret_cast<const float4*>(&Mb[kQC + q0]);
-      if constexpr (MASKED) {
-        mlo[b] = *reinterpret_cast<const int4*>(&Mb[2 * kQC + q0]);
-        mhi[b] = *reinterpret_cast<const int4*>(&Mb[3 * kQC + q0]);
-      }
+      mlo[b] = *reinterpret_cast<const int4*>(&Mb[2 * kQC + q0]);
+      mhi[b] = *reinterpret_cast<const int4*>(&Mb[3 * kQC + q0]);
     };
     // The chunk runs in pieces: NP = D / 16 per phase, and the P, dS work of
     // a half is spread over NP pieces, EPP elements each.
@@ -330,16 +348,14 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
       for (int e = 0; e < EPP; ++e) {
         const int r = EPP * w + e, jj = r >> 2, i = r & 3, b = jj & 1;
-        const float l2 = i == 0 ? ml[b].x : i == 1 ? ml[b].y : i == 2 ? ml[b].z : ml[b].w;
-        const float dl = i == 0 ? md[b].x : i == 1 ? md[b].y : i == 2 ? md[b].z : md[b].w;
-        float pk = fast_exp2(fmaf(sacc[hv][r], scale_log2, -l2));
+        float pk = fast_exp2(sacc[hv][r]);
         if constexpr (MASKED) {
           const int lo = i == 0 ? mlo[b].x : i == 1 ? mlo[b].y : i == 2 ? mlo[b].z : mlo[b].w;
           const int hi = i == 0 ? mhi[b].x : i == 1 ? mhi[b].y : i == 2 ? mhi[b].z : mhi[b].w;
           pk = (mykey >= lo && mykey < hi) ? pk : 0.f;
         }
         sacc[hv][r] = pk;
-        pacc[hv][r] = pk * (pacc[hv][r] - dl);
+        pacc[hv][r] = pk * pacc[hv][r];
       }
     };
     auto pack = [&](int hv, int h2) {
@@ -371,10 +387,13 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       else if (ph < 4) load_upd(ph - 2, i / DT, i % DT, x % 3);
     };
     auto dist = [](int x) { return (x / NP == 0 || x / NP == 3) ? 2 : 1; };
-    // The records of 8-vector group jj of half hv are first used in piece
-    // NP (hv + 1) + 4 jj / EPP; they are loaded G = 4 / EPP pieces earlier,
-    // when the group two back (same register slot) is done.
+    // The key intervals of 8-vector group jj of half hv (masked chunks) are
+    // first used in piece NP (hv + 1) + 4 jj / EPP; they are loaded G = 4 / EPP
+    // pieces earlier, when the group two back (same register slot) is done.
+    // Half 0's accumulator starts are read before the first piece, half 1's
+    // two pieces before its products begin.
     constexpr int G = 4 / EPP;
+    load_init(0);
     load_piece(0);
     load_piece(1);
 #pragma unroll
@@ -382,17 +401,16 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
       for (int x = pc + 1; x <= pc + 2; ++x)
         if (x >= 2 && x < 4 * NP && x - dist(x) == pc) load_piece(x);
+      if constexpr (MASKED) {
 #pragma unroll
-      for (int hv = 0; hv < NH; ++hv)
+        for (int hv = 0; hv < NH; ++hv)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (NP * (hv + 1) + (4 * jj) / EPP - G == pc) load_meta(hv, jj);
+          for (int jj = 0; jj < 4; ++jj)
+            if (NP * (hv + 1) + (4 * jj) / EPP - G == pc) load_meta(hv, jj);
+      }
+      if (pc == NP - 2) load_init(1);
       const int ph = pc / NP, i = pc % NP, b = pc % 3;
       if (ph < 2) {
-        if (i == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) { sacc[ph][r] = 0.f; pacc[ph][r] = 0.f; }
-        }
         sacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opa[b]), kf[i], sacc[ph], 0, 0, 0);
         pacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opb[b]), vf[i], pacc[ph], 0, 0, 0);
       } else {
