@@ -2,9 +2,13 @@
 times (same binding calls, the plan's critical-path rank r* = argmax load).
 
 For each workload the GPU runs the whole rank share; the oracle recomputes a
-sample of outputs one by one: forward o_p / lse_p for sampled rows (all
-heads), dq for sampled rows, dk / dv for sampled keys (all kv heads), merged
-o / lse for sampled rows against the unsplit attention over the whole context.
+sample of outputs one by one: forward o_p / lse_p for 64 sampled rows (all
+heads; the shortest and the longest windows among them), dq for sampled rows,
+dk / dv for 64 sampled keys (all kv heads). The whole-step tests run the
+bench's call sequence (every rank's forward, the merge, every rank's backward
+from the merged output) and check the merged o / lse and dq against the
+unsplit attention over the whole context, and dk / dv on keys whose only
+viewers are sampled blocks, all with the oracle's own lse and Delta.
 """
 import numpy as np
 import pytest
@@ -40,8 +44,11 @@ class Share:
         self.v = inputs.gen_local_kv(w, SEED, self.ids, "v")
         self.qd, self.kd, self.vd = to_dev(self.q), to_dev(self.k), to_dev(self.v)
         self.cs = to_dev(self.ids.astype(np.int64) * w.m)
+        # 64 rows, all heads: the first block (shortest window) and the last
+        # block (longest) of the batch and two random blocks
         g = np.random.default_rng(99)
-        self.rows = np.unique(np.concatenate([[0, w.Q - 1], g.choice(w.Q, 8, replace=False)]))
+        self.blocks = sample_blocks(w, g, 2)
+        self.rows = block_rows(self.blocks, w.B)
 
     def fwd(self):
         o, l = binding.splitkv_attn_fwd(self.sd, self.ad, self.w.B, self.cs, self.w.m, self.qd,
@@ -55,6 +62,17 @@ class Share:
                                    vals64(self.k), vals64(self.v), w.d ** -0.5)
 
 
+def sample_blocks(w, g, n_random):
+    """The first and the last block of the batch (the shortest and the longest
+    context windows of the workload) and n_random other blocks."""
+    rest = g.choice(np.arange(1, w.N - 1), n_random, replace=False)
+    return np.unique(np.concatenate([[0, w.N - 1], rest]))
+
+
+def block_rows(blocks, B):
+    return (np.asarray(blocks)[:, None] * B + np.arange(B)[None, :]).reshape(-1)
+
+
 _cache = {}
 
 
@@ -66,7 +84,10 @@ def share(name):
     return _cache[name]
 
 
-@pytest.mark.parametrize("name", ["weak8", "strong8", "qs4", "qs32", "weak64"])
+FULL = ["weak8", "strong8", "qs4", "qs8", "qs16", "qs32", "weak64"]
+
+
+@pytest.mark.parametrize("name", FULL)
 def test_fwd_full_size_sampled_rows(name):
     sh = share(name)
     o, l = sh.fwd()
@@ -83,7 +104,7 @@ def test_fwd_full_size_sampled_rows(name):
     assert np.isfinite(got_l[~empty]).all()
 
 
-@pytest.mark.parametrize("name", ["weak8", "strong8", "qs4", "qs32", "weak64"])
+@pytest.mark.parametrize("name", FULL)
 def test_bwd_full_size_sampled(name):
     sh = share(name)
     w = sh.w
@@ -95,12 +116,14 @@ def test_bwd_full_size_sampled(name):
                                              to_dev(o_syn), to_dev(do), to_dev(lse_syn), dq)
     torch.cuda.synchronize()
     g = np.random.default_rng(5)
-    dq_rows = np.unique(np.concatenate([[w.Q - 1], g.choice(w.Q, 2, replace=False)]))
-    # keys: both ends of the buffer, a block's last live key, random ones
+    # dq: the last block (longest window) and a random block, all heads
+    dq_rows = block_rows(np.unique([w.N - 1, int(g.integers(0, w.N - 1))]), w.B)
+    # 64 keys: both ends of the buffer, a block's last live key and the one
+    # after it, random ones
     i = int(g.integers(0, w.N))
     last_live = int(np.searchsorted(sh.pos, sh.a[i]) - 1)
     keys = np.unique(np.clip(np.concatenate([[0, len(sh.pos) - 1, last_live, last_live + 1],
-                                             g.choice(len(sh.pos), 10, replace=False)]),
+                                             g.choice(len(sh.pos), 60, replace=False)]),
                              0, len(sh.pos) - 1))
     dl = oracle.delta(vals64(o_syn), vals64(do))
     np.testing.assert_allclose(to_f64(delta)[dq_rows], dl[dq_rows], rtol=1e-3, atol=1e-6)
@@ -149,3 +172,109 @@ def test_merge_full_size_weak64_shape():
     o_ref, l_ref = oracle.merge(vals64(o_parts[:, sel]), lse_parts[:, sel].astype(np.float64))
     assert_lse(to_f64(lm)[sel], l_ref, tol=1e-5)
     assert_close_bf16(to_f64(om)[sel], o_ref, "merge")
+
+
+def window_view(w, blocks, s, a):
+    """The context span [lo, hi) that the given blocks' windows cover."""
+    return int(s[blocks].min()), int(a[blocks].max())
+
+
+@pytest.mark.parametrize("name", ["weak8", "strong8"])
+def test_step_full_size(name):
+    """The whole step as bench.py runs it (plan; forward of every rank; merge
+    of the P partials; backward of every rank with the merged lse, Delta
+    taken from the merged output by the first call and passed to the
+    others; dq summed over ranks), checked against the oracle's unsplit
+    attention with its own lse and Delta: merged o / lse and dq on 64 rows
+    (the first two blocks and the last two: the shortest and the longest
+    windows; all heads), dk / dv
+    on keys seen by the last two blocks only, from whichever ranks hold
+    them."""
+    _cache.clear()
+    torch.cuda.empty_cache()
+    w = inputs.WORKLOADS[name]
+    print("[step] %s: S=%d Q=%d P=%d J=%d" % (name, w.S, w.Q, w.P, w.J), flush=True)
+    s, a = inputs.workload_anchors(w, SEED)
+    sd, ad = to_dev(s), to_dev(a)
+    _, owner, bundles, _ = [t.cpu().numpy() for t in binding.splitkv_plan(
+        sd, ad, w.B, w.S, w.m, w.P, w.J)]
+    q, do = inputs.gen_q(w, SEED), inputs.gen_do(w, SEED)
+    qd, dod = to_dev(q), to_dev(do)
+    locs = []
+    for p in range(w.P):
+        ids = bundles[p]
+        locs.append((to_dev(ids.astype(np.int64) * w.m), to_dev(inputs.gen_local_kv(w, SEED, ids, "k")),
+                     to_dev(inputs.gen_local_kv(w, SEED, ids, "v"))))
+    o_parts = torch.empty((w.P, w.Q, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    l_parts = torch.empty((w.P, w.Q, w.hq), dtype=torch.float32, device="cuda")
+    for p, (cs, k, v) in enumerate(locs):
+        binding.splitkv_attn_fwd(sd, ad, w.B, cs, w.m, qd, k, v, out=(o_parts[p], l_parts[p]))
+    om, lm = binding.splitkv_lse_merge(o_parts, l_parts)
+    del o_parts, l_parts
+    dq = torch.zeros((w.Q, w.hq, w.d), dtype=torch.float32, device="cuda")
+    delta = torch.empty((w.Q, w.hq), dtype=torch.float32, device="cuda")
+    grads = []
+    for p, (cs, k, v) in enumerate(locs):
+        dk, dv, _ = binding.splitkv_attn_bwd(sd, ad, w.B, cs, w.m, qd, k, v, om if p == 0 else None,
+                                             dod, lm, dq, delta=delta)
+        grads.append((dk, dv))
+    torch.cuda.synchronize()
+    print("[step] %s: GPU step done" % name, flush=True)
+
+    last = w.N - 1
+    blocks = np.unique([0, 1, last - 1, last])
+    rows = block_rows(blocks, w.B)
+    scale = w.d ** -0.5
+    # oracle: unsplit forward of the sampled blocks over their windows, then
+    # Delta and dq from it; blocks of one sample share a window start
+    o_ref = np.zeros((len(rows), w.hq, w.d))
+    l_ref = np.zeros((len(rows), w.hq))
+    dq_ref = np.zeros((len(rows), w.hq, w.d))
+    for bi, b in enumerate(blocks):
+        lo, hi = window_view(w, [b], s, a)
+        kg = vals64(inputs.gen_kv_rows(w, SEED, "k", lo, hi - lo))
+        vg = vals64(inputs.gen_kv_rows(w, SEED, "v", lo, hi - lo))
+        r = block_rows([b], w.B)
+        sl = slice(bi * w.B, (bi + 1) * w.B)
+        sb, ab = s[[b]], a[[b]]
+        o_b, l_b = oracle.partial_attn(np.arange(w.B), w.B, sb, ab, vals64(q[r]),
+                                       np.arange(lo, hi), kg, vg, scale)
+        dl_b = oracle.delta(o_b, vals64(do[r]))
+        dq_b, _, _ = oracle.attn_bwd(w.B, sb, ab, vals64(q[r]), vals64(do[r]), l_b, dl_b,
+                                     np.arange(lo, hi), kg, vg, scale, np.arange(w.B),
+                                     np.zeros(0, np.int64))
+        o_ref[sl], l_ref[sl], dq_ref[sl] = o_b, l_b, dq_b
+        del kg, vg
+    print("[step] %s: oracle rows done" % name, flush=True)
+    assert_lse(to_f64(lm)[rows], l_ref, "%s merged lse" % name)
+    assert_close_bf16(to_f64(om)[rows], o_ref, "%s merged o" % name)
+    assert_close_bf16(to_f64(dq)[rows], dq_ref, "%s dq (summed over ranks)" % name)
+
+    # keys that only the last two blocks see: [a_{last-2}, a_last) (the
+    # windows of one sample share their start, anchors ascend)
+    assert s[last - 2] == s[last]
+    g = np.random.default_rng(7)
+    span = np.arange(a[last - 2], a[last])
+    xs = np.sort(g.choice(span, min(64, len(span)), replace=False))
+    vb = np.array([last - 1, last])
+    vrows = block_rows(vb, w.B)
+    ix = np.searchsorted(blocks, vb)
+    vr = (ix[:, None] * w.B + np.arange(w.B)[None, :]).reshape(-1)   # their rows in the sample
+    kx = vals64(np.concatenate([inputs.gen_kv_rows(w, SEED, "k", int(x), 1) for x in xs]))
+    vx = vals64(np.concatenate([inputs.gen_kv_rows(w, SEED, "v", int(x), 1) for x in xs]))
+    dl_v = oracle.delta(o_ref[vr], vals64(do[vrows]))
+    _, dk_ref, dv_ref = oracle.attn_bwd(w.B, s[vb], a[vb], vals64(q[vrows]), vals64(do[vrows]),
+                                        l_ref[vr], dl_v, xs, kx, vx, scale, np.zeros(0, np.int64),
+                                        np.arange(len(xs)))
+    dk_got = np.zeros_like(dk_ref)
+    dv_got = np.zeros_like(dv_ref)
+    for i, x in enumerate(xs):
+        p = int(owner[x // w.m])
+        ids = bundles[p]
+        j = int(np.nonzero(ids == x // w.m)[0][0])
+        li = j * w.m + int(x % w.m)                 # row of x in rank p's buffer
+        dk_got[i] = to_f64(grads[p][0][li])
+        dv_got[i] = to_f64(grads[p][1][li])
+    assert len(xs) >= min(64, len(span))
+    assert_close_bf16(dk_got, dk_ref, "%s dk (keys seen by the last two blocks)" % name)
+    assert_close_bf16(dv_got, dv_ref, "%s dv (keys seen by the last two blocks)" % name)
