@@ -33,7 +33,7 @@ EXPORTED = ("splitkv_workspace_bytes", "splitkv_validate_anchors", "splitkv_plan
             "splitkv_locality_match", "splitkv_plan_baseline",
             "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
             "splitkv_delta", "splitkv_gemm", "splitkv_gemm_pair", "splitkv_cast_bf16",
-            "splitkv_attn_bwd",
+            "splitkv_attn_bwd", "splitkv_attn_bwd_noalloc",
             "splitkv_status_str")
 
 SPLITKV_GEMM_NT, SPLITKV_GEMM_NN, SPLITKV_GEMM_TN = 0, 1, 2
