@@ -14,7 +14,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsplitkv.so")
+# SPLITKV_LIB may name another build of the same library (e.g. one with host
+# sanitizers); there is no other implementation behind these calls.
+LIB_PATH = os.environ.get("SPLITKV_LIB") or os.path.join(_HERE, "libsplitkv.so")
 
 SPLITKV_OK = 0
 SPLITKV_ERR_INVALID_ARG = -1

@@ -36,28 +36,56 @@ CFLAGS = [
 EXTRA_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+# Host code (the C ABI's validation and launch setup) checked by Address- and
+# UndefinedBehaviorSanitizer; device code is built as usual. Such a library
+# runs with clang's ASan runtime preloaded (see host_asan_runtime()).
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                 "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, objdir: str = OBJDIR, extra=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + CFLAGS + EXTRA_FLAGS.get(src, []) + list(extra) + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, host_sanitize_to: str = "") -> str:
+    """Compile and link the library (in-tree), or, with host_sanitize_to, a
+    copy whose host code carries the sanitizers, at that path."""
+    out = host_sanitize_to or LIB
+    objdir = os.path.join(os.path.dirname(out), "_obj_san") if host_sanitize_to else OBJDIR
+    extra = HOST_SANITIZE if host_sanitize_to else []
+    os.makedirs(objdir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, objdir, extra), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
+    link_extra = ["-Xarch_host", "-shared-libsan"] if host_sanitize_to else []
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + link_extra + \
+        ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
+
+
+def host_asan_runtime() -> str:
+    """clang's shared AddressSanitizer runtime (to preload for a library built
+    with host_sanitize_to)."""
+    r = subprocess.run([os.path.join(os.path.dirname(HIPCC), "..", "llvm", "bin", "clang"),
+                        "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's ASan runtime not found")
+    return path
 
 
 if __name__ == "__main__":

@@ -37,6 +37,10 @@ namespace {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SPLITKV_OK : SPLITKV_ERR_HIP; }
 
+// Tensors the kernels touch with 16-byte vector loads, copies or stores must
+// start on a 16-byte boundary (NULL passes: presence is checked separately).
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 int check_anchors(const splitkv_anchors* an) {
   if (an == nullptr) return SPLITKV_ERR_INVALID_ARG;
   if (an->n_blocks < 0 || an->block_size < 1) return SPLITKV_ERR_INVALID_ARG;
@@ -77,7 +81,7 @@ int check_attn_common(const splitkv_anchors* an, const splitkv_heads* hd, const 
 }
 
 int check_bwd_args(const splitkv_anchors* an, const splitkv_heads* hd, const splitkv_local* loc,
-                   const void* q, const void* k, const void* v, const void* dout,
+                   const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, const float* delta, const float* dq, const void* dk,
                    const void* dv) {
   int st = check_attn_common(an, hd, loc);
@@ -88,6 +92,8 @@ int check_bwd_args(const splitkv_anchors* an, const splitkv_heads* hd, const spl
                 dq == nullptr))
     return SPLITKV_ERR_INVALID_ARG;
   if (n_keys > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return SPLITKV_ERR_INVALID_ARG;
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(o) || !a16(dout) || !a16(dq) || !a16(dk) || !a16(dv))
     return SPLITKV_ERR_INVALID_ARG;
   return SPLITKV_OK;
 }
@@ -247,6 +253,7 @@ int splitkv_attn_fwd(const splitkv_anchors* an, const splitkv_heads* hd,
   if (an->n_blocks == 0) return SPLITKV_OK;
   if (q == nullptr || o_part == nullptr || lse_part == nullptr) return SPLITKV_ERR_INVALID_ARG;
   if (n_keys > 0 && (k == nullptr || v == nullptr)) return SPLITKV_ERR_INVALID_ARG;
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(o_part)) return SPLITKV_ERR_INVALID_ARG;
   const FwdWorkspace ws = fwd_workspace_layout(an->n_blocks);
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total))
     return SPLITKV_ERR_WORKSPACE;
@@ -268,6 +275,7 @@ int splitkv_lse_merge(int32_t P, int64_t rows, int32_t d, const void* o_parts, i
   if (rows == 0) return SPLITKV_OK;
   if (o_parts == nullptr || lse_parts == nullptr || o == nullptr || lse == nullptr)
     return SPLITKV_ERR_INVALID_ARG;
+  if (!a16(o_parts) || !a16(o)) return SPLITKV_ERR_INVALID_ARG;
   if ((rows * (d / 8) + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
   return hip_status(launch_merge(P, rows, d, o_parts, in_dtype, lse_parts, o, out_dtype, lse,
                                  static_cast<hipStream_t>(stream)));
@@ -292,6 +300,7 @@ int splitkv_lse_rescale(int64_t rows, int32_t d, const void* o_part, int in_dtyp
   if (rows == 0) return SPLITKV_OK;
   if (o_part == nullptr || lse_part == nullptr || lse == nullptr || o_bar == nullptr)
     return SPLITKV_ERR_INVALID_ARG;
+  if (!a16(o_part) || !a16(o_bar)) return SPLITKV_ERR_INVALID_ARG;
   // in place only when the element types agree
   if (o_part == o_bar && in_dtype != out_dtype) return SPLITKV_ERR_INVALID_ARG;
   if ((rows * (d / 8) + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
@@ -308,6 +317,7 @@ int splitkv_delta(int64_t rows, int32_t d, const void* o, int o_dtype, const voi
     return SPLITKV_ERR_UNSUPPORTED;
   if (rows == 0) return SPLITKV_OK;
   if (o == nullptr || dout == nullptr || delta == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if (!a16(o) || !a16(dout)) return SPLITKV_ERR_INVALID_ARG;
   if ((rows * (d / 8) + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
   return hip_status(launch_delta(rows, d, o, o_dtype, dout, do_dtype, delta, accumulate != 0,
                                  static_cast<hipStream_t>(stream)));
@@ -317,6 +327,7 @@ int splitkv_cast_bf16(int64_t n, const float* src, void* dst, void* stream) {
   if (n < 0 || n % 8 != 0) return SPLITKV_ERR_INVALID_ARG;
   if (n == 0) return SPLITKV_OK;
   if (src == nullptr || dst == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if (!a16(src) || !a16(dst)) return SPLITKV_ERR_INVALID_ARG;
   if ((n / 8 + 255) / 256 >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
   return hip_status(launch_cast_bf16(n, src, dst, static_cast<hipStream_t>(stream)));
 }
@@ -330,6 +341,7 @@ int splitkv_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* A, con
   if (c_dtype != SPLITKV_BF16 && c_dtype != SPLITKV_FP32) return SPLITKV_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return SPLITKV_OK;
   if (A == nullptr || B == nullptr || C == nullptr) return SPLITKV_ERR_INVALID_ARG;
+  if (!a16(A) || !a16(B) || !a16(C)) return SPLITKV_ERR_INVALID_ARG;
   // tile count; the kernel addresses each operand with 32-bit byte offsets
   if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
   if (M * K >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
@@ -348,6 +360,7 @@ int splitkv_gemm_pair(int layout, int64_t M, int64_t N, int64_t K, const void* A
   if (M == 0 || N == 0) return SPLITKV_OK;
   if (A1 == nullptr || B1 == nullptr || A2 == nullptr || B2 == nullptr || C == nullptr)
     return SPLITKV_ERR_INVALID_ARG;
+  if (!a16(A1) || !a16(B1) || !a16(A2) || !a16(B2) || !a16(C)) return SPLITKV_ERR_INVALID_ARG;
   if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
   if (M * K >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 31)) return SPLITKV_ERR_UNSUPPORTED;
   return hip_status(launch_gemm(layout, M, N, K, A1, B1, A2, B2, C, c_dtype, bias,
@@ -358,7 +371,7 @@ int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
                      const splitkv_local* loc, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, float* delta, float* dq,
                      void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_bwd_args(an, hd, loc, q, k, v, dout, lse, delta, dq, dk, dv);
+  int st = check_bwd_args(an, hd, loc, q, k, v, o, dout, lse, delta, dq, dk, dv);
   if (st != SPLITKV_OK) return st;
   const BwdWorkspace ws = bwd_workspace_layout(an->n_blocks, an->block_size, hd->hq, hd->hkv);
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total))
@@ -371,7 +384,7 @@ int splitkv_attn_bwd_noalloc(const splitkv_anchors* an, const splitkv_heads* hd,
                              const splitkv_local* loc, const void* q, const void* k,
                              const void* v, const void* o, const void* dout, const float* lse,
                              float* delta, float* dq, void* dk, void* dv, void* stream) {
-  int st = check_bwd_args(an, hd, loc, q, k, v, dout, lse, delta, dq, dk, dv);
+  int st = check_bwd_args(an, hd, loc, q, k, v, o, dout, lse, delta, dq, dk, dv);
   if (st != SPLITKV_OK) return st;
   const BwdWorkspace ws = bwd_workspace_layout(an->n_blocks, an->block_size, hd->hq, hd->hkv);
   if (ws.total > SPLITKV_NOALLOC_SCRATCH_BYTES) return SPLITKV_ERR_WORKSPACE;

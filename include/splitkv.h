@@ -25,6 +25,12 @@
  *     lse = -inf and o = 0.
  *   - Supported: d in {64, 128}; hq % hkv == 0; q/k/v dtype bf16 (matrix-core
  *     path) or fp32; J*m < 2^31; N*B*hq < 2^31; hq*d < 2^25.
+ *   - Alignment: every tensor of query, key/value, output, gradient or
+ *     product-operand shape (q, k, v, o, o_part(s), o_bar, dout, dq, dk, dv,
+ *     the products' A, B, C and the conversion's src, dst) must start on a
+ *     16-byte boundary (the kernels move them 16 bytes per lane); otherwise
+ *     the call returns SPLITKV_ERR_INVALID_ARG with nothing enqueued. Anchor,
+ *     chunk, LSE, Delta and plan arrays need only their element alignment.
  */
 #ifndef SPLITKV_H
 #define SPLITKV_H

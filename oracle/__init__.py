@@ -30,22 +30,29 @@ i32p = ctypes.POINTER(ctypes.c_int32)
 f64p = ctypes.POINTER(ctypes.c_double)
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc (-O2, OpenMP, IEEE semantics: no fast-math)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+def build(force: bool = True, sanitize_to: Optional[str] = None) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, IEEE semantics: no fast-math).
+    With sanitize_to, build instead an AddressSanitizer + UndefinedBehavior-
+    Sanitizer copy at that path (any finding aborts); load it by running with
+    SPLITKV_ORACLE_LIB=<path> and gcc's libasan preloaded."""
+    out = sanitize_to or _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        san = (["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                "-fno-omit-frame-pointer", "-g"] if sanitize_to else [])
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                               "-Wall", "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+                               "-Wall", "-fno-fast-math"] + san + ["-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("SPLITKV_ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=True)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         L.oracle_validate_anchors.argtypes = [ctypes.c_int64, i64p, i64p, ctypes.c_int64, i64p]
         L.oracle_locality_match.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             i32p, i64p, i64p]
