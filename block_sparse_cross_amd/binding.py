@@ -35,7 +35,7 @@ EXPORTED = ("splitkv_workspace_bytes", "splitkv_validate_anchors", "splitkv_plan
             "splitkv_locality_match", "splitkv_plan_baseline",
             "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
             "splitkv_delta", "splitkv_gemm", "splitkv_gemm_pair", "splitkv_cast_bf16",
-            "splitkv_attn_bwd", "splitkv_attn_bwd_noalloc",
+            "splitkv_attn_bwd", "splitkv_attn_bwd_noalloc", "splitkv_own_block_local",
             "splitkv_status_str")
 
 SPLITKV_GEMM_NT, SPLITKV_GEMM_NN, SPLITKV_GEMM_TN = 0, 1, 2
@@ -82,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.splitkv_locality_match.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                              vp, vp, vp, vp]
         L.splitkv_locality_match.restype = ctypes.c_int
+        L.splitkv_own_block_local.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp,
+                                              ctypes.POINTER(ctypes.c_int64), vp]
+        L.splitkv_own_block_local.restype = ctypes.c_int
         L.splitkv_plan.argtypes = [A, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_int32, vp, vp, vp, vp, vp]
         L.splitkv_plan.restype = ctypes.c_int
@@ -285,17 +288,21 @@ def splitkv_plan_baseline(strategy: int, s: torch.Tensor, a: torch.Tensor, block
     return out
 
 
-def own_block_local(s: torch.Tensor, block_size: int):
+def own_block_local(s: torch.Tensor, block_size: int, stream: Optional[torch.cuda.Stream] = None):
     """Windows and key table for the own-block part of the mask (Figure 1 of the
-    Split-KV paper: a block's rows also attend all B tokens of their own block).
-    The block keys are laid out in block order as one chunk of n_blocks*B
-    positions, so block i's window is [iB, (i+1)B). Returns (s', a',
-    chunk_start, chunk_len) to pass to splitkv_attn_fwd / splitkv_attn_bwd with
-    the block keys and values."""
+    Split-KV paper: a block's rows also attend all B tokens of their own block),
+    from splitkv_own_block_local. Returns (s', a', chunk_start, chunk_len) to
+    pass to splitkv_attn_fwd / splitkv_attn_bwd with the block keys and
+    values (block i's window over them is [iB, (i+1)B))."""
     n = s.numel()
-    i = torch.arange(n, dtype=torch.int64, device=s.device)
-    return (i * block_size, (i + 1) * block_size,
-            torch.zeros(1, dtype=torch.int64, device=s.device), n * block_size)
+    s2 = torch.empty(n, dtype=torch.int64, device=s.device)
+    a2 = torch.empty(n, dtype=torch.int64, device=s.device)
+    cs = torch.empty(1, dtype=torch.int64, device=s.device)
+    clen = ctypes.c_int64(0)
+    _check("splitkv_own_block_local", lib().splitkv_own_block_local(
+        int(n), int(block_size), _ptr(s2), _ptr(a2), _ptr(cs), ctypes.byref(clen),
+        _stream(stream)))
+    return s2, a2, cs, int(clen.value)
 
 
 def splitkv_attn_fwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v,

@@ -48,7 +48,30 @@ validate_anchors_kernel(const int64_t* __restrict__ s, const int64_t* __restrict
   }
 }
 
+// Own-block windows: block i's rows also attend all B tokens of their own
+// block (Figure 1: the block is bidirectional). With the block keys laid out
+// in block order as one local segment of n_blocks * B positions starting at
+// 0, block i's window over that segment is [i B, (i + 1) B).
+__global__ void __launch_bounds__(256)
+own_block_windows_kernel(int64_t n_blocks, int64_t B, int64_t* __restrict__ s,
+                         int64_t* __restrict__ a, int64_t* __restrict__ chunk_start) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n_blocks) {
+    s[i] = i * B;
+    a[i] = (i + 1) * B;
+  }
+  if (i == 0) chunk_start[0] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_own_block_windows(int64_t n_blocks, int32_t B, int64_t* s, int64_t* a,
+                                    int64_t* chunk_start, hipStream_t stream) {
+  const int64_t grid = n_blocks > 0 ? (n_blocks + 255) / 256 : 1;
+  hipLaunchKernelGGL(own_block_windows_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     n_blocks, (int64_t)B, s, a, chunk_start);
+  return hipGetLastError();
+}
 
 hipError_t launch_validate_anchors(const int64_t* s, const int64_t* a, int64_t n_blocks,
                                    int64_t S, int64_t* result, hipStream_t stream) {

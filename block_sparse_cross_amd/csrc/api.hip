@@ -178,6 +178,19 @@ int splitkv_validate_anchors(const splitkv_anchors* an, int64_t S, int64_t* resu
                                             static_cast<hipStream_t>(stream)));
 }
 
+int splitkv_own_block_local(int64_t n_blocks, int32_t block_size, int64_t* s_out,
+                            int64_t* a_out, int64_t* chunk_start_out, int64_t* chunk_len,
+                            void* stream) {
+  if (n_blocks < 0 || block_size < 1 || chunk_len == nullptr || chunk_start_out == nullptr)
+    return SPLITKV_ERR_INVALID_ARG;
+  if (n_blocks > 0 && (s_out == nullptr || a_out == nullptr)) return SPLITKV_ERR_INVALID_ARG;
+  // the segment is one local chunk: its length must stay below 2^31 keys
+  if ((__int128)n_blocks * block_size >= ((__int128)1 << 31)) return SPLITKV_ERR_UNSUPPORTED;
+  *chunk_len = n_blocks * (int64_t)block_size;
+  return hip_status(launch_own_block_windows(n_blocks, block_size, s_out, a_out, chunk_start_out,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int splitkv_plan(const splitkv_anchors* an, int64_t S, int64_t m, int32_t P, int32_t J,
                  int64_t* chunk_cost, int32_t* chunk_owner, int32_t* rank_chunks,
                  int64_t* rank_load, void* stream) {

@@ -6,8 +6,11 @@
 // Work decomposition (bf16 path). A "query vector" is one (row, q-head) pair;
 // vectors are numbered v = row * G + hh, where G = hq / hkv and hh indexes the
 // q heads sharing kv head g, so consecutive vectors share a row (and so a
-// block and a key range) and sit contiguously in q. A workgroup takes 128
-// consecutive vectors of one kv head; each of its 4 waves owns 32 of them.
+// block and a key range) and sit contiguously in q. A workgroup takes 256
+// consecutive vectors of one kv head; each of its 8 waves (two per SIMD) owns
+// 32 of them, and each K and V tile copied into LDS serves all 256 (half the
+// copies per product of a 128-vector workgroup: 1.5% faster at the
+// strong-scaling share).
 // Because the local buffer is sorted by global position, every block reaches
 // one contiguous local key interval [lo, hi); the workgroup walks only the
 // 64-key tiles of the union of its vectors' intervals.
@@ -37,9 +40,9 @@ namespace splitkv {
 
 namespace {
 
-constexpr int kFwdThreads = 256;  // 4 waves
+constexpr int kFwdThreads = 512;  // 8 waves, two per SIMD
 constexpr int kVecPerWave = 32;
-constexpr int kVecPerWG = 128;
+constexpr int kVecPerWG = 256;
 constexpr int kKT = 64;           // keys per tile
 constexpr float kRescaleSlack = 8.f;
 
@@ -77,7 +80,7 @@ template <> struct Store4<bf16_t> {
 };
 
 template <int D, typename Tout>
-__global__ void __launch_bounds__(kFwdThreads, 2)
+__global__ void __launch_bounds__(kFwdThreads, 1)
 attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const bf16_t* __restrict__ v, Tout* __restrict__ o, float* __restrict__ lse,
                      const int2* __restrict__ block_range, int64_t n_vec, int G, int hq, int hkv,
@@ -88,7 +91,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16_t V0[kKT * D];
   __shared__ __attribute__((aligned(16))) bf16_t K1[kKT * D];
   __shared__ __attribute__((aligned(16))) bf16_t V1[kKT * D];
-  __shared__ int wave_lo[4], wave_hi[4];
+  __shared__ int wave_lo[kFwdThreads / 64], wave_hi[kFwdThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -134,7 +137,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __syncthreads();
   int lo = 0x7fffffff, hi = -1;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) { lo = min(lo, wave_lo[w]); hi = max(hi, wave_hi[w]); }
+  for (int w = 0; w < kFwdThreads / 64; ++w) { lo = min(lo, wave_lo[w]); hi = max(hi, wave_hi[w]); }
   // the same in every lane: keep the tile loop and its addressing scalar
   lo = __builtin_amdgcn_readfirstlane(lo);
   hi = __builtin_amdgcn_readfirstlane(hi);

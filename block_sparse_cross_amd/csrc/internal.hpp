@@ -51,6 +51,9 @@ hipError_t launch_locality_match(const int32_t* rank_chunks, int32_t P, int32_t 
                                  int32_t* phys_rank, int64_t* send_rows, int64_t* kept_moved,
                                  hipStream_t stream);
 
+hipError_t launch_own_block_windows(int64_t n_blocks, int32_t B, int64_t* s, int64_t* a,
+                                    int64_t* chunk_start, hipStream_t stream);
+
 hipError_t launch_validate_anchors(const int64_t* s, const int64_t* a, int64_t n_blocks,
                                    int64_t S, int64_t* result, hipStream_t stream);
 

@@ -101,6 +101,18 @@ size_t splitkv_workspace_bytes(int op, const splitkv_anchors* an, const splitkv_
  * the call. Requires S >= 0 and result != NULL; n_blocks == 0 gives {0, -1}. */
 int splitkv_validate_anchors(const splitkv_anchors* an, int64_t S, int64_t* result, void* stream);
 
+/* The own-block part of the mask (Figure 1: each block's rows also attend
+ * all B tokens of their own block, in both directions; the D term of §4.2).
+ * The block tokens' keys and values are laid out in block order as one local
+ * segment of n_blocks * B positions, so block i sees [i*B, (i+1)*B) of it.
+ * Writes that layout for splitkv_attn_fwd / splitkv_attn_bwd: s_out, a_out
+ * device int64 [n_blocks] (the windows), chunk_start_out device int64 [1]
+ * (= 0) and *chunk_len (HOST int64, = n_blocks * B: the segment is one chunk).
+ * Requires n_blocks * B < 2^31 (else SPLITKV_ERR_UNSUPPORTED). */
+int splitkv_own_block_local(int64_t n_blocks, int32_t block_size, int64_t* s_out,
+                            int64_t* a_out, int64_t* chunk_start_out, int64_t* chunk_len,
+                            void* stream);
+
 /* Chunk pricing (Eq. 6) and cost-aware LPT (§4.2).
  *   cost[j]  = B * sum_i ( min(a_i, j*m + m) - max(s_i, j*m) )^+, j < P*J   (int64)
  *   Chunks are taken by cost, highest first (equal costs: lower j first); each

@@ -167,3 +167,12 @@ def test_workspace_queries_with_missing_structs(L):
     assert b.splitkv_workspace_bytes(b.SPLITKV_OP_FWD) == 0
     assert b.splitkv_workspace_bytes(b.SPLITKV_OP_BWD, an()) == 0
     assert b.splitkv_workspace_bytes(99, an(), hd(), loc()) == 0
+
+
+def test_own_block_layout(L):
+    n = ctypes.c_int64(0)
+    assert L.splitkv_own_block_local(-1, 16, P16, P16, P16, ctypes.byref(n), None) == INV
+    assert L.splitkv_own_block_local(4, 0, P16, P16, P16, ctypes.byref(n), None) == INV
+    assert L.splitkv_own_block_local(4, 16, None, P16, P16, ctypes.byref(n), None) == INV
+    assert L.splitkv_own_block_local(4, 16, P16, P16, P16, None, None) == INV
+    assert L.splitkv_own_block_local(1 << 27, 16, P16, P16, P16, ctypes.byref(n), None) == UNS

@@ -130,3 +130,16 @@ def test_own_block_partial_at_full_size_sampled_blocks():
     assert_close_bf16(to_f64(dq)[rows], dq_ref, "dq (own blocks)")
     assert_close_bf16(to_f64(dkb)[rows], dk_ref, "dk (own blocks)")
     assert_close_bf16(to_f64(dvb)[rows], dv_ref, "dv (own blocks)")
+
+
+@pytest.mark.parametrize("n,B", [(0, 16), (1, 16), (7, 4), (512, 16), (4096, 16)])
+def test_own_block_layout_matches_oracle(n, B):
+    """splitkv_own_block_local writes the windows [iB, (i+1)B), chunk start 0
+    and segment length n B that the oracle's own-block windows define."""
+    s = torch.zeros(n, dtype=torch.int64, device="cuda")
+    bs, ba, bcs, blen = binding.own_block_local(s, B)
+    torch.cuda.synchronize()
+    rs, ra, rp = oracle.own_block_windows(n, B)
+    np.testing.assert_array_equal(bs.cpu().numpy(), rs)
+    np.testing.assert_array_equal(ba.cpu().numpy(), ra)
+    assert bcs.cpu().numpy().tolist() == [0] and blen == n * B == len(rp)
