@@ -146,9 +146,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="strong8",
-                    help="strong8 (default: the largest fwd+bwd share on one GPU), weak8, "
-                         "qs4/qs8/qs16/qs32, weak64 or tiny")
+    ap.add_argument("--workload", default=None,
+                    help="strong8 (the default: the largest fwd+bwd share on one GPU), weak8, "
+                         "qs4/qs8/qs16/qs32, weak64 or tiny; --layer defaults to weak8")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=24,
@@ -174,7 +174,10 @@ def parse():
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--command", default="",
                     help="with --summarize-counters: the profiling commands, for the record")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.workload is None:
+        args.workload = "weak8" if args.layer else "strong8"
+    return args
 
 
 def main():
