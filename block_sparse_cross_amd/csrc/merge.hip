@@ -2,14 +2,19 @@
 // Parallelism for Training Diffusion Drafters", §4.1):
 //   lse = log sum_p exp(lse_p),   o = sum_p exp(lse_p - lse) o_p.
 //
-// Bandwidth-bound: every byte of the P partial outputs is read once. One
-// thread owns 8 consecutive output elements of one row and streams the P
-// partials with 16-byte (bf16) or 2x16-byte (fp32) loads; the d/8 threads of a
-// row are adjacent, so each partial's row segment is read fully coalesced.
-// The lse_p of a row are read by all its threads (cache broadcast). The
-// partials are read with non-temporal loads (they are not read again); on
-// MI355X that alone took the weak-scaling share's merge (P = 8, 262144 rows of
-// 128) from 5.49 to 6.28 TB/s, and P = 64 from 5.40 to 5.98 TB/s.
+// Bandwidth-bound: every byte of the P partial outputs is read once. A unit
+// is 8 consecutive output elements of one row, read from each partial with one
+// 16-byte (bf16) or two 16-byte (fp32) non-temporal loads (the partials are not
+// read again); the d/8 units of a row are adjacent, so each partial's row
+// segment is read fully coalesced, and the lse_p of a row are read by all its
+// units' threads (cache broadcast). Each thread owns four units, 256 units
+// apart, and keeps two partials (bf16) in flight for all four: on MI355X that
+// took the merge at P = 32 over 2M rows of 128 from 65% to 69.5% of HBM
+// bandwidth and P = 9 from 67% to 75% (the earlier kernel, one unit per thread
+// with eight partials in flight, kept many DRAM rows of one bank open at once
+// when the partials lie a power of two apart); P = 8 and 64 were unchanged or
+// up to 3% faster. Non-temporal loads had taken the weak-scaling share's merge
+// (P = 8, 262144 rows) from 5.49 to 6.28 TB/s.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -18,7 +23,7 @@ namespace splitkv {
 namespace {
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeGroup = 8;  // partial loads kept in flight per thread
+constexpr int kMergeRows = 4;  // units (8 outputs of a row) per merge thread
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -84,101 +89,165 @@ template <> struct Vec8<float> {
   }
 };
 
-template <typename Tin, typename Tout>
-__global__ void __launch_bounds__(kMergeThreads)
-lse_merge_kernel(int P, int64_t rows, int d, const Tin* __restrict__ o_parts,
-                 const float* __restrict__ lse_parts, Tout* __restrict__ o,
-                 float* __restrict__ lse) {
+// Where a thread's units lie. A unit u holds elements [8u, 8u + 8) of each
+// partial (row u / (d/8)); a thread's R units are kMergeThreads apart, so each
+// of its loads is part of a workgroup-wide contiguous run.
+//  - Whole (d = 64, 128 or 256): all R units exist, and the r-th sits a fixed,
+//    compile-time distance from the first in rows and elements, so all its
+//    loads come off one address with constant offsets (a group's loads then
+//    issue back to back).
+//  - Edge (the tail of the rows, or any other d): units are placed one by one;
+//    a unit past the end repeats the last one (loaded, never stored).
+// Launched separately, so the tail's bookkeeping costs the main launch no
+// registers.
+template <int kSegs>
+struct WholeUnits {
+  static constexpr int kRowStep = kMergeThreads / kSegs;  // rows between a thread's units
+  int64_t unit0, row0;
+  bool head0;  // the first unit starts its row
+  __device__ int64_t unit(int r) const { return unit0 + (int64_t)r * kMergeThreads; }
+  __device__ int64_t row(int r) const { return row0 + r * kRowStep; }
+  __device__ bool live(int) const { return true; }
+  __device__ bool head(int) const { return head0; }
+};
+template <int R>
+struct EdgeUnits {
+  int64_t unit_[R], row_[R];
+  bool live_[R];
+  int segs;
+  __device__ int64_t unit(int r) const { return unit_[r]; }
+  __device__ int64_t row(int r) const { return row_[r]; }
+  __device__ bool live(int r) const { return live_[r]; }
+  __device__ bool head(int r) const { return row_[r] * segs == unit_[r]; }
+};
+
+template <typename Tin, typename Tout, int R, class Units>
+__device__ __forceinline__ void merge_units(int P, int64_t rows, int d, const Tin* o_parts,
+                                            const float* lse_parts, Tout* o, float* lse,
+                                            const Units& U) {
   using Raw = typename Vec8<Tin>::Raw;
-  constexpr int G = kMergeGroup;
-  const int segs = d / 8;
-  const int64_t units = rows * segs;
-  const int64_t unit = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
-  if (unit >= units) return;
-  int64_t row;
-  int seg;
-  if (units <= INT32_MAX) {  // uniform: 32-bit division when the index fits
-    const uint32_t u32 = (uint32_t)unit;
-    row = u32 / (uint32_t)segs;
-    seg = (int)(u32 - (uint32_t)row * (uint32_t)segs);
-  } else {
-    row = unit / segs;
-    seg = (int)(unit % segs);
-  }
-  const Tin* src = o_parts + row * d + seg * 8;
+  constexpr int G = sizeof(Tin) == 2 ? 2 : 1;  // partials per group
   const int64_t pstride = rows * (int64_t)d;
-  const float* lrow = lse_parts + row;
-
-  // Partials are taken G at a time: a group's lse_p and its o_p segments are
-  // loaded together (LSEs first, so they arrive first), and the next group's
-  // loads are in flight while the current one is summed. Indices past the
-  // last partial load partial P-1 again (unused), so every load is issued
-  // unconditionally and the waits can count them.
   auto pidx = [P](int p) -> int64_t { return p < P ? p : P - 1; };
-  float lcur[G];
-  Raw cur[G];
+  auto load_group = [&](int g, float (*l)[G], Raw (*x8)[G]) {
 #pragma unroll
-  for (int u = 0; u < G; ++u) lcur[u] = lrow[pidx(u) * rows];
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-  for (int u = 0; u < G; ++u) cur[u] = Vec8<Tin>::ld(src + pidx(u) * pstride);
+      for (int u = 0; u < G; ++u) l[r][u] = lse_parts[pidx(g + u) * rows + U.row(r)];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < G; ++u)
+        x8[r][u] = Vec8<Tin>::ld(o_parts + pidx(g + u) * pstride + U.unit(r) * 8);
+  };
 
-  float mx = -INFINITY;
+  // Partials are taken G at a time for all R units: a group's lse_p and its
+  // o_p segments are loaded together (LSEs first, so they arrive first), and
+  // the next group's loads are in flight while the current one is summed.
+  // Indices past the last partial load partial P-1 again (unused), so every
+  // load is issued unconditionally and the waits can count them.
+  float lcur[R][G];
+  Raw cur[R][G];
+  load_group(0, lcur, cur);
+  float mx[R];
 #pragma unroll
-  for (int u = 0; u < G; ++u)
-    if (u < P) mx = fmaxf(mx, lcur[u]);
-  for (int p0 = G; p0 < P; p0 += G) {
-    float l[G];
-#pragma unroll
-    for (int u = 0; u < G; ++u) l[u] = lrow[pidx(p0 + u) * rows];
+  for (int r = 0; r < R; ++r) {
+    mx[r] = -INFINITY;
 #pragma unroll
     for (int u = 0; u < G; ++u)
-      if (p0 + u < P) mx = fmaxf(mx, l[u]);
+      if (u < P) mx[r] = fmaxf(mx[r], lcur[r][u]);
+  }
+  for (int p0 = G; p0 < P; p0 += G) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float l[G];
+#pragma unroll
+      for (int u = 0; u < G; ++u) l[u] = lse_parts[pidx(p0 + u) * rows + U.row(r)];
+#pragma unroll
+      for (int u = 0; u < G; ++u)
+        if (p0 + u < P) mx[r] = fmaxf(mx[r], l[u]);
+    }
   }
 
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  Tout* orow = o + row * d + seg * 8;
-  if (mx == -INFINITY) {  // every partial empty
-    Vec8<Tout>::store(orow, acc);
-    if (seg == 0) lse[row] = -INFINITY;
-    return;
-  }
   // Unnormalised sum with weights exp(lse_p - max), p ascending; empty
-  // partials weigh 0.
-  float wsum = 0.f;
-  auto sum_group = [&](int g, const float* l, const Raw* x8) {
+  // partials weigh 0. (A row whose partials are all empty has max = -inf; its
+  // sums are discarded below.)
+  float acc[R][8], wsum[R];
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
-      if (g + u < P) {
-        const float w = __expf(l[u] - mx);
-        float x[8];
-        Vec8<Tin>::cvt(x8[u], x);
-        wsum += w;
+  for (int r = 0; r < R; ++r) {
+    wsum[r] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+  }
+  auto sum_group = [&](int g, float (*l)[G], Raw (*x8)[G]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        if (g + u < P) {
+          const float w = __expf(l[r][u] - mx[r]);
+          float x[8];
+          Vec8<Tin>::cvt(x8[r][u], x);
+          wsum[r] += w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(w, x[e], acc[r][e]);
+        }
       }
-    }
-  };
-  auto load_group = [&](int g, float* l, Raw* x8) {
-#pragma unroll
-    for (int u = 0; u < G; ++u) l[u] = lrow[pidx(g + u) * rows];
-#pragma unroll
-    for (int u = 0; u < G; ++u) x8[u] = Vec8<Tin>::ld(src + pidx(g + u) * pstride);
   };
   // Two register buffers in turn, so a group's loads are issued before the
   // group ahead of it is summed and no buffer is copied.
-  float lnx[G];
-  Raw nxt[G];
+  float lnx[R][G];
+  Raw nxt[R][G];
   for (int g = 0; g < P; g += 2 * G) {
     if (g + G < P) load_group(g + G, lnx, nxt);
     sum_group(g, lcur, cur);
     if (g + 2 * G < P) load_group(g + 2 * G, lcur, cur);
     if (g + G < P) sum_group(g + G, lnx, nxt);
   }
-  const float inv = 1.f / wsum;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] *= inv;
-  Vec8<Tout>::store(orow, acc);
-  if (seg == 0) lse[row] = mx + __logf(wsum);
+  for (int r = 0; r < R; ++r) {
+    if (!U.live(r)) continue;
+    const bool empty = mx[r] == -INFINITY;  // every partial empty
+    const float inv = empty ? 0.f : 1.f / wsum[r];
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = empty ? 0.f : acc[r][e] * inv;
+    Vec8<Tout>::store(o + U.unit(r) * 8, out);
+    if (U.head(r)) lse[U.row(r)] = empty ? -INFINITY : mx[r] + __logf(wsum[r]);
+  }
+}
+
+// Units [unit_base, unit_base + gridDim.x * kMergeThreads * R), clipped to
+// rows * d/8 on the Edge form (kSegs = 0); the Whole form (kSegs = d/8) takes
+// only whole workgroups.
+template <typename Tin, typename Tout, int R, int kSegs>
+__global__ void __launch_bounds__(kMergeThreads)
+lse_merge_kernel(int P, int64_t rows, int d, int64_t unit_base, const Tin* __restrict__ o_parts,
+                 const float* __restrict__ lse_parts, Tout* __restrict__ o,
+                 float* __restrict__ lse) {
+  const int segs = d / 8;
+  const int64_t units = rows * segs;
+  const int64_t first = unit_base + (int64_t)blockIdx.x * (kMergeThreads * R) + threadIdx.x;
+  if (first >= units) return;
+  if constexpr (kSegs > 0) {
+    WholeUnits<kSegs> U;
+    U.unit0 = first;
+    U.row0 = first / kSegs;
+    U.head0 = first % kSegs == 0;
+    merge_units<Tin, Tout, R>(P, rows, d, o_parts, lse_parts, o, lse, U);
+  } else {
+    EdgeUnits<R> U;
+    U.segs = segs;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t unit = first + (int64_t)r * kMergeThreads;
+      U.live_[r] = unit < units;
+      U.unit_[r] = U.live_[r] ? unit : units - 1;
+      U.row_[r] = units <= INT32_MAX ? (int64_t)((uint32_t)U.unit_[r] / (uint32_t)segs)
+                                     : U.unit_[r] / segs;
+    }
+    merge_units<Tin, Tout, R>(P, rows, d, o_parts, lse_parts, o, lse, U);
+  }
 }
 
 // Eq. 4 split into the two halves each rank applies when the partials sit on
@@ -281,12 +350,29 @@ hipError_t launch_delta_t(int64_t rows, int32_t d, const void* o, const void* do
 template <typename Tin, typename Tout>
 hipError_t launch_merge_t(int32_t P, int64_t rows, int32_t d, const void* o_parts,
                           const float* lse_parts, void* o, float* lse, hipStream_t stream) {
-  const int64_t units = rows * (d / 8);
-  const int64_t grid = (units + kMergeThreads - 1) / kMergeThreads;
-  hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout>), dim3((unsigned)grid), dim3(kMergeThreads),
-                     0, stream, P, rows, d, static_cast<const Tin*>(o_parts), lse_parts,
-                     static_cast<Tout*>(o), lse);
-  return hipGetLastError();
+  const int segs = d / 8;
+  const int64_t units = rows * segs;
+  constexpr int64_t kWholeUnits = (int64_t)kMergeThreads * kMergeRows;  // per workgroup
+  const int64_t whole = (segs == 8 || segs == 16 || segs == 32) ? units / kWholeUnits : 0;
+  if (whole > 0) {
+    const dim3 grid((unsigned)whole);
+    auto kern = segs == 8    ? lse_merge_kernel<Tin, Tout, kMergeRows, 8>
+                : segs == 16 ? lse_merge_kernel<Tin, Tout, kMergeRows, 16>
+                             : lse_merge_kernel<Tin, Tout, kMergeRows, 32>;
+    hipLaunchKernelGGL(kern, grid, dim3(kMergeThreads), 0, stream, P, rows, d, (int64_t)0,
+                       static_cast<const Tin*>(o_parts), lse_parts, static_cast<Tout*>(o), lse);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rest = units - whole * kWholeUnits;
+  if (rest > 0) {
+    hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout, 1, 0>),
+                       dim3((unsigned)((rest + kMergeThreads - 1) / kMergeThreads)),
+                       dim3(kMergeThreads), 0, stream, P, rows, d, whole * kWholeUnits,
+                       static_cast<const Tin*>(o_parts), lse_parts, static_cast<Tout*>(o), lse);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace

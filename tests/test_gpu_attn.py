@@ -185,10 +185,11 @@ def test_tiny_fp32_workload_partials_merge_and_backward():
     (8, 5000, 128, "fp32", "fp32"),
     (64, 4096, 128, "bf16", "bf16"),
     (7, 129, 8, "fp32", "bf16"),
-    (9, 777, 128, "bf16", "bf16"),      # partials taken in groups of 8: one full group + 1
+    (9, 777, 128, "bf16", "bf16"),      # bf16 partials go in pairs: four pairs + 1
     (17, 300, 64, "fp32", "fp32"),      # the third group is reloaded into the first buffer
     (24, 257, 128, "bf16", "fp32"),
-    (33, 100, 16, "fp32", "bf16"),
+    (33, 100, 16, "fp32", "bf16"),      # d/8 = 2: every unit on the edge launch
+    (5, 600, 256, "bf16", "bf16"),      # d = 256 on the whole-workgroup launch, plus a tail
 ])
 def test_merge(P, rows, d, in_dt, out_dt):
     o_parts, lse_parts = inputs.gen_partials(P, rows, d, seed=P * 1000 + rows, dtype=in_dt)
@@ -205,12 +206,16 @@ def test_merge(P, rows, d, in_dt, out_dt):
     assert (got[np.isneginf(l_ref)] == 0).all()
 
 
-@pytest.mark.parametrize("P", [3, 8, 11, 20, 40])
-def test_merge_one_live_partial_per_row(P):
+@pytest.mark.parametrize("P,d", [(3, 32), (8, 32), (11, 32), (20, 32), (40, 32),
+                                 (3, 128), (11, 128), (40, 128)])
+def test_merge_one_live_partial_per_row(P, d):
     """Row r sees only partial r mod P: its weight is exp(0) = 1, so the merged
     row must be exactly that partial's row and lse its lse_p (fp32 in and out).
-    A wrong partial index, group offset or buffer turn picks another row."""
-    rows, d = 3 * P + 5, 32
+    A wrong partial index, group offset, buffer turn or unit placement picks
+    another row. d = 128 with 64P + 5 rows puts most rows on the
+    whole-workgroup launch (1024 units of 8 elements each) and the rest on
+    the edge launch."""
+    rows = 3 * P + 5 if d == 32 else 64 * P + 5
     _, lse_parts = inputs.gen_partials(P, rows, d, seed=P, dtype="fp32")
     # every (partial, row) distinct and nonzero, so a wrong pick cannot match
     o_parts = (np.arange(P * rows * d, dtype=np.float32).reshape(P, rows, d) % 65521.0) + 1.0
