@@ -397,6 +397,13 @@ def main():
     # ceilings the attention and merge rates can be read against).
     result["context"] = box_ceilings(torch, dev)
     result["merge_frac_copy"] = round(merge_gbs / result["context"]["device_copy_gbs"], 4)
+    # the attention rates against the product loop's rate on random operands
+    # (the backward's executed products are 14 d-contractions per pair for the
+    # 10 credited)
+    ceil = result["context"]["mfma_loop_random_bf16_tflops"]
+    result["frac_of_mfma_loop"] = {"fwd": round(fwd_tflops / ceil, 4),
+                                   "bwd_credited": round(bwd_tflops / ceil, 4),
+                                   "bwd_executed": round(bwd_tflops * 1.4 / ceil, 4)}
 
     if args.copy_calibration:
         x = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
@@ -412,8 +419,10 @@ def main():
 
 
 def box_ceilings(torch, dev) -> dict:
-    """Dense bf16 8192^3 product (torch.matmul, the vendor library) and a 1 GiB
-    device-to-device copy, each the median of 5 timed runs after 2 warmups."""
+    """Dense bf16 8192^3 product (torch.matmul, the vendor library), a 1 GiB
+    device-to-device copy and a pure matrix-core loop (libsplitkv_ceiling.so)
+    on random and on constant bf16 operands, each the median of 5 timed runs
+    after 2 warmups."""
     def med_ms(fn):
         for _ in range(2):
             fn()
@@ -435,10 +444,48 @@ def box_ceilings(torch, dev) -> dict:
     y = torch.empty_like(x)
     copy_ms = med_ms(lambda: y.copy_(x))
     del x, y
+    mfma = mfma_ceiling_tflops(torch, dev, med_ms)
     return {"dense_bf16_gemm_tflops": round(2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
             "device_copy_gbs": round(2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
-            "what": "torch.matmul bf16 8192^3 and a 1 GiB device copy (read + write bytes), "
+            "mfma_loop_random_bf16_tflops": mfma["random"],
+            "mfma_loop_constant_bf16_tflops": mfma["constant"],
+            "what": "torch.matmul bf16 8192^3; a 1 GiB device copy (read + write bytes); a loop "
+                    "of v_mfma_f32_32x32x16_bf16 products alone (2048 workgroups, 8 "
+                    "accumulators per wave) on random N(0, 0.05^2) and on constant operands; "
                     "medians of 5 after the timed steps"}
+
+
+def mfma_ceiling_tflops(torch, dev, med_ms) -> dict:
+    """Rate of the matrix-core loop of libsplitkv_ceiling.so (the practical
+    product ceiling the attention kernels run against: the board's power limit
+    lowers the clock when the products toggle real data)."""
+    import ctypes
+    from block_sparse_cross_amd import build as B
+    if not os.path.exists(B.CEILING_LIB):
+        raise RuntimeError("%s is missing: build first (__graft_entry__.build())" % B.CEILING_LIB)
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    fn = lib.splitkv_ceiling_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    n_wg, iters = 2048, 2000
+    flop = float(n_wg) * 4 * iters * 32 * 32768
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    operands = {"random": (torch.randn(8 * 64 * 8, generator=g, device=dev) * 0.05).to(
+                    torch.bfloat16),
+                "constant": torch.full((8 * 64 * 8,), 0.0078125, device=dev,
+                                       dtype=torch.bfloat16)}
+    out = torch.empty(n_wg * 256, device=dev)
+    res = {}
+    for name, fr in operands.items():
+        def run():
+            rc = fn(ctypes.c_void_p(fr.data_ptr()), iters, n_wg, ctypes.c_void_p(out.data_ptr()),
+                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError("splitkv_ceiling_mfma failed: %d" % rc)
+        res[name] = round(flop / (med_ms(run) * 1e-3) / 1e12, 1)
+    return res
 
 
 def layer_bench(args):

@@ -17,6 +17,9 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsplitkv.so")
 SOURCES = ["api.hip", "anchors.hip", "plan.hip", "merge.hip", "attn_fwd.hip", "attn_bwd.hip",
            "gemm.hip"]
+# The matrix-core ceiling loop (bench.py's context), a library of its own.
+CEILING_LIB = os.path.join(HERE, "libsplitkv_ceiling.so")
+CEILING_SOURCES = ["mfma_ceiling.hip"]
 ARCH = os.environ.get("SPLITKV_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -54,23 +57,30 @@ def _compile(src: str, objdir: str = OBJDIR, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, host_sanitize_to: str = "") -> str:
-    """Compile and link the library (in-tree), or, with host_sanitize_to, a
-    copy whose host code carries the sanitizers, at that path."""
-    out = host_sanitize_to or LIB
-    objdir = os.path.join(os.path.dirname(out), "_obj_san") if host_sanitize_to else OBJDIR
-    extra = HOST_SANITIZE if host_sanitize_to else []
-    os.makedirs(objdir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda src: _compile(src, objdir, extra), SOURCES))
+def _link(objs, out: str, extra=()) -> None:
     tmp = out + ".tmp%d" % os.getpid()
-    link_extra = ["-Xarch_host", "-shared-libsan"] if host_sanitize_to else []
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + link_extra + \
-        ["-o", tmp] + objs
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + list(extra) + ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, out)
+
+
+def build(verbose: bool = False, host_sanitize_to: str = "") -> str:
+    """Compile and link the library (in-tree) and the ceiling library beside it,
+    or, with host_sanitize_to, only a copy of the library whose host code
+    carries the sanitizers, at that path."""
+    out = host_sanitize_to or LIB
+    objdir = os.path.join(os.path.dirname(out), "_obj_san") if host_sanitize_to else OBJDIR
+    extra = HOST_SANITIZE if host_sanitize_to else []
+    os.makedirs(objdir, exist_ok=True)
+    srcs = SOURCES if host_sanitize_to else SOURCES + CEILING_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda src: _compile(src, objdir, extra), srcs)))
+    _link([objs[x] for x in SOURCES], out,
+          ["-Xarch_host", "-shared-libsan"] if host_sanitize_to else [])
+    if not host_sanitize_to:
+        _link([objs[x] for x in CEILING_SOURCES], CEILING_LIB)
     if verbose:
         print("built", out)
     return out

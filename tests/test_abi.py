@@ -63,3 +63,21 @@ def test_library_has_no_oracle_symbols(lib):
     for name in ("oracle_lpt", "oracle_partial_attn", "oracle_merge"):
         with pytest.raises(AttributeError):
             getattr(lib, name)
+
+
+def test_ceiling_library_exports_its_loop(lib):
+    """The matrix-core ceiling loop bench.py reports beside the attention rates
+    is a library of its own, built with the main one; it rejects bad arguments
+    on the host (no launch)."""
+    from block_sparse_cross_amd import build
+    if not os.path.exists(build.CEILING_LIB):
+        build.build()
+    c = ctypes.CDLL(build.CEILING_LIB)
+    fn = c.splitkv_ceiling_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    assert fn(None, 1, 1, None, None) == -1
+    assert fn(ctypes.c_void_p(16), -1, 1, ctypes.c_void_p(16), None) == -1
+    assert fn(ctypes.c_void_p(16), 1, 0, ctypes.c_void_p(16), None) == -1
+    assert fn(ctypes.c_void_p(17), 1, 1, ctypes.c_void_p(16), None) == -1
