@@ -1,11 +1,15 @@
 """One draft layer in Split-KV form on the GPU (block_sparse_cross_amd.layer)
 against the oracle's composition (fp64 on the exact bf16 inputs): forward Y and
-every gradient, at a small size spanning several tiles of every kernel.
+every gradient, at a small size spanning several tiles of every kernel, and Y
+and dX through the oracle's whole chain on sampled rows at the weak-scaling
+share with the 27B drafter's width.
 
-Tolerance: the GPU keeps q, k, v, the partials, the rescaled partials, do and
-the rank-summed dq as bf16 between steps (seven roundings of 2^-8 relative on
-the way to a weight gradient), so outputs are held to a relative Frobenius
-error <= 2e-2 and a max error <= 5e-2 of the largest reference magnitude."""
+Tolerance: the bf16 bounds the attention outputs and gradients are held to
+(relative Frobenius error <= 1e-2, max abs error <= 2e-2), the absolute bound
+scaled by the reference's largest magnitude where that exceeds 1 (the weight
+gradients are sums over thousands of rows and reach ~10). The GPU keeps q, k,
+v, the partials, the rescaled partials, do and the rank-summed dq as bf16
+between steps; measured errors are <= 5e-3 relative Frobenius."""
 import numpy as np
 import pytest
 import torch
@@ -21,8 +25,10 @@ pytestmark = pytest.mark.gpu
 def assert_layer_close(got, ref, what):
     assert np.isfinite(got).all(), what
     rf = rel_fro(got, ref)
-    mx = float(np.abs(got - ref).max()) / max(float(np.abs(ref).max()), 1e-30)
-    assert rf <= 2e-2 and mx <= 5e-2, "%s: rel fro %.3e, rel max %.3e" % (what, rf, mx)
+    err = float(np.abs(got - ref).max())
+    bound = 2e-2 * max(1.0, float(np.abs(ref).max()))
+    assert rf <= 1e-2 and err <= bound, "%s: rel fro %.3e, max err %.3e (bound %.3e)" % (
+        what, rf, err, bound)
 
 
 def build_case(seed, P=4, J=2, m=128, B=16, hq=4, hkv=2, d=64, H=192, L=512, A=6):
@@ -75,8 +81,8 @@ def test_layer_full_size_weak8_sampled():
     d_model 5120, 32/8 heads of 128) through the same calls bench.py --layer
     times. Each product is checked on sampled rows against the fp64 product of
     the bf16 operands the GPU used (its own q, rescaled partials, do, dq, dk,
-    dv), i.e. the definition of that step; the attention steps are covered at
-    this size by the full-size attention tests."""
+    dv), i.e. the definition of that step; then Y and dX on the same rows
+    against the oracle's whole chain from the layer inputs."""
     w = inputs.WORKLOADS["weak8"]
     H, seed = 5120, 0
     s, a = inputs.workload_anchors(w, seed)
@@ -138,3 +144,37 @@ def test_layer_full_size_weak8_sampled():
         dkp = to_f64(layer.dk[pp]).reshape(-1, nkv)
         dwk_ref += dkp[:, kc].T @ vals64(U[pp])
     assert_layer_close(to_f64(g["dWk"])[kc], dwk_ref, "dWk = sum_p dk_p^T U_p")
+
+    # The sampled rows through the oracle's own chain from the layer inputs
+    # (fp64 on the bf16 values), no GPU intermediate: q = X Wq^T; every rank's
+    # k_p = U_p Wk^T, v_p = U_p Wv^T and its Eq. 3 partial; the Eq. 4 merge as
+    # each rank applies it (LSE reduction, rescaled partials); Y = the summed
+    # OProj of the rescaled partials + bo. Backward: do = dY Wo, Delta =
+    # sum_p <do, obar_p>, each rank's dq (Algorithm 1, global lse and Delta),
+    # summed; dX = dq Wq.
+    n, scale = len(rows), w.d ** -0.5
+    q_r = (x64[rows] @ wq.T).reshape(n, w.hq, w.d)
+    parts = []
+    for pp in range(w.P):
+        pos = oracle.local_key_positions(bundles[pp], w.m)
+        u64p = vals64(U[pp])
+        kp = (u64p @ wk.T).reshape(-1, w.hkv, w.d)
+        vp = (u64p @ wv.T).reshape(-1, w.hkv, w.d)
+        o_p, l_p = oracle.partial_attn(rows, w.B, s, a, q_r, pos, kp, vp, scale)
+        parts.append((pos, kp, vp, o_p, l_p))
+    lse_r = oracle.lse_reduce(np.stack([pt[4].reshape(-1) for pt in parts]))
+    obar_r = [oracle.lse_rescale(pt[3].reshape(-1, w.d), pt[4].reshape(-1), lse_r).reshape(n, nq)
+              for pt in parts]
+    assert_layer_close(Yh[rows], sum(ob @ wo.T for ob in obar_r) + bo[None, :],
+                       "Y, oracle chain from X, U and the weights")
+    do_r = (dy[rows] @ wo).reshape(n, w.hq, w.d)
+    dlt_r = sum(oracle.delta(ob.reshape(n, w.hq, w.d), do_r) for ob in obar_r)
+    # the oracle's backward indexes q, do, lse and Delta by row: full-height
+    # arrays holding the sampled rows (the others are not read for them)
+    full = lambda x: np.zeros((w.Q,) + x.shape[1:])  # noqa: E731
+    qf, dof, lf, df = full(q_r), full(do_r), full(dlt_r), full(dlt_r)
+    qf[rows], dof[rows], lf[rows], df[rows] = q_r, do_r, lse_r.reshape(n, w.hq), dlt_r
+    dq_r = sum(oracle.attn_bwd(w.B, s, a, qf, dof, lf, df, pt[0], pt[1], pt[2], scale, rows,
+                               np.zeros(0, dtype=np.int64))[0] for pt in parts)
+    assert_layer_close(to_f64(g["dX"])[rows], dq_r.reshape(n, nq) @ wq,
+                       "dX, oracle chain from X, U, dY and the weights")
