@@ -273,26 +273,60 @@ lpt_kernel(const int64_t* __restrict__ cost, int n_chunks, int P, int J,
 // r J .. r J + J - 1; placing bundle b on rank r keeps
 //   keep(b, r) = m * #{ chunks of b whose home is r }
 // rows. The best placement is a linear assignment problem, solved exactly by
-// the Hungarian method: row (bundle) and column (rank) potentials on the cost
-// J m - keep >= 0 (the constant leaves the best placement unchanged, and with
-// non-negative costs every slack stays >= 0), bundles entering one at a time
-// along a shortest augmenting path.
+// the Hungarian method on the cost c(b, r) = J - keep(b, r) / m in [0, J]
+// (the constant and the unit leave the best placement unchanged), with row
+// (bundle) and column (rank) potentials, u(b) + v(r) <= c(b, r) everywhere and
+// equality on placed pairs.
+//
+// Greedy start (column reduction): v(r) is the least cost in column r, and the
+// bundle that attains it (lowest on ties) takes the column unless a lower
+// column claims it too; all u start at 0, so the potentials are feasible and
+// the placed pairs tight. Every bundle left over then enters along a shortest
+// augmenting path: one Dijkstra-like scan per step over the free columns,
+// potentials moved by the step's least slack.
 //
 // One wave. Lane l keeps, in registers, column l + 1 + 64 k and row
-// l + 1 + 64 k (k < kMatchSlots): the column's potential, slack (minv),
-// predecessor (way), used flag and matched row, and the row's potential and
-// tree flag (a row is in the tree once the column it is matched to is used;
-// those rows take + delta, the used columns - delta). The keep counts sit in
-// LDS as a [P][P] table. A step scans the lane's free columns (ascending, so
-// ties keep the lowest) and packs (slack, column) into one 64-bit key whose
-// wave minimum (DPP steps and four lane reads, no LDS) is the smallest slack
-// at the lowest column: the result is unique. Single values of other lanes are read with readlane at a uniform
-// lane. Chunk ids outside [0, P J) count as neither kept nor sent.
+// l + 1 + 64 k (k < SLOTS, SLOTS = ceil(P / 64)): the column's potential,
+// slack (minv), predecessor (way), used flag and matched row, and the row's
+// potential and tree flag (a row is in the tree once the column it is matched
+// to is used; those rows take + delta, the used columns - delta). The keep
+// counts sit in LDS as a [P][P] table. A step scans the lane's unused columns
+// and packs (slack, taken, column) into one 32-bit key whose wave minimum (DPP
+// steps and four lane reads) is the smallest slack, among equal slacks a
+// column no bundle holds yet (the path then ends at once: with costs in
+// [0, J] ties are the rule, and at P = 64 this cuts the steps tenfold), then
+// the lowest column: the result is unique. A free column
+// keeps its starting potential (0 <= v <= J), so an entering bundle's path is
+// at most J long and every potential moves by at most J per augmentation:
+// slacks stay below 3 (P + 1) J <= 2^14 and keys below 2^24. Single values of
+// other lanes are read with readlane at a uniform lane. Chunk ids outside
+// [0, P J) count as neither kept nor sent.
 constexpr int kMatchThreads = kWave;
-constexpr int kMatchSlots = kMaxMatchRanks / kWave;
 constexpr int kColBits = 9;  // columns 1 .. 256 in the low bits of a wave-minimum key
+constexpr unsigned kNoKey32 = 0xffffffffu;
+constexpr int kMatchInf = 1 << 30;
 static_assert(kMaxMatchRanks < (1 << kColBits), "column must fit its key bits");
 
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_min_step32(unsigned v) {
+  const unsigned o = (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  return o < v ? o : v;
+}
+
+// Wave minimum of a 32-bit key, wave-uniform (as wave_min_key).
+__device__ __forceinline__ unsigned wave_min_u32(unsigned v) {
+  v = dpp_min_step32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_min_step32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_min_step32<0x141>(v);  // row_half_mirror
+  v = dpp_min_step32<0x140>(v);  // row_mirror
+  const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)v, 0);
+  const unsigned r1 = (unsigned)__builtin_amdgcn_readlane((int)v, 16);
+  const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)v, 32);
+  const unsigned r3 = (unsigned)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+template <int SLOTS>
 __global__ void __launch_bounds__(kMatchThreads)
 locality_match_kernel(const int32_t* __restrict__ bundles, int P, int J, int64_t m,
                       int32_t* __restrict__ perm, int64_t* __restrict__ send,
@@ -300,12 +334,12 @@ locality_match_kernel(const int32_t* __restrict__ bundles, int P, int J, int64_t
   __shared__ int32_t bl[kMaxPlanChunks];
   __shared__ uint16_t keepc[kMaxMatchRanks * kMaxMatchRanks];  // [bundle][home rank] chunk counts
   __shared__ int32_t placed[kMaxMatchRanks];
+  __shared__ int32_t claim[kMaxMatchRanks];  // greedy start: lowest column taking each bundle
   const int lane = threadIdx.x;
   const int PJ = P * J;
-  const long long kInf = INT64_MAX / 4;
   for (int x = lane; x < PJ; x += kMatchThreads) bl[x] = bundles[x];
   for (int x = lane; x < P * P; x += kMatchThreads) keepc[x] = 0;
-  for (int x = lane; x < P; x += kMatchThreads) placed[x] = x;
+  for (int x = lane; x < P; x += kMatchThreads) { placed[x] = x; claim[x] = 0x7fffffff; }
   __syncthreads();
   for (int bb = lane; bb < P; bb += kMatchThreads)  // lane owns row bb of the table
     for (int k = 0; k < J; ++k) {
@@ -313,62 +347,76 @@ locality_match_kernel(const int32_t* __restrict__ bundles, int P, int J, int64_t
       if (j >= 0 && j < PJ) keepc[bb * P + j / J] += 1;
     }
   __syncthreads();
+  // cost of bundle i on rank c (both 1-based)
+  auto cost = [&](int i, int c) { return J - (int)keepc[(i - 1) * P + (c - 1)]; };
 
-  long long v[kMatchSlots], minv[kMatchSlots], u[kMatchSlots];
-  int way[kMatchSlots], match[kMatchSlots];
-  bool used[kMatchSlots], tree[kMatchSlots];
+  int v[SLOTS], minv[SLOTS], u[SLOTS], way[SLOTS], match[SLOTS], cand[SLOTS];
+  bool used[SLOTS], tree[SLOTS];
+  // ---- greedy start: column reduction ----
 #pragma unroll
-  for (int k = 0; k < kMatchSlots; ++k) { v[k] = 0; u[k] = 0; match[k] = 0; way[k] = 0; }
+  for (int k = 0; k < SLOTS; ++k) {
+    const int c = lane + 1 + kWave * k;
+    v[k] = 0; u[k] = 0; match[k] = 0; way[k] = 0; cand[k] = 0;
+    if (c <= P) {
+      int best = kMatchInf;
+      for (int i = 1; i <= P; ++i) {
+        const int ci = cost(i, c);
+        if (ci < best) { best = ci; cand[k] = i; }
+      }
+      v[k] = best;
+      atomicMin(&claim[cand[k] - 1], c);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    const int c = lane + 1 + kWave * k;
+    if (c <= P && claim[cand[k] - 1] == c) match[k] = cand[k];
+  }
+
   // value of register array x for global index g (1-based), read from its lane
   auto lane_of = [](int g) { return (g - 1) % kWave; };
   auto slot_of = [](int g) { return (g - 1) / kWave; };
-  auto read_i = [&](const int (&x)[kMatchSlots], int g) {
-    const int k = slot_of(g);
+  auto read_i = [&](const int (&x)[SLOTS], int g) {
     int val = x[0];
+    if constexpr (SLOTS > 1) {
+      const int k = slot_of(g);
 #pragma unroll
-    for (int q = 1; q < kMatchSlots; ++q) val = (k == q) ? x[q] : val;
+      for (int q = 1; q < SLOTS; ++q) val = (k == q) ? x[q] : val;
+    }
     return __builtin_amdgcn_readlane(val, lane_of(g));
   };
-  auto read_l = [&](const long long (&x)[kMatchSlots], int g) {
-    const int k = slot_of(g);
-    long long val = x[0];
-#pragma unroll
-    for (int q = 1; q < kMatchSlots; ++q) val = (k == q) ? x[q] : val;
-    const int lo = __builtin_amdgcn_readlane((int)(val & 0xffffffffll), lane_of(g));
-    const int hi = __builtin_amdgcn_readlane((int)(val >> 32), lane_of(g));
-    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
-  };
 
+  // ---- the bundles left over enter one at a time ----
   for (int i = 1; i <= P; ++i) {
+    if (claim[i - 1] != 0x7fffffff) continue;  // placed by the greedy start (uniform)
 #pragma unroll
-    for (int k = 0; k < kMatchSlots; ++k) { minv[k] = kInf; used[k] = false; tree[k] = false; }
+    for (int k = 0; k < SLOTS; ++k) { minv[k] = kMatchInf; used[k] = false; tree[k] = false; }
     int j0 = 0;
     // at most P steps: every step uses up one more of the P real columns
     for (int step = 0; step <= P; ++step) {
       const int i0 = j0 == 0 ? i : read_i(match, j0);
 #pragma unroll
-      for (int k = 0; k < kMatchSlots; ++k) {
+      for (int k = 0; k < SLOTS; ++k) {
         if (j0 != 0 && lane == lane_of(j0) && k == slot_of(j0)) used[k] = true;
         if (lane == lane_of(i0) && k == slot_of(i0)) tree[k] = true;
       }
-      const long long ui0 = read_l(u, i0);
-      long long best = kInf;
-      int col = 0x7fffffff;
+      const int ui0 = read_i(u, i0);
+      unsigned key = kNoKey32;
 #pragma unroll
-      for (int k = 0; k < kMatchSlots; ++k) {
+      for (int k = 0; k < SLOTS; ++k) {
         const int c = lane + 1 + kWave * k;
         if (c > P || used[k]) continue;
-        const long long cur = (long long)(J - keepc[(i0 - 1) * P + (c - 1)]) * m - ui0 - v[k];
+        const int cur = cost(i0, c) - ui0 - v[k];
         if (cur < minv[k]) { minv[k] = cur; way[k] = j0; }
-        if (minv[k] < best) { best = minv[k]; col = c; }
+        const unsigned taken = match[k] != 0 ? (1u << kColBits) : 0u;
+        key = min(key, ((unsigned)minv[k] << (kColBits + 1)) | taken | (unsigned)c);
       }
-      const unsigned long long key =
-          col > P ? kNoKey : (((unsigned long long)best << kColBits) | (unsigned)col);
-      const unsigned long long wkey = wave_min_key(key);
-      const long long delta = (long long)(wkey >> kColBits);
-      col = wkey == kNoKey ? 0x7fffffff : (int)(wkey & ((1u << kColBits) - 1));
+      const unsigned wkey = wave_min_u32(key);
+      const int delta = (int)(wkey >> (kColBits + 1));
+      const int col = wkey == kNoKey32 ? 0x7fffffff : (int)(wkey & ((1u << kColBits) - 1));
 #pragma unroll
-      for (int k = 0; k < kMatchSlots; ++k) {
+      for (int k = 0; k < SLOTS; ++k) {
         const int c = lane + 1 + kWave * k;
         if (c <= P) {
           if (used[k]) v[k] -= delta;
@@ -384,14 +432,14 @@ locality_match_kernel(const int32_t* __restrict__ bundles, int P, int J, int64_t
       const int j1 = read_i(way, j0);
       const int row = j1 == 0 ? i : read_i(match, j1);
 #pragma unroll
-      for (int k = 0; k < kMatchSlots; ++k)
+      for (int k = 0; k < SLOTS; ++k)
         if (lane == lane_of(j0) && k == slot_of(j0)) match[k] = row;
       j0 = j1;
     }
   }
 
 #pragma unroll
-  for (int k = 0; k < kMatchSlots; ++k) {
+  for (int k = 0; k < SLOTS; ++k) {
     const int c = lane + 1 + kWave * k;
     const int b = match[k] - 1;  // the matching is perfect: every bundle is placed once
     if (c <= P && b >= 0 && b < P) placed[b] = c - 1;
@@ -423,8 +471,11 @@ locality_match_kernel(const int32_t* __restrict__ bundles, int P, int J, int64_t
 hipError_t launch_locality_match(const int32_t* rank_chunks, int32_t P, int32_t J, int64_t m,
                                  int32_t* phys_rank, int64_t* send_rows, int64_t* kept_moved,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(locality_match_kernel, dim3(1), dim3(kMatchThreads), 0, stream, rank_chunks,
-                     P, J, m, phys_rank, send_rows, kept_moved);
+  auto kern = P <= kWave       ? locality_match_kernel<1>
+              : P <= 2 * kWave ? locality_match_kernel<2>
+                               : locality_match_kernel<kMaxMatchRanks / kWave>;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kMatchThreads), 0, stream, rank_chunks, P, J, m,
+                     phys_rank, send_rows, kept_moved);
   return hipGetLastError();
 }
 

@@ -32,7 +32,8 @@ def assert_optimal_placement(bundles, m):
     assert km.tolist() == [kept, moved]
 
 
-@pytest.mark.parametrize("P,J", [(1, 1), (2, 2), (3, 5), (8, 4), (16, 8), (64, 8), (256, 16)])
+@pytest.mark.parametrize("P,J", [(1, 1), (2, 2), (3, 5), (8, 4), (16, 8), (64, 8), (65, 3),
+                                 (100, 6), (128, 8), (129, 2), (256, 16)])
 def test_random_bundles(P, J):
     g = np.random.default_rng(P * 100 + J)
     for trial in range(3):
