@@ -395,6 +395,16 @@ def main():
     # Context measured on the same box after the timed steps: a dense bf16
     # product through the vendor library and a plain 1 GiB device copy (the
     # ceilings the attention and merge rates can be read against).
+    # host side of one plan call (argument checks and two launches, enqueued
+    # without waiting), apart from its GPU time above
+    torch.cuda.synchronize()
+    n_calls = 200
+    t0 = time.perf_counter()
+    for _ in range(n_calls):
+        binding.splitkv_plan(sd, ad, w.B, w.S, w.m, w.P, w.J, out=plan_out)
+    result["plan_host_us"] = round((time.perf_counter() - t0) * 1e6 / n_calls, 1)
+    torch.cuda.synchronize()
+
     result["context"] = box_ceilings(torch, dev)
     result["merge_frac_copy"] = round(merge_gbs / result["context"]["device_copy_gbs"], 4)
     # the attention rates against the product loop's rate on random operands
