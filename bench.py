@@ -50,7 +50,7 @@ ENTRY_KERNELS = {
     "splitkv_lse_reduce": ["lse_reduce_kernel"],
     "splitkv_lse_rescale": ["lse_rescale_kernel"],
     "splitkv_delta": ["delta_rows_kernel"],
-    "splitkv_attn_bwd": ["block_range_kernel", "bwd_prep_kernel", "chunk_range_kernel",
+    "splitkv_attn_bwd": ["block_range_kernel", "bwd_prep", "chunk_range_kernel",
                          "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"],
 }
 COPY_CALIBRATION_BYTES = 1 << 30   # the --copy-calibration device copy

@@ -8,10 +8,11 @@
 // emulated ranks of one device sum into one buffer.
 //
 // bf16 path, four kernels:
-//  1. bwd_prep_kernel: Delta (from o and do, or given) and, per query vector,
-//     a record {-lse * log2 e, -Delta, lo, hi} with the row's local key
-//     interval (lse = -inf stays -inf so that P = exp2(. - inf) = 0), laid out
-//     per (kv head, 64-vector chunk) as four 64-wide arrays.
+//  1. bwd_prep_delta_kernel (Delta from o and do) or bwd_prep_kernel (Delta
+//     given): per query vector, a record {-lse * log2 e, -Delta, lo, hi} with
+//     the row's local key interval (lse = -inf stays -inf so that
+//     P = exp2(. - inf) = 0), laid out per (kv head, 64-vector chunk) as four
+//     64-wide arrays.
 //  2. chunk_range_kernel: per 64-vector query chunk (one wave), the union of its
 //     intervals and the interval that every vector of the chunk covers.
 //  3. attn_bwd_dkdv_kernel: a workgroup owns 128 local keys of one kv head (32
@@ -54,70 +55,103 @@ delta_kernel(const T* __restrict__ o, const T* __restrict__ dout, float* __restr
   delta[t] = acc;
 }
 
-// bf16 path: one record slot per (kv head g, 64-vector chunk c, t < 64); D/8
-// lanes per slot when Delta comes from o and do (16-byte loads, shuffle
-// reduction), one when it is given. The records are laid out as
-// [g][c][field][t] with fields {-lse * log2 e, -Delta, lo, hi} (the starting
-// values of the S and dP accumulators of the dK/dV kernel), so that one 1 KB
-// copy stages a chunk's records as four 64-wide arrays. Rows without live keys
-// and slots past the last vector start S at -inf (P = 0); dead slots have an
-// empty interval.
-template <int D, int L>
+// bf16 path: one record slot per (kv head g, 64-vector chunk c, t < 64), laid
+// out as [g][c][field][t] with fields {-lse * log2 e, -Delta, lo, hi} (the
+// starting values of the S and dP accumulators of the dK/dV kernel), so that
+// one 1 KB copy stages a chunk's records as four 64-wide arrays. Rows without
+// live keys and slots past the last vector start S at -inf (P = 0); dead slots
+// have an empty interval.
+//
+// Delta from o and do: D/16 lanes per (row, head) in memory order (each lane
+// two 16-byte pieces of o and of do, then a shuffle reduction), so the reads
+// sweep o and do front to back, and the item's record goes to its slot.
+// Threads past the last item fill the dead slots of every kv head's last
+// chunk (vectors n_vec .. n_qc * 64 - 1). (Walking the slots instead read o
+// and do one 1 KB piece per 8 KB row per kv head, at 40% of HBM bandwidth.)
+template <int D>
 __global__ void __launch_bounds__(256)
-bwd_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
-                const float* __restrict__ lse, float* __restrict__ delta,
-                const int2* __restrict__ block_range, float* __restrict__ meta, int64_t n_vec,
-                int64_t n_qc, int G, int gshift, int hq, int hkv, int B) {
-  // L lanes per slot: D / 8 (8 or 16, a divisor of 64) when Delta is taken
-  // from o and do, 1 when it is given
+bwd_prep_delta_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+                      const float* __restrict__ lse, float* __restrict__ delta,
+                      const int2* __restrict__ block_range, float* __restrict__ meta,
+                      int64_t n_items, int64_t n_vec, int64_t n_qc, int G, int hq, int hkv,
+                      int B) {
+  constexpr int L = D / 16;  // lanes per item, two 16-byte pieces of o and of do each
   const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t slot = gt / L;
+  const int64_t item = gt / L;
   const int part = (int)(gt % L);
-  const int64_t n_slots = (int64_t)hkv * n_qc * kQC;
-  const bool ok = slot < n_slots;
-  int64_t item = -1;
-  uint32_t rw = 0;
-  if (ok) {
-    const int64_t gc = slot / kQC;
-    const int g = (int)(gc / n_qc);
-    const uint32_t vec = (uint32_t)((gc % n_qc) * kQC + slot % kQC);
-    if (vec < n_vec) {
-      rw = gshift >= 0 ? vec >> gshift : vec / (uint32_t)G;
-      item = (int64_t)rw * hq + g * G + (vec - rw * G);
-    }
-  }
+  const bool ok = item < n_items;
   float acc = 0.f;
-  if (item >= 0 && o != nullptr) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + item * D + part * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + item * D + part * 8);
+  if (ok) {
+    const u32x4* op = reinterpret_cast<const u32x4*>(o + item * D) + part;
+    const u32x4* dp = reinterpret_cast<const u32x4*>(dout + item * D) + part;
+    const u32x4 a0 = __builtin_nontemporal_load(op), a1 = __builtin_nontemporal_load(op + L);
+    const u32x4 b0 = __builtin_nontemporal_load(dp), b1 = __builtin_nontemporal_load(dp + L);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
-      acc = fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(b[w] & 0xffff0000u), acc);
+      acc = fmaf(__uint_as_float(a0[w] << 16), __uint_as_float(b0[w] << 16), acc);
+      acc = fmaf(__uint_as_float(a0[w] & 0xffff0000u), __uint_as_float(b0[w] & 0xffff0000u), acc);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(__uint_as_float(a1[w] << 16), __uint_as_float(b1[w] << 16), acc);
+      acc = fmaf(__uint_as_float(a1[w] & 0xffff0000u), __uint_as_float(b1[w] & 0xffff0000u), acc);
     }
   }
 #pragma unroll
   for (int off = L / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (!ok || part != 0) return;
-  float* rec = meta + (slot / kQC) * (4 * kQC) + slot % kQC;
-  if (item < 0) {
+  if (part != 0) return;
+  if (ok) {
+    const int64_t row = item / hq;
+    const int h = (int)(item - row * hq), g = h / G;
+    const int64_t vec = row * G + (h - g * G);
+    float* rec = meta + ((int64_t)g * n_qc + vec / kQC) * (4 * kQC) + vec % kQC;
+    delta[item] = acc;
+    const float l = lse[item];
+    const int2 r = block_range[row / B];
+    rec[0] = l == -INFINITY ? -INFINITY : -l * kLog2e;
+    rec[kQC] = -acc;
+    rec[2 * kQC] = __int_as_float(r.x);
+    rec[3 * kQC] = __int_as_float(r.y);
+    return;
+  }
+  const int64_t pad = n_qc * kQC - n_vec;  // dead slots per kv head
+  const int64_t d = item - n_items;
+  if (d >= pad * hkv) return;
+  const int g = (int)(d / pad);
+  const int64_t vec = n_vec + d % pad;
+  float* rec = meta + ((int64_t)g * n_qc + vec / kQC) * (4 * kQC) + vec % kQC;
+  rec[0] = -INFINITY;
+  rec[kQC] = 0.f;
+  rec[2 * kQC] = __int_as_float(0);
+  rec[3 * kQC] = __int_as_float(0);
+}
+
+// Delta given: one lane per slot, in slot order (the record writes coalesce).
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_prep_kernel(const float* __restrict__ lse, const float* __restrict__ delta,
+                const int2* __restrict__ block_range, float* __restrict__ meta, int64_t n_vec,
+                int64_t n_qc, int G, int gshift, int hq, int hkv, int B) {
+  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n_slots = (int64_t)hkv * n_qc * kQC;
+  if (slot >= n_slots) return;
+  const int64_t gc = slot / kQC;
+  const int g = (int)(gc / n_qc);
+  const uint32_t vec = (uint32_t)((gc % n_qc) * kQC + slot % kQC);
+  float* rec = meta + gc * (4 * kQC) + slot % kQC;
+  if (vec >= n_vec) {
     rec[0] = -INFINITY;
     rec[kQC] = 0.f;
     rec[2 * kQC] = __int_as_float(0);
     rec[3 * kQC] = __int_as_float(0);
     return;
   }
-  float dl;
-  if (o != nullptr) {
-    dl = acc;
-    delta[item] = dl;
-  } else {
-    dl = delta[item];
-  }
+  const uint32_t rw = gshift >= 0 ? vec >> gshift : vec / (uint32_t)G;
+  const int64_t item = (int64_t)rw * hq + g * G + (vec - rw * G);
   const float l = lse[item];
   const int2 r = block_range[rw / B];
   rec[0] = l == -INFINITY ? -INFINITY : -l * kLog2e;
-  rec[kQC] = -dl;
+  rec[kQC] = -delta[item];
   rec[2 * kQC] = __int_as_float(r.x);
   rec[3 * kQC] = __int_as_float(r.y);
 }
@@ -824,17 +858,18 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
     int4* chunk_range = static_cast<int4*>(chunk_ws);
     if (n_rh > 0) {
       const int64_t slots = (int64_t)hd.hkv * n_qc * kQC;
-      if (o != nullptr)
-        hipLaunchKernelGGL((bwd_prep_kernel<D, D / 8>),
-                           dim3((unsigned)((slots * (D / 8) + 255) / 256)), dim3(256), 0, stream,
-                           static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), lse,
-                           delta, block_range, meta, n_vec, n_qc, G, gshift, hd.hq, hd.hkv,
-                           an.block_size);
-      else  // Delta given: one lane per slot
-        hipLaunchKernelGGL((bwd_prep_kernel<D, 1>), dim3((unsigned)((slots + 255) / 256)),
-                           dim3(256), 0, stream, static_cast<const bf16_t*>(nullptr),
-                           static_cast<const bf16_t*>(dout), lse, delta, block_range, meta, n_vec,
-                           n_qc, G, gshift, hd.hq, hd.hkv, an.block_size);
+      if (o != nullptr) {
+        // every (row, head), then the dead slots of each kv head's last chunk
+        const int64_t threads = (n_rh + (n_qc * kQC - n_vec) * hd.hkv) * (D / 16);
+        hipLaunchKernelGGL((bwd_prep_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
+                           dim3(256), 0, stream, static_cast<const bf16_t*>(o),
+                           static_cast<const bf16_t*>(dout), lse, delta, block_range, meta,
+                           n_rh, n_vec, n_qc, G, hd.hq, hd.hkv, an.block_size);
+      } else {  // Delta given: one lane per slot
+        hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((slots + 255) / 256)),
+                           dim3(256), 0, stream, lse, delta, block_range, meta, n_vec, n_qc, G,
+                           gshift, hd.hq, hd.hkv, an.block_size);
+      }
       if ((err = hipGetLastError()) != hipSuccess) return err;
       const int64_t per_wg = kRangeThreads / kWave;  // chunks per workgroup
       hipLaunchKernelGGL(chunk_range_kernel, dim3((unsigned)((n_qc + per_wg - 1) / per_wg)),
