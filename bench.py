@@ -51,7 +51,8 @@ ENTRY_KERNELS = {
     "splitkv_lse_rescale": ["lse_rescale_kernel"],
     "splitkv_delta": ["delta_rows_kernel"],
     "splitkv_attn_bwd": ["block_range_kernel", "bwd_prep", "chunk_range_kernel",
-                         "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"],
+                         "ds_offsets_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel",
+                         "attn_bwd_dq_ds_kernel"],
 }
 COPY_CALIBRATION_BYTES = 1 << 30   # the --copy-calibration device copy
 
@@ -157,6 +158,9 @@ def parse():
     ap.add_argument("--own-blocks", action="store_true",
                     help="whole mask: also the own-block partial of every block (its B "
                          "block keys), merged with the P context partials and in the backward")
+    ap.add_argument("--recompute-dq", action="store_true",
+                    help="take dq by recomputing S and dP (the minimum backward workspace) "
+                         "instead of from the dS the dK/dV pass stores")
     ap.add_argument("--merge-form", choices=("merged", "per-rank"), default="merged",
                     help="merged: one LSE-merge kernel over the P partials and Delta from the "
                          "merged output; per-rank: the form each rank applies when the partials "
@@ -246,8 +250,18 @@ def main():
     dvs = [torch.empty_like(v) for _, _, v in locs]
     an = binding.make_anchors(sd, ad, w.B)
     hd = binding.make_heads(hq, w.hkv, d, tdt)
+    # the backward's workspace holds every rank's dS unless dq is recomputed
+    # (one rank at a time: the largest rank's room serves all)
+    ds_bytes = 0
+    if not args.recompute_dq:
+        calls = [(sd, ad, cs, w.m) for cs, _, _ in locs]
+        if args.own_blocks:
+            calls.append((bs, ba, bcs, blen))
+        ds_bytes = max(binding.splitkv_attn_bwd_ds_bytes(s_, a_, w.B, cs_, m_, hq, w.hkv, d, tdt)
+                       for s_, a_, cs_, m_ in calls)
     ws_bytes = max(binding.splitkv_workspace_bytes(binding.SPLITKV_OP_FWD, an, hd, None),
-                   binding.splitkv_workspace_bytes(binding.SPLITKV_OP_BWD, an, hd, None))
+                   binding.splitkv_workspace_bytes(binding.SPLITKV_OP_BWD, an, hd, None) +
+                   ds_bytes)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
@@ -362,6 +376,8 @@ def main():
                      "plan + fwd(all ranks) + merge + bwd(all ranks)"),
             "live_pairs_per_head": pairs,
             "merge_form": args.merge_form,
+            "dq": "recomputed (S, dP again)" if args.recompute_dq else
+                  "from the dS the dK/dV pass stored (%.2f GB of workspace)" % (ds_bytes / 1e9),
         },
         "fwd_tflops": round(fwd_tflops, 2),
         "bwd_tflops": round(bwd_tflops, 2),
@@ -377,7 +393,8 @@ def main():
         "rank_load_max_over_mean_with_D": round(float((load.max() + D) / (load.mean() + D)), 5),
         "roofline": {
             "bound": "mfma",
-            "kernel": ("splitkv_attn_bwd (attn_bwd_dkdv_kernel + attn_bwd_dq_kernel)"
+            "kernel": (("splitkv_attn_bwd (attn_bwd_dkdv_kernel + %s)" %
+                        ("attn_bwd_dq_kernel" if args.recompute_dq else "attn_bwd_dq_ds_kernel"))
                        if dominant == "bwd" else "splitkv_attn_fwd (attn_fwd_bf16_kernel)"),
             "per_launch": "one emulated rank's call; achieved = the phase's mask-live FLOPs "
                           "over its measured time (= per-launch FLOPs / mean launch time)",
@@ -408,12 +425,13 @@ def main():
     result["context"] = box_ceilings(torch, dev)
     result["merge_frac_copy"] = round(merge_gbs / result["context"]["device_copy_gbs"], 4)
     # the attention rates against the product loop's rate on random operands
-    # (the backward's executed products are 14 d-contractions per pair for the
-    # 10 credited)
+    # (the backward executes the 10 credited d-contractions per pair, or 14
+    # when dq recomputes S and dP)
     ceil = result["context"]["mfma_loop_random_bf16_tflops"]
+    executed = 1.4 if args.recompute_dq else 1.0
     result["frac_of_mfma_loop"] = {"fwd": round(fwd_tflops / ceil, 4),
                                    "bwd_credited": round(bwd_tflops / ceil, 4),
-                                   "bwd_executed": round(bwd_tflops * 1.4 / ceil, 4)}
+                                   "bwd_executed": round(bwd_tflops * executed / ceil, 4)}
 
     if args.copy_calibration:
         x = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB

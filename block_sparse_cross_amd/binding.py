@@ -35,8 +35,8 @@ EXPORTED = ("splitkv_workspace_bytes", "splitkv_validate_anchors", "splitkv_plan
             "splitkv_locality_match", "splitkv_plan_baseline",
             "splitkv_attn_fwd", "splitkv_lse_merge", "splitkv_lse_reduce", "splitkv_lse_rescale",
             "splitkv_delta", "splitkv_gemm", "splitkv_gemm_pair", "splitkv_cast_bf16",
-            "splitkv_attn_bwd", "splitkv_attn_bwd_noalloc", "splitkv_own_block_local",
-            "splitkv_status_str")
+            "splitkv_attn_bwd", "splitkv_attn_bwd_ds_bytes", "splitkv_attn_bwd_noalloc",
+            "splitkv_own_block_local", "splitkv_status_str")
 
 SPLITKV_GEMM_NT, SPLITKV_GEMM_NN, SPLITKV_GEMM_TN = 0, 1, 2
 
@@ -116,6 +116,8 @@ def lib() -> ctypes.CDLL:
         L.splitkv_cast_bf16.restype = ctypes.c_int
         L.splitkv_attn_bwd.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.splitkv_attn_bwd.restype = ctypes.c_int
+        L.splitkv_attn_bwd_ds_bytes.argtypes = [A, H, Lc, vp, sz, vp, vp]
+        L.splitkv_attn_bwd_ds_bytes.restype = ctypes.c_int
         L.splitkv_attn_bwd_noalloc.argtypes = [A, H, Lc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                vp]
         L.splitkv_attn_bwd_noalloc.restype = ctypes.c_int
@@ -535,7 +537,9 @@ def splitkv_attn_bwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v
     """Backward of the local partial with the global lse (and Delta = <do, o>).
 
     dq (fp32 [Q, hq, d]) is accumulated in place. Pass o=None and delta=... to
-    supply Delta directly. Returns (dk, dv, delta)."""
+    supply Delta directly. A workspace past the minimum (bwd_workspace) holds
+    dS from the dK/dV pass, so that dq need not recompute it. Returns (dk, dv,
+    delta)."""
     an, hd, loc, delta, dk, dv = _bwd_args(s, a, block_size, chunk_start, chunk_len, q, k, v, o,
                                            dout, lse, dq, scale, delta, out)
     nbytes = splitkv_workspace_bytes(SPLITKV_OP_BWD, an, hd, loc)
@@ -545,6 +549,36 @@ def splitkv_attn_bwd(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v
         _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
         ws_ptr, ws_bytes, _stream(stream)))
     return dk, dv, delta
+
+
+def splitkv_attn_bwd_ds_bytes(s, a, block_size: int, chunk_start, chunk_len: int, hq: int,
+                              hkv: int, d: int, dtype: torch.dtype,
+                              stream: Optional[torch.cuda.Stream] = None) -> int:
+    """Bytes of stored dS (past the minimum backward workspace) that cover every
+    query row. Runs on the device and waits for the result."""
+    an, hd, loc = make_anchors(s, a, block_size), make_heads(hq, hkv, d, dtype), \
+        make_local(chunk_start, chunk_len)
+    nbytes = splitkv_workspace_bytes(SPLITKV_OP_BWD, an, hd, loc)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=s.device)
+    need = torch.zeros(1, dtype=torch.int64, device=s.device)
+    _check("splitkv_attn_bwd_ds_bytes", lib().splitkv_attn_bwd_ds_bytes(
+        ctypes.byref(an), ctypes.byref(hd), ctypes.byref(loc), _ptr(ws), nbytes, _ptr(need),
+        _stream(stream)))
+    (stream if stream is not None else torch.cuda.current_stream()).synchronize()
+    return int(need.item())
+
+
+def bwd_workspace(s, a, block_size: int, chunk_start, chunk_len: int, hq: int, hkv: int, d: int,
+                  dtype: torch.dtype, ds_bytes: Optional[int] = None) -> torch.Tensor:
+    """A workspace for splitkv_attn_bwd with room for ds_bytes of stored dS
+    (default: enough for every query row, from splitkv_attn_bwd_ds_bytes)."""
+    if ds_bytes is None:
+        ds_bytes = splitkv_attn_bwd_ds_bytes(s, a, block_size, chunk_start, chunk_len, hq, hkv, d,
+                                             dtype)
+    an, hd, loc = make_anchors(s, a, block_size), make_heads(hq, hkv, d, dtype), \
+        make_local(chunk_start, chunk_len)
+    nbytes = splitkv_workspace_bytes(SPLITKV_OP_BWD, an, hd, loc)
+    return torch.empty(max(nbytes + int(ds_bytes), 1), dtype=torch.uint8, device=s.device)
 
 
 def splitkv_attn_bwd_noalloc(s, a, block_size: int, chunk_start, chunk_len: int, q, k, v, o,

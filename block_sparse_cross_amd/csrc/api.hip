@@ -27,7 +27,8 @@ BwdWorkspace bwd_workspace_layout(int64_t n_blocks, int32_t block_size, int32_t 
   const int64_t n_qc = (n_vec + kBwdChunk - 1) / kBwdChunk;
   // 4 fp32 fields per vector, per (kv head, query chunk)
   w.chunk_range = w.meta + align256((size_t)hkv * n_qc * 4 * kBwdChunk * sizeof(float));
-  w.total = w.chunk_range + align256((size_t)n_qc * sizeof(int4));
+  w.ds_off = w.chunk_range + align256((size_t)n_qc * sizeof(int4));
+  w.total = w.ds_off + align256((size_t)n_qc * sizeof(int));
   return w;
 }
 
@@ -98,19 +99,21 @@ int check_bwd_args(const splitkv_anchors* an, const splitkv_heads* hd, const spl
   return SPLITKV_OK;
 }
 
-// The backward's kernels on a workspace laid out as `ws` at `base` (device).
+// The backward's kernels on a workspace laid out as `ws` at `base` (device),
+// ds_bytes past ws.total of it free for stored dS.
 int run_bwd(const splitkv_anchors* an, const splitkv_heads* hd, const splitkv_local* loc,
             const void* q, const void* k, const void* v, const void* o, const void* dout,
             const float* lse, float* delta, float* dq, void* dk, void* dv, char* base,
-            const BwdWorkspace& ws, hipStream_t s) {
+            const BwdWorkspace& ws, size_t ds_bytes, hipStream_t s) {
   const int64_t n_keys = (int64_t)loc->n_chunks * loc->chunk_len;
   int2* block_range = reinterpret_cast<int2*>(base + ws.block_range);
   hipError_t e = launch_block_ranges(an->s, an->a, an->n_blocks, loc->chunk_start, loc->n_chunks,
                                      loc->chunk_len, block_range, s);
   if (e != hipSuccess) return SPLITKV_ERR_HIP;
   return hip_status(launch_bwd(*an, *hd, n_keys, block_range, base + ws.meta,
-                               base + ws.chunk_range, q, k, v, o, dout, lse, delta, dq, dk, dv,
-                               s));
+                               base + ws.chunk_range, reinterpret_cast<int*>(base + ws.ds_off),
+                               ds_bytes > 0 ? base + ws.total : nullptr, ds_bytes, q, k, v, o,
+                               dout, lse, delta, dq, dk, dv, s));
 }
 
 // Fixed device scratch of splitkv_attn_bwd_noalloc, for callers that cannot
@@ -389,8 +392,31 @@ int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
   const BwdWorkspace ws = bwd_workspace_layout(an->n_blocks, an->block_size, hd->hq, hd->hkv);
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total))
     return SPLITKV_ERR_WORKSPACE;
+  if (workspace_bytes > ws.total && !a16(workspace)) return SPLITKV_ERR_INVALID_ARG;
   return run_bwd(an, hd, loc, q, k, v, o, dout, lse, delta, dq, dk, dv,
-                 static_cast<char*>(workspace), ws, static_cast<hipStream_t>(stream));
+                 static_cast<char*>(workspace), ws,
+                 workspace == nullptr ? 0 : workspace_bytes - ws.total,
+                 static_cast<hipStream_t>(stream));
+}
+
+int splitkv_attn_bwd_ds_bytes(const splitkv_anchors* an, const splitkv_heads* hd,
+                              const splitkv_local* loc, void* workspace, size_t workspace_bytes,
+                              int64_t* ds_bytes, void* stream) {
+  int st = check_attn_common(an, hd, loc);
+  if (st != SPLITKV_OK) return st;
+  if (ds_bytes == nullptr || (reinterpret_cast<uintptr_t>(ds_bytes) & 7) != 0)
+    return SPLITKV_ERR_INVALID_ARG;
+  const BwdWorkspace ws = bwd_workspace_layout(an->n_blocks, an->block_size, hd->hq, hd->hkv);
+  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total))
+    return SPLITKV_ERR_WORKSPACE;
+  char* base = static_cast<char*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int2* block_range = reinterpret_cast<int2*>(base + ws.block_range);
+  hipError_t e = launch_block_ranges(an->s, an->a, an->n_blocks, loc->chunk_start, loc->n_chunks,
+                                     loc->chunk_len, block_range, s);
+  if (e != hipSuccess) return SPLITKV_ERR_HIP;
+  return hip_status(launch_bwd_ds_need(*an, *hd, block_range, base + ws.chunk_range,
+                                       reinterpret_cast<int*>(base + ws.ds_off), ds_bytes, s));
 }
 
 int splitkv_attn_bwd_noalloc(const splitkv_anchors* an, const splitkv_heads* hd,
@@ -403,7 +429,8 @@ int splitkv_attn_bwd_noalloc(const splitkv_anchors* an, const splitkv_heads* hd,
   if (ws.total > SPLITKV_NOALLOC_SCRATCH_BYTES) return SPLITKV_ERR_WORKSPACE;
   char* base = nullptr;
   if ((st = device_scratch(&base)) != SPLITKV_OK) return st;
-  return run_bwd(an, hd, loc, q, k, v, o, dout, lse, delta, dq, dk, dv, base, ws,
+  // the scratch past the fixed part stays unused: every dQ is recomputed
+  return run_bwd(an, hd, loc, q, k, v, o, dout, lse, delta, dq, dk, dv, base, ws, 0,
                  static_cast<hipStream_t>(stream));
 }
 

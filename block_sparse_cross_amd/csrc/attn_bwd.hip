@@ -7,14 +7,16 @@
 // dk and dv stay local to the rank; dq is accumulated (+=) so that the P
 // emulated ranks of one device sum into one buffer.
 //
-// bf16 path, four kernels:
+// bf16 path:
 //  1. bwd_prep_delta_kernel (Delta from o and do) or bwd_prep_kernel (Delta
 //     given): per query vector, a record {-lse * log2 e, -Delta, lo, hi} with
 //     the row's local key interval (lse = -inf stays -inf so that
 //     P = exp2(. - inf) = 0), laid out per (kv head, 64-vector chunk) as four
 //     64-wide arrays.
 //  2. chunk_range_kernel: per 64-vector query chunk (one wave), the union of its
-//     intervals and the interval that every vector of the chunk covers.
+//     intervals and the interval that every vector of the chunk covers;
+//     ds_offsets_kernel: where each chunk's dS goes in the workspace (if it
+//     fits; see the stored-dS layout below).
 //  3. attn_bwd_dkdv_kernel: a workgroup owns 128 local keys of one kv head (32
 //     per wave; K and V fragments and the dK, dV accumulators in registers)
 //     and walks the query chunks whose union reaches those keys. Q, dO and the
@@ -24,10 +26,14 @@
 //     S = Q K^T and dP = dO V^T so that a lane owns one key and 16 vectors;
 //     dV^T += dO^T P and dK^T += Q^T dS, the Q^T and dO^T fragments read by
 //     the transposing LDS read. Chunks whose vectors all cover a wave's 32
-//     keys skip the per-key mask.
-//  4. attn_bwd_dq_kernel: query-outer like the forward; recomputes S and dP
-//     per key tile and accumulates dQ^T += K^T dS^T in registers, so dq needs
-//     no atomics and is deterministic.
+//     keys skip the per-key mask. With room in the workspace it also stores
+//     the packed dS (bf16) as it feeds dK^T.
+//  4. dq, either way deterministic and without atomics:
+//     attn_bwd_dq_ds_kernel: from the stored dS, dQ^T += K^T dS^T (one
+//       d-contraction per pair, bound by streaming the dS from HBM);
+//     attn_bwd_dq_kernel: query-outer like the forward, recomputing S and dP
+//       per key tile (three d-contractions per pair), for the vector groups
+//       whose dS was not stored.
 #include <type_traits>
 
 #include "common.hpp"
@@ -41,6 +47,33 @@ constexpr int kBwdThreads = 256;  // 4 waves
 constexpr int kBwdKeys = 128;     // keys per workgroup, 32 per wave
 constexpr int kQC = kBwdChunk;    // query vectors per chunk (dK/dV kernel)
 constexpr int kListCap = 1024;    // chunk indices buffered per scan
+constexpr int kDqThreads = 512;  // dQ kernels: 8 waves, two per SIMD
+constexpr int kDqWaves = kDqThreads / 64;
+constexpr int kDqVecPerWG = 32 * kDqWaves;
+constexpr int kDqKT = 64;
+
+// Stored dS. For kv head g and query chunk c (64 vectors) whose key union is
+// [ulo, uhi), each 32-key group kg = ulo / 32 .. ceil(uhi / 32) - 1 gets one
+// 4 KB tile: two 2 KB halves (vectors 0-31, 32-63 of the chunk), each 32 key
+// rows of 64 bytes. A row holds the half's 32 vectors as four 16-byte slots,
+// slot 2 h2 + h = vectors 16 h2 + 4 h + (0..3) and 16 h2 + 8 + 4 h + (0..3):
+// exactly the 8 values one lane of the dK/dV kernel packs for a 16-vector step
+// (one 16-byte store), which the dQ kernel reads back transposed (8 keys of
+// one vector) with ds_read_b64_tr_b16. Tile (g, c, kg) is number
+// g cap + ds_off[c] + kg of the dS area (cap tiles per kv head); ds_off[c] is
+// the exclusive prefix sum of the chunks' group counts minus ulo / 32, or
+// kDsNone when the chunk's dQ-from-dS workgroup (8 chunks) does not fit and
+// recomputes S and dP instead.
+constexpr int kDsKeys = 32;
+constexpr int kDsTileBytes = kQC * kDsKeys * 2;
+constexpr int kDsVecPerWG = 512;                  // vectors per workgroup of the dQ-from-dS kernel
+constexpr int kDsChunksPerWG = kDsVecPerWG / kQC;  // stored or not together
+constexpr int kDsNone = -0x7fffffff - 1;
+// Byte offset, in a half tile's 64-byte key row, of the 4 vectors u .. u + 3
+// (u a multiple of 4 below 32).
+__device__ __forceinline__ int ds_word_off(int u) {
+  return 16 * (2 * (u >> 4) + ((u >> 2) & 1)) + 8 * ((u >> 3) & 1);
+}
 
 // Delta[r, h] = <do[r, h], o[r, h]>, one thread per (row, head). fp32 path.
 template <int D, typename T>
@@ -179,12 +212,57 @@ chunk_range_kernel(const int2* __restrict__ block_range, int64_t n_vec, int G, i
   if (lane == 0) out[c] = uhi < 0 ? make_int4(0, 0, 0, 0) : make_int4(ulo, uhi, clo, chi);
 }
 
+// ds_off (see kDsNone) for every chunk: one workgroup scans the group counts
+// in pieces of 1024 chunks with a running carry. A dQ-from-dS workgroup's 8 chunks
+// are stored when the prefix sum at their end fits in cap tiles per kv head,
+// so the stored workgroups are a prefix in vector order. need (if not null)
+// receives the bytes that store every chunk: hkv tiles_total kDsTileBytes.
+constexpr int kDsScanThreads = 1024;
+__global__ void __launch_bounds__(kDsScanThreads)
+ds_offsets_kernel(const int4* __restrict__ chunk_range, int64_t n_qc, int64_t cap, int hkv,
+                  int* __restrict__ ds_off, int64_t* __restrict__ need) {
+  static_assert(kWave % kDsChunksPerWG == 0, "a dQ workgroup's chunks lie in one wave");
+  __shared__ int64_t wsum[kDsScanThreads / kWave];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < n_qc; base += kDsScanThreads) {
+    const int64_t c = base + tid;
+    int4 cr = make_int4(0, 0, 0, 0);
+    if (c < n_qc) cr = chunk_range[c];
+    const int64_t n = cr.x < cr.y ? ((cr.y + kDsKeys - 1) / kDsKeys) - cr.x / kDsKeys : 0;
+    int64_t incl = n;  // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int64_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int64_t before = carry, total = 0;
+#pragma unroll
+    for (int w = 0; w < kDsScanThreads / kWave; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    incl += before;
+    // prefix sum at the end of this chunk's dQ workgroup (chunks past n_qc
+    // count zero, so the last lane of the group holds it)
+    const int64_t end = __shfl(incl, lane | (kDsChunksPerWG - 1));
+    if (c < n_qc)
+      ds_off[c] = end <= cap ? (int)(incl - n - cr.x / kDsKeys) : kDsNone;
+    carry += total;
+    __syncthreads();  // wsum is rewritten by the next piece
+  }
+  if (need != nullptr && tid == 0) *need = carry * hkv * kDsTileBytes;
+}
+
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads, 1)
 attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                      const float* __restrict__ meta, bf16_t* __restrict__ dk,
                      bf16_t* __restrict__ dv, const int4* __restrict__ chunk_range,
+                     bf16_t* __restrict__ ds, const int* __restrict__ ds_off, int64_t ds_cap,
                      int64_t n_vec, int64_t n_qc, int G, int gshift, int hq, int hkv,
                      int n_keys, float scale, float scale_log2) {
   constexpr int NS = D / 8;
@@ -205,6 +283,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ __attribute__((aligned(16))) float Ms1[4 * kQC];
   __shared__ int list[kListCap];
   __shared__ int4 lrange[kListCap];
+  __shared__ int ldsoff[kListCap];
   __shared__ int wave_cnt[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
@@ -243,7 +322,9 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int r = 0; r < 16; ++r) { dvt[dt][r] = 0.f; dkt[dt][r] = 0.f; }
 
   // Stage chunk c (kQC vectors): Q, dO rows and the records by asynchronous
-  // copies. Vectors past the end reuse the last vector's rows (their records
+  // copies (inline assembly the compiler does not track: the chunk step's own
+  // waits are the only ones, and may leave the last chunk's dS stores in
+  // flight). Vectors past the end reuse the last vector's rows (their records
   // are dead, so they add exact zeros).
   //
   // Fast path (G a power of two dividing kQC, chunk inside the buffer): a
@@ -273,11 +354,11 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       for (int pp = 0; pp < QPASSES; ++pp) {
         const int r0 = RPP * pp;
         const uint32_t step = (uint32_t)((((int64_t)(r0 >> gshift)) * hq + (r0 & (G - 1))) * D * 2);
-        async_copy16_buf(qr, lane_off, step, Qd + pp * kBwdThreads * 8 + lds_wave);
-        async_copy16_buf(dr, lane_off, step, Dd + pp * kBwdThreads * 8 + lds_wave);
+        async_copy16_buf_asm(qr, lane_off, step, Qd + pp * kBwdThreads * 8 + lds_wave);
+        async_copy16_buf_asm(dr, lane_off, step, Dd + pp * kBwdThreads * 8 + lds_wave);
       }
       if (wave == NW - 1 && lane < kQC)
-        async_copy16(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
+        async_copy16_asm(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
       return;
     }
 #pragma unroll
@@ -290,10 +371,10 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const uint32_t rw = gshift >= 0 ? vec >> gshift : vec / (uint32_t)G;
       const int64_t idx = (int64_t)rw * hq + g * G + (vec - rw * G);
       const bf16_t* src = (tsel ? dout : q) + idx * D + (phys ^ swz_both<NS>(row)) * 8;
-      async_copy16(src, (tsel ? Dd : Qd) + (uu - lane) * 8);
+      async_copy16_asm(src, (tsel ? Dd : Qd) + (uu - lane) * 8);
     }
     if (wave == NW - 1 && lane < kQC)
-      async_copy16(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
+      async_copy16_asm(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
   };
 
   // Element offsets of this lane's transposing reads of Q and dO (rows t and
@@ -323,6 +404,12 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   int rec_off = 4 * half;
   asm volatile("" : "+v"(rec_off));
 
+  // Byte offset of this lane's dS slot in a stored tile: its key's row, slot
+  // `half` (the vector half and h2 add 2048 hv + 32 h2 as immediates).
+  int ds_lane = (lane & 31) * (kDsKeys * 2) + 16 * half;
+  asm volatile("" : "+v"(ds_lane));
+  bool stored_last = false;  // the last computed chunk stored its dS
+
   // S = Q K^T and dP = dO V^T (lane = key, 16 vectors per lane), P, dS,
   // dV^T += dO^T P, dK^T += Q^T dS, for the chunk's 32-vector halves. The
   // products of all halves are issued before the elementwise work, so one
@@ -331,7 +418,8 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // MASKED: some vector's interval cuts this wave's 32 keys (per-key test);
   // otherwise every vector of the chunk covers them all. The two variants are
   // separate code so that the common unmasked one has no branches inside.
-  auto compute_chunk = [&](auto masked, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
+  auto compute_chunk = [&](auto masked, const bf16_t* Qb, const bf16_t* Db, const float* Mb,
+                           int dso) {
     constexpr bool MASKED = decltype(masked)::value;
     static_assert(NH == 2, "chunk = two 32-vector halves");
     f32x16 sacc[NH], pacc[NH];
@@ -340,6 +428,21 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     u32x4 opa[3], opb[3];
     int4 mlo[2], mhi[2];     // key intervals of 4 vectors (masked chunks only)
     u32x4 pu, su;            // P and dS of the current 16-vector step, bf16
+    // this wave's stored dS tile of the chunk (a scalar base; the lane offset
+    // and the step's immediate are added by the store)
+    const bool st = dso != kDsNone;
+    stored_last = st;  // this chunk issues 4 stores
+    const int64_t tile = (int64_t)g * ds_cap + (st ? dso : 0) + (kw0 / kDsKeys);
+    typedef __attribute__((address_space(1))) char gchar;
+    gchar* const dst = (gchar*)uniform_ptr(ds + tile * (kDsTileBytes / 2));
+    // dS of the current 16-vector step: one 16-byte store (a plain one: the
+    // non-temporal form was 5% slower here)
+    auto store_ds = [&](int hv, int h2) {
+      if (!st) return;
+      typedef __attribute__((address_space(1))) u32x4 gu32x4;
+      *reinterpret_cast<gu32x4*>(dst + (uint32_t)ds_lane + hv * (kDsTileBytes / 2) + 32 * h2) =
+          su;
+    };
 
     auto load_sd = [&](int hv, int ks, int b) {
       opa[b] = *reinterpret_cast<const u32x4*>(&Qb[hv * 32 * D + row_off[ks]]);
@@ -449,7 +552,10 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         pacc[ph] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opb[b]), vf[i], pacc[ph], 0, 0, 0);
       } else {
         const int hv = ph - 2, h2 = i / DT, dt = i % DT;
-        if (dt == 0) pack(hv, h2);
+        if (dt == 0) {
+          pack(hv, h2);
+          store_ds(hv, h2);
+        }
         dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opa[b]), as_bf16x8(pu), dvt[dt], 0, 0, 0);
         dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opb[b]), as_bf16x8(su), dkt[dt], 0, 0, 0);
       }
@@ -458,13 +564,14 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
   };
 
-  auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float* Mb) {
+  auto compute_phase = [&](const int4 cr, const bf16_t* Qb, const bf16_t* Db, const float* Mb,
+                           int dso) {
     const bool active = cr.x < kw0 + 32 && cr.y > kw0;
     if (!active) return;
     if (cr.z <= kw0 && cr.w >= kw0 + 32)
-      compute_chunk(std::false_type{}, Qb, Db, Mb);
+      compute_chunk(std::false_type{}, Qb, Db, Mb, dso);
     else
-      compute_chunk(std::true_type{}, Qb, Db, Mb);
+      compute_chunk(std::true_type{}, Qb, Db, Mb, dso);
   };
 
   for (int64_t scan = 0; scan < n_qc;) {
@@ -474,9 +581,11 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const int64_t c = scan + tid;
       int4 cr = make_int4(0, 0, 0, 0);
       bool live = false;
+      int dso = kDsNone;
       if (c < n_qc) {
         cr = chunk_range[c];
         live = cr.x < cr.y && cr.x < kend && cr.y > k0;
+        dso = ds_off[c];
       }
       const unsigned long long bal = __ballot(live);
       if (lane == 0) wave_cnt[wave] = __popcll(bal);
@@ -488,6 +597,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         const int slot = off + __popcll(bal & ((1ull << lane) - 1ull));
         list[slot] = (int)c;
         lrange[slot] = cr;
+        ldsoff[slot] = dso;
       }
       n += total;
       scan += kBwdThreads;
@@ -501,14 +611,22 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     auto at = [](int it) { return it; };
     auto step = [&](int it, const bf16_t* Qb, const bf16_t* Db, const float* Mb, bf16_t* Qn,
                     bf16_t* Dn, float* Mn) {
-      wait_async();
-      __syncthreads();
+      // the copies of chunk it; the 4 dS stores of the last chunk (issued
+      // after them, counted by vmcnt too) may stay in flight
+      if (stored_last)
+        wait_vmcnt<4>();
+      else
+        wait_async();
+      stored_last = false;
+      // a bare barrier (__syncthreads' fence would wait for the stores)
+      asm volatile("s_barrier" ::: "memory");
       if (it + 1 < n) issue_chunk(__builtin_amdgcn_readfirstlane(list[at(it + 1)]), Qn, Dn, Mn);
       const int4 cr = lrange[at(it)];
       compute_phase(make_int4(__builtin_amdgcn_readfirstlane(cr.x), __builtin_amdgcn_readfirstlane(cr.y),
                               __builtin_amdgcn_readfirstlane(cr.z), __builtin_amdgcn_readfirstlane(cr.w)),
-                    Qb, Db, Mb);
+                    Qb, Db, Mb, __builtin_amdgcn_readfirstlane(ldsoff[at(it)]));
     };
+    stored_last = false;  // no store follows the copies of chunk 0
     if (n > 0) issue_chunk(__builtin_amdgcn_readfirstlane(list[at(0)]), Qs0, dOs0, Ms0);
     for (int it = 0; it < n; it += 2) {
       step(it, Qs0, dOs0, Ms0, Qs1, dOs1, Ms1);
@@ -545,19 +663,20 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 //   S^T = K Q^T, dP^T = V dO^T, dS^T = P (dP - Delta), dQ^T += K^T dS^T,
 // the K^T fragments coming from the row-major K tile through the transposing
 // read. dq += scale * dQ once at the end (each (row, head) has one owner).
-constexpr int kDqThreads = 512;  // 8 waves, two per SIMD
-constexpr int kDqWaves = kDqThreads / 64;
-constexpr int kDqVecPerWG = 32 * kDqWaves;
-constexpr int kDqKT = 64;
-
 template <int D>
 __global__ void __launch_bounds__(kDqThreads, 1)
 attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ delta,
-                   float* __restrict__ dq, const int2* __restrict__ block_range, int64_t n_vec,
-                   int G, int hq, int hkv, int B, int n_keys, float scale, float scale_log2) {
+                   float* __restrict__ dq, const int2* __restrict__ block_range,
+                   const int* __restrict__ ds_off, int64_t n_vec, int G, int hq, int hkv, int B,
+                   int n_keys, float scale, float scale_log2) {
   constexpr int NS = D / 8;
+  // vector groups in reverse (longest windows first), as in the forward
+  const int64_t group = (gridDim.x / hkv) - 1 - blockIdx.x / hkv;
+  // a group whose dS the dK/dV kernel stored is attn_bwd_dq_ds_kernel's (the
+  // decision is the same for all chunks of its larger groups)
+  if (ds_off[group * (kDqVecPerWG / kQC)] != kDsNone) return;
   __shared__ __attribute__((aligned(16))) bf16_t K0[kDqKT * D];
   __shared__ __attribute__((aligned(16))) bf16_t V0[kDqKT * D];
   __shared__ __attribute__((aligned(16))) bf16_t K1[kDqKT * D];
@@ -568,8 +687,7 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int s16 = lane & 15;
   const int g = __builtin_amdgcn_readfirstlane(blockIdx.x % hkv);
-  // vector groups in reverse (longest windows first), as in the forward
-  const int64_t vec = (int64_t)((gridDim.x / hkv) - 1 - blockIdx.x / hkv) * kDqVecPerWG + wave * 32 + (lane & 31);
+  const int64_t vec = group * kDqVecPerWG + wave * 32 + (lane & 31);
   const bool valid = vec < n_vec;
   int64_t row = 0;
   int hh = 0, qlo = 0, qhi = 0;
@@ -757,6 +875,227 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
 }
 
+// dQ from the stored dS, for the vector groups whose dS the dK/dV kernel
+// stored: a workgroup takes 512 consecutive vectors of one kv head, one
+// 64-vector chunk per wave (groups in reverse order, longest windows first).
+// Per tile of KT keys (KT / 32 stored groups), dQ^T += K^T dS^T with the K^T
+// fragments read from the row-major K tile by the transposing read (each one
+// serves both 32-vector halves of the wave's chunk) and the dS^T fragments (8
+// keys of the lane's vector) likewise from the stored key rows. Each wave
+// copies its own chunk's tiles (4 KB per group) and all waves the shared K
+// tile, global -> LDS asynchronously into a ring of NSTAGE stages, NSTAGE - 1
+// tiles ahead. The kernel streams 2 bytes of dS per live (vector, key) pair
+// from HBM and does one d-contraction per pair.
+template <int D>
+__global__ void __launch_bounds__(kDqThreads, 1)
+attn_bwd_dq_ds_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ ds,
+                      const float* __restrict__ lse, float* __restrict__ dq,
+                      const int2* __restrict__ block_range, const int4* __restrict__ chunk_range,
+                      const int* __restrict__ ds_off, int64_t ds_cap, int64_t n_vec,
+                      int64_t n_qc, int G, int hq, int hkv, int B, int n_keys, float scale) {
+  constexpr int NS = D / 8;
+  constexpr int KT = D == 128 ? kDsKeys : 2 * kDsKeys;  // keys per tile (one K copy pass)
+  constexpr int NG = KT / kDsKeys;                       // stored groups per tile
+  constexpr int TE = kDsTileBytes / 2;         // elements of a stored tile (a chunk's group)
+  constexpr int KPASS = KT * NS / kDqThreads;  // K copies per lane per tile
+  constexpr int GCOPY = kDsTileBytes / (kWave * 16);  // dS copies per lane per group
+  constexpr int NCOPY = KPASS + NG * GCOPY;    // copies per lane per tile
+  constexpr int SE = KT * D + kDqWaves * NG * TE;       // stage: K tile, then the waves' dS
+  constexpr int NSTAGE = (150 * 1024) / (SE * 2) < 3 ? (150 * 1024) / (SE * 2) : 3;
+  constexpr int LA = NSTAGE - 1;               // tiles in flight ahead of the computed one
+  static_assert(KPASS == 1 && GCOPY == 4 && NSTAGE >= 2 && NCOPY * LA < 64, "ring");
+  static_assert(kDsVecPerWG == kQC * kDqWaves, "one chunk per wave");
+
+  const int64_t group = (gridDim.x / hkv) - 1 - blockIdx.x / hkv;
+  const int64_t c0 = group * kDsChunksPerWG;
+  if (ds_off[c0] == kDsNone) return;  // recomputed by attn_bwd_dq_kernel
+
+  // one ring (the copies are assembly the compiler does not see: the waits
+  // below are the only ones, so one array with a run-time stage serves)
+  __shared__ __attribute__((aligned(16))) bf16_t ring[NSTAGE * SE];
+  __shared__ int wave_lo[kDqWaves], wave_hi[kDqWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s16 = lane & 15;
+  const int g = __builtin_amdgcn_readfirstlane(blockIdx.x % hkv);
+  const int64_t c = c0 + wave;  // this wave's chunk
+
+  // the wave's stored groups [glo, ghi)
+  int glo = 0, ghi = 0, dso = 0;
+  if (c < n_qc) {
+    const int4 cr = chunk_range[c];
+    if (cr.x < cr.y) {
+      glo = cr.x / kDsKeys;
+      ghi = (cr.y + kDsKeys - 1) / kDsKeys;
+      dso = ds_off[c];
+    }
+  }
+  glo = __builtin_amdgcn_readfirstlane(glo);
+  ghi = __builtin_amdgcn_readfirstlane(ghi);
+  dso = __builtin_amdgcn_readfirstlane(dso);
+  if (lane == 0) {
+    wave_lo[wave] = glo < ghi ? glo : 0x7fffffff;
+    wave_hi[wave] = glo < ghi ? ghi : -1;
+  }
+
+  // the lane's two vectors (one per 32-vector half of the chunk)
+  bool live_lane[2];
+  int64_t head_off[2];
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv) {
+    const int64_t vec = c * kQC + hv * 32 + (lane & 31);
+    live_lane[hv] = false;
+    head_off[hv] = 0;
+    if (vec < n_vec) {
+      const int64_t row = vec / G;
+      const int64_t idx = row * hq + (int64_t)g * G + (int)(vec % G);
+      head_off[hv] = idx * D;
+      if (lse[idx] != -INFINITY) {
+        const int2 r = block_range[row / B];
+        live_lane[hv] = r.x < r.y;
+      }
+    }
+  }
+
+  __syncthreads();
+  int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+  for (int w = 0; w < kDqWaves; ++w) { lo = min(lo, wave_lo[w]); hi = max(hi, wave_hi[w]); }
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+  const int n_t = lo < hi ? (hi - lo + NG - 1) / NG : 0;
+
+  const uint32_t k_off = tile_lane_offset<D, kDqThreads, kSwzBoth>((int64_t)hkv * D, tid);
+  // a stored tile is copied as it lies (copy j takes bytes 1024 j + 16 lane)
+  const uint32_t ds_src = (uint32_t)(lane * 16);
+  auto issue = [&](int t, bf16_t* St) {
+    const int kg0 = lo + NG * t;
+    const int k0 = kg0 * kDsKeys;
+    // rows past the last key read as zero (their dS is zero)
+    issue_tile_async_asm<D, KT, kDqThreads>(k + ((int64_t)k0 * hkv + g) * D, (int64_t)hkv * D,
+                                            k_off, St, tid, n_keys - k0);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int kg = kg0 + gi;
+      const bool present = kg >= glo && kg < ghi;
+      const int64_t tile = (int64_t)g * ds_cap + dso + kg;
+      // an absent group is a zero-range copy into the wave's own slot: every
+      // wave counts the same copies per tile (the waits count copies)
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(present ? uniform_ptr(ds + tile * TE) : (const void*)ds,
+                    present ? (uint32_t)kDsTileBytes : 0u);
+#pragma unroll
+      for (int j = 0; j < GCOPY; ++j)
+        async_copy16_buf_asm<true>(r, ds_src, (uint32_t)(j * kWave * 16),
+                                   St + KT * D + (wave * NG + gi) * TE + j * kWave * 8);
+    }
+  };
+
+  // transposing reads of K (rows t and t + 8 of each 16-key step) and of the
+  // lane's dS (opaque offsets, so that step offsets become immediates): lane s
+  // of each 16-lane group addresses key row 4 half + s / 4 and the 4 vectors
+  // 16 ((lane / 16) % 2) + 4 (s % 4) of a half (rows 8 further for the second
+  // read, 16 further per 16-key step, 1024 elements further for the second
+  // half); the read hands lane l the 4 keys of vector l % 32
+  int tr_off[D / 32][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int t = 4 * half + (s16 >> 2);
+    const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    tr_off[dt][0] = t * D + (((dcol >> 3) ^ swz_both<NS>(t)) * 8) + (dcol & 7);
+    tr_off[dt][1] = (t + 8) * D + (((dcol >> 3) ^ swz_both<NS>(t + 8)) * 8) + (dcol & 7);
+    asm volatile("" : "+v"(tr_off[dt][0]), "+v"(tr_off[dt][1]));
+  }
+  int rd_off;
+  {
+    const int s = lane & 15;
+    const int u = 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    rd_off = KT * D + wave * NG * TE + (4 * half + (s >> 2)) * kDsKeys + ds_word_off(u) / 2;
+    asm volatile("" : "+v"(rd_off));
+  }
+
+  f32x16 dqacc[2][D / 32];
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqacc[hv][dt][r] = 0.f;
+
+  auto compute = [&](int t, const bf16_t* St) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int kg = lo + NG * t + gi;
+      if (!(kg >= glo && kg < ghi)) continue;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        u32x4 su[2];
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const int sb = gi * TE + hv * (TE / 2) + h2 * 16 * kDsKeys;
+          const u32x2 y0 = read_tr4(&St[sb + rd_off]);
+          const u32x2 y1 = read_tr4(&St[sb + 8 * kDsKeys + rd_off]);
+          su[hv] = u32x4{y0.x, y0.y, y1.x, y1.y};
+        }
+        const int kbase = (gi * kDsKeys + 16 * h2) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const u32x2 x0 = read_tr4(&St[kbase + tr_off[dt][0]]);
+          const u32x2 x1 = read_tr4(&St[kbase + tr_off[dt][1]]);
+          const u32x4 au = {x0.x, x0.y, x1.x, x1.y};
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv)
+            dqacc[hv][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(au), as_bf16x8(su[hv]), dqacc[hv][dt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Step u: wait until this wave's copies of tile t = u - LA have landed (the
+  // later tiles' copies, NCOPY each, stay in flight), barrier (tile t visible
+  // to all waves; every wave is done with tile u - NSTAGE, whose stage tile u
+  // takes), copies of tile u, compute tile t.
+  int s_issue = 0, s_comp = 0;  // stages of tiles u and t
+  for (int u = 0; u < n_t + LA; ++u) {
+    const int t = u - LA;
+    if (t >= 0) {
+      const int later = min(u - 1, n_t - 1) - t;  // tiles issued after t
+      if (later >= 2)
+        wait_vmcnt<(LA >= 3 ? 2 : 0) * NCOPY>();
+      else if (later == 1)
+        wait_vmcnt<NCOPY>();
+      else
+        wait_async();
+    }
+    // a bare barrier: __syncthreads' fence would wait for every copy in flight
+    asm volatile("s_barrier" ::: "memory");
+    if (u < n_t) issue(u, ring + s_issue * SE);
+    if (t >= 0) compute(t, ring + s_comp * SE);
+    s_issue = s_issue + 1 == NSTAGE ? 0 : s_issue + 1;
+    if (t >= 0) s_comp = s_comp + 1 == NSTAGE ? 0 : s_comp + 1;
+  }
+
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv) {
+    if (!live_lane[hv]) continue;
+    float* dp = dq + head_off[hv];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = dt * 32 + 8 * jj + 4 * half;
+        float4 cur = *reinterpret_cast<float4*>(dp + d0);
+        cur.x = fmaf(dqacc[hv][dt][4 * jj], scale, cur.x);
+        cur.y = fmaf(dqacc[hv][dt][4 * jj + 1], scale, cur.y);
+        cur.z = fmaf(dqacc[hv][dt][4 * jj + 2], scale, cur.z);
+        cur.w = fmaf(dqacc[hv][dt][4 * jj + 3], scale, cur.w);
+        *reinterpret_cast<float4*>(dp + d0) = cur;
+      }
+  }
+}
+
 // fp32 path, part 1: dq per (row, head), one thread each, plain loops.
 template <int D>
 __global__ void __launch_bounds__(128)
@@ -840,12 +1179,19 @@ bwd_dkdv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   for (int c = 0; c < D; ++c) { dk[t * D + c] = ak[c]; dv[t * D + c] = av[c]; }
 }
 
+// Stored-dS tiles per kv head that ds_bytes hold (0 when fewer than one per
+// head; at most 2^30 so that tile numbers stay in int range).
+int64_t ds_capacity(size_t ds_bytes, int hkv) {
+  const int64_t cap = (int64_t)(ds_bytes / ((size_t)kDsTileBytes * (size_t)hkv));
+  return cap < (int64_t(1) << 30) ? cap : (int64_t(1) << 30);
+}
+
 template <int D>
 hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
-                        const int2* block_range, void* meta_ws, void* chunk_ws, const void* q,
-                        const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, float* delta, float* dq, void* dk, void* dv,
-                        hipStream_t stream) {
+                        const int2* block_range, void* meta_ws, void* chunk_ws, int* ds_off,
+                        void* ds_area, size_t ds_bytes, const void* q, const void* k,
+                        const void* v, const void* o, const void* dout, const float* lse,
+                        float* delta, float* dq, void* dk, void* dv, hipStream_t stream) {
   const int64_t Q = an.n_blocks * an.block_size;
   const int64_t n_rh = Q * hd.hq;
   hipError_t err;
@@ -856,6 +1202,8 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
     float* meta = static_cast<float*>(meta_ws);
     const int gshift = (G & (G - 1)) == 0 ? __builtin_ctz(G) : -1;
     int4* chunk_range = static_cast<int4*>(chunk_ws);
+    const int64_t cap = ds_capacity(ds_bytes, hd.hkv);
+    bf16_t* ds_bf16 = static_cast<bf16_t*>(ds_area);
     if (n_rh > 0) {
       const int64_t slots = (int64_t)hd.hkv * n_qc * kQC;
       if (o != nullptr) {
@@ -876,6 +1224,9 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
                          dim3(kRangeThreads), 0, stream, block_range, n_vec, G, an.block_size,
                          n_qc, chunk_range);
       if ((err = hipGetLastError()) != hipSuccess) return err;
+      hipLaunchKernelGGL(ds_offsets_kernel, dim3(1), dim3(kDsScanThreads), 0, stream,
+                         chunk_range, n_qc, cap, hd.hkv, ds_off, static_cast<int64_t*>(nullptr));
+      if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (n_keys == 0) return hipSuccess;
     const int64_t n_tiles = (n_keys + kBwdKeys - 1) / kBwdKeys;
@@ -883,16 +1234,25 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
                        dim3(kBwdThreads), 0, stream, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
                        static_cast<const bf16_t*>(dout), meta, static_cast<bf16_t*>(dk),
-                       static_cast<bf16_t*>(dv), chunk_range, n_vec, n_qc, G, gshift, hd.hq,
-                       hd.hkv, (int)n_keys, hd.scale, hd.scale * kLog2e);
+                       static_cast<bf16_t*>(dv), chunk_range, ds_bf16, ds_off, cap, n_vec, n_qc,
+                       G, gshift, hd.hq, hd.hkv, (int)n_keys, hd.scale, hd.scale * kLog2e);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (n_rh == 0) return hipSuccess;
+    // each vector group takes exactly one of the two dQ kernels (ds_off)
     const int64_t n_groups = (n_vec + kDqVecPerWG - 1) / kDqVecPerWG;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((unsigned)(n_groups * hd.hkv)),
                        dim3(kDqThreads), 0, stream, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-                       static_cast<const bf16_t*>(dout), lse, delta, dq, block_range, n_vec, G,
-                       hd.hq, hd.hkv, an.block_size, (int)n_keys, hd.scale, hd.scale * kLog2e);
+                       static_cast<const bf16_t*>(dout), lse, delta, dq, block_range, ds_off,
+                       n_vec, G, hd.hq, hd.hkv, an.block_size, (int)n_keys, hd.scale,
+                       hd.scale * kLog2e);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (cap == 0) return hipSuccess;  // only groups without keys count as stored
+    const int64_t n_ds_groups = (n_vec + kDsVecPerWG - 1) / kDsVecPerWG;
+    hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D>), dim3((unsigned)(n_ds_groups * hd.hkv)),
+                       dim3(kDqThreads), 0, stream, static_cast<const bf16_t*>(k), ds_bf16, lse,
+                       dq, block_range, chunk_range, ds_off, cap, n_vec, n_qc, G, hd.hq, hd.hkv,
+                       an.block_size, (int)n_keys, hd.scale);
     return hipGetLastError();
   }
   if (o != nullptr && n_rh > 0) {
@@ -921,15 +1281,36 @@ hipError_t launch_bwd_t(const splitkv_anchors& an, const splitkv_heads& hd, int6
 }  // namespace
 
 hipError_t launch_bwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
-                      const int2* block_range, void* meta, void* chunk_range, const void* q,
-                      const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, float* delta, float* dq, void* dk, void* dv,
-                      hipStream_t stream) {
+                      const int2* block_range, void* meta, void* chunk_range, int* ds_off,
+                      void* ds_area, size_t ds_bytes, const void* q, const void* k,
+                      const void* v, const void* o, const void* dout, const float* lse,
+                      float* delta, float* dq, void* dk, void* dv, hipStream_t stream) {
   if (hd.d == 128)
-    return launch_bwd_t<128>(an, hd, n_keys, block_range, meta, chunk_range, q, k, v, o, dout,
-                             lse, delta, dq, dk, dv, stream);
-  return launch_bwd_t<64>(an, hd, n_keys, block_range, meta, chunk_range, q, k, v, o, dout, lse,
-                          delta, dq, dk, dv, stream);
+    return launch_bwd_t<128>(an, hd, n_keys, block_range, meta, chunk_range, ds_off, ds_area,
+                             ds_bytes, q, k, v, o, dout, lse, delta, dq, dk, dv, stream);
+  return launch_bwd_t<64>(an, hd, n_keys, block_range, meta, chunk_range, ds_off, ds_area,
+                          ds_bytes, q, k, v, o, dout, lse, delta, dq, dk, dv, stream);
+}
+
+hipError_t launch_bwd_ds_need(const splitkv_anchors& an, const splitkv_heads& hd,
+                              const int2* block_range, void* chunk_ws, int* ds_off,
+                              int64_t* need, hipStream_t stream) {
+  const int G = hd.hq / hd.hkv;
+  const int64_t n_vec = an.n_blocks * an.block_size * G;
+  const int64_t n_qc = (n_vec + kQC - 1) / kQC;
+  int4* chunk_range = static_cast<int4*>(chunk_ws);
+  if (n_qc > 0) {
+    const int64_t per_wg = kRangeThreads / kWave;
+    hipLaunchKernelGGL(chunk_range_kernel, dim3((unsigned)((n_qc + per_wg - 1) / per_wg)),
+                       dim3(kRangeThreads), 0, stream, block_range, n_vec, G, an.block_size,
+                       n_qc, chunk_range);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  // the bf16 path alone stores dS; fp32 needs none (hkv 0 makes need 0)
+  hipLaunchKernelGGL(ds_offsets_kernel, dim3(1), dim3(kDsScanThreads), 0, stream, chunk_range,
+                     n_qc, (int64_t)0, hd.dtype == SPLITKV_BF16 ? hd.hkv : 0, ds_off, need);
+  return hipGetLastError();
 }
 
 }  // namespace splitkv

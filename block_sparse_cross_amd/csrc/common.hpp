@@ -88,6 +88,14 @@ __device__ __forceinline__ void async_copy16(const void* gsrc, void* lds_wave_ba
 }
 
 __device__ __forceinline__ void wait_async() { __builtin_amdgcn_s_waitcnt(0); }
+// Wait until at most N of this wave's vector-memory operations are still in
+// flight (they complete in issue order for this count), leaving the LDS and
+// export counters alone: copies issued after the ones needed stay in flight.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  // vmcnt in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15: no wait
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ u32x2 read_tr4(const bf16_t* p) {
   const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
@@ -166,6 +174,33 @@ __device__ __forceinline__ void async_copy16_buf(__amdgpu_buffer_rsrc_t r, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, lane_off,
                                            scalar_off, 0, 0);
 }
+// The same copy written as inline assembly, so that the compiler does not
+// know of it and inserts no waits of its own before later LDS reads (its
+// alias tracking of asynchronous LDS writes is conservative across a loop of
+// three stages and waited for every copy in flight). The caller waits for the
+// copies itself (wait_vmcnt / wait_async) and must not use M0 or the
+// compiler's own LDS copies in the same kernel: the assembly sets M0 to the
+// wave's LDS destination. The LDS address is read from the first lane. NT
+// marks data read once (non-temporal: not kept in the caches).
+template <bool NT = false>
+__device__ __forceinline__ void async_copy16_buf_asm(__amdgpu_buffer_rsrc_t r, uint32_t lane_off,
+                                                     uint32_t scalar_off, void* lds_wave_base) {
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)((lds_void_t*)lds_wave_base));
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(lds), "v"(lane_off), "s"(r), "s"(scalar_off) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(lane_off), "s"(r), "s"(scalar_off) : "memory");
+}
+// async_copy16 as inline assembly (see async_copy16_buf_asm).
+__device__ __forceinline__ void async_copy16_asm(const void* gsrc, void* lds_wave_base) {
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)((lds_void_t*)lds_wave_base));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(gsrc) : "memory");
+}
 // A 64-bit address that is the same in every lane, read from the first lane
 // into scalar registers (readfirstlane returns a signed int: each half goes
 // through uint32_t so that it is zero-extended).
@@ -195,7 +230,8 @@ __device__ __forceinline__ uint32_t tile_lane_offset(int64_t row_stride, int tid
 }
 template <int D, int ROWS, int THREADS>
 __device__ __forceinline__ void issue_tile_async_off(const bf16_t* first, int64_t row_stride,
-                                                     uint32_t lane_off, bf16_t* tile, int tid) {
+                                                     uint32_t lane_off, bf16_t* tile, int tid,
+                                                     int valid_rows = ROWS) {
   constexpr int NS = D / 8;
   constexpr int PASSES = ROWS * NS / THREADS;
   constexpr int ROWS_PER_PASS = THREADS / NS;
@@ -203,12 +239,33 @@ __device__ __forceinline__ void issue_tile_async_off(const bf16_t* first, int64_
   static_assert(ROWS_PER_PASS % 16 == 0, "pass step must keep the swizzle");
   uint32_t off = lane_off;
   asm volatile("" : "+v"(off));
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(first), (uint32_t)(ROWS * row_stride * 2));
+  // rows from valid_rows on lie outside the range: they read as zero
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(uniform_ptr(first), (uint32_t)(min(valid_rows, ROWS) * row_stride * 2));
   const uint32_t step = (uint32_t)(ROWS_PER_PASS * row_stride * 2);
   const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass)
     async_copy16_buf(r, off, pass * step, tile + pass * THREADS * 8 + lds_off);
+}
+
+// issue_tile_async_off through async_copy16_buf_asm.
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void issue_tile_async_asm(const bf16_t* first, int64_t row_stride,
+                                                     uint32_t lane_off, bf16_t* tile, int tid,
+                                                     int valid_rows) {
+  constexpr int NS = D / 8;
+  constexpr int PASSES = ROWS * NS / THREADS;
+  constexpr int ROWS_PER_PASS = THREADS / NS;
+  static_assert(PASSES * THREADS == ROWS * NS, "tile must split evenly over the threads");
+  static_assert(ROWS_PER_PASS % 16 == 0, "pass step must keep the swizzle");
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(uniform_ptr(first), (uint32_t)(min(valid_rows, ROWS) * row_stride * 2));
+  const uint32_t step = (uint32_t)(ROWS_PER_PASS * row_stride * 2);
+  const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass)
+    async_copy16_buf_asm(r, lane_off, pass * step, tile + pass * THREADS * 8 + lds_off);
 }
 
 // Local (per-rank) key range of one block. The local buffer holds the rank's

@@ -33,7 +33,8 @@ struct BwdWorkspace {
   size_t block_range;  // int2 [N]
   size_t meta;         // fp32 [hkv][n_qc][4][kBwdChunk]: lse*log2e, Delta, lo, hi
   size_t chunk_range;  // int4 [n_qc], n_qc = ceil(Q*G / kBwdChunk)
-  size_t total;
+  size_t ds_off;       // int32 [n_qc]: first stored-dS tile of each chunk
+  size_t total;        // bytes past total (if any) hold stored dS tiles
 };
 FwdWorkspace fwd_workspace_layout(int64_t n_blocks);
 BwdWorkspace bwd_workspace_layout(int64_t n_blocks, int32_t block_size, int32_t hq, int32_t hkv);
@@ -85,10 +86,17 @@ hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const void* 
                        const void* A2, const void* B2, void* C, int c_dtype, const float* bias,
                        int accumulate, hipStream_t stream);
 
+// ds_area / ds_bytes: room for stored dS tiles (may be empty: then every dQ
+// is recomputed).
 hipError_t launch_bwd(const splitkv_anchors& an, const splitkv_heads& hd, int64_t n_keys,
-                      const int2* block_range, void* meta, void* chunk_range, const void* q,
-                      const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, float* delta, float* dq, void* dk, void* dv,
-                      hipStream_t stream);
+                      const int2* block_range, void* meta, void* chunk_range, int* ds_off,
+                      void* ds_area, size_t ds_bytes, const void* q, const void* k,
+                      const void* v, const void* o, const void* dout, const float* lse,
+                      float* delta, float* dq, void* dk, void* dv, hipStream_t stream);
+
+// Bytes of stored dS that cover every chunk, written to *need (device).
+hipError_t launch_bwd_ds_need(const splitkv_anchors& an, const splitkv_heads& hd,
+                              const int2* block_range, void* chunk_range, int* ds_off,
+                              int64_t* need, hipStream_t stream);
 
 }  // namespace splitkv

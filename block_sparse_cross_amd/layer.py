@@ -43,12 +43,15 @@ class DraftLayer:
 
     s, a: device int64 anchors [N]; B: block size; chunk_starts[p]: device int64
     chunk starts of rank p (ascending); m: chunk length; weights: bf16 Wq
-    [hq d, H], Wk, Wv [hkv d, H], Wo [H, hq d] and fp32 bo [H]."""
+    [hq d, H], Wk, Wv [hkv d, H], Wo [H, hq d] and fp32 bo [H]. store_ds: the
+    backward's workspace holds each partial's dS, so that dq is not
+    recomputed."""
 
     def __init__(self, s: torch.Tensor, a: torch.Tensor, B: int, hq: int, hkv: int, d: int,
                  chunk_starts: Sequence[torch.Tensor], m: int, Wq: torch.Tensor,
                  Wk: torch.Tensor, Wv: torch.Tensor, Wo: torch.Tensor, bo: torch.Tensor,
-                 scale: Optional[float] = None, own_blocks: bool = False):
+                 scale: Optional[float] = None, own_blocks: bool = False,
+                 store_ds: bool = True):
         self.s, self.a, self.B = s, a, B
         self.hq, self.hkv, self.d, self.m = hq, hkv, d, m
         self.cs = list(chunk_starts)
@@ -83,8 +86,15 @@ class DraftLayer:
         self.dv = [torch.empty((n, hkv, d), **bf) for n in n_keys]
         an = binding.make_anchors(s, a, B)
         hd = binding.make_heads(hq, hkv, d, torch.bfloat16, self.scale)
+        # room for the largest partial's stored dS (dq then needs no recompute)
+        ds = 0
+        if store_ds:
+            ds = max(binding.splitkv_attn_bwd_ds_bytes(*self._segment(p)[:2], B,
+                                                       *self._segment(p)[2:], hq, hkv, d,
+                                                       torch.bfloat16)
+                     for p in range(self.n_parts))
         ws = max(binding.splitkv_workspace_bytes(binding.SPLITKV_OP_FWD, an, hd, None),
-                 binding.splitkv_workspace_bytes(binding.SPLITKV_OP_BWD, an, hd, None))
+                 binding.splitkv_workspace_bytes(binding.SPLITKV_OP_BWD, an, hd, None) + ds)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
 
     # ------------------------------------------------------------- forward --

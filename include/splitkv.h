@@ -263,17 +263,35 @@ int splitkv_cast_bf16(int64_t n, const float* src, void* dst, void* stream);
  * dq: fp32 [Q, hq, d], ACCUMULATED (+=) so that P emulated ranks sum into one
  *   buffer (the reduce-scatter of Algorithm 1); the caller zeroes it first.
  * dk, dv: [J*m, hkv, d] in hd->dtype, overwritten (local to the rank).
- * workspace: splitkv_workspace_bytes(SPLITKV_OP_BWD, ...) bytes. */
+ * workspace: at least splitkv_workspace_bytes(SPLITKV_OP_BWD, ...) bytes
+ *   (W). With bf16, bytes past W (workspace 16-byte aligned) hold the ds of
+ *   the pairs as the dK/dV pass computes them (2 bytes per (q head, row, local
+ *   key) pair the key union of a 64-vector query chunk spans), so that dq
+ *   comes from them instead of recomputing S and dP; the query rows are taken
+ *   256 (row, head) vectors of a kv head at a time, in order, as far as the
+ *   room goes, and the rest recompute. splitkv_attn_bwd_ds_bytes gives the
+ *   room that covers every row. Both ways compute the same sums; the rounding
+ *   of dq may differ in the last bits between them. */
 int splitkv_attn_bwd(const splitkv_anchors* an, const splitkv_heads* hd,
                      const splitkv_local* loc, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, float* delta,
                      float* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Room for the stored ds of splitkv_attn_bwd (bytes past W) that covers every
+ * query row of these anchors, heads and local chunks: enqueued on `stream`,
+ * written to *ds_bytes (DEVICE int64, 8-byte aligned) as the pair count above
+ * times 2, rounded up to whole 32-key groups. 0 for fp32 (that path stores
+ * nothing). workspace: W bytes, overwritten. */
+int splitkv_attn_bwd_ds_bytes(const splitkv_anchors* an, const splitkv_heads* hd,
+                              const splitkv_local* loc, void* workspace, size_t workspace_bytes,
+                              int64_t* ds_bytes, void* stream);
+
 /* The backward above without a workspace argument, for callers that cannot
  * allocate device memory at all (code under stream capture, tight serving
  * loops, harnesses that forbid allocation). Same arguments, results and
- * kernels as splitkv_attn_bwd; its scratch (the per-block key ranges, the
+ * kernels as splitkv_attn_bwd with a workspace of exactly W bytes (dq
+ * recomputed, no stored ds); its scratch (the per-block key ranges, the
  * per-vector records and the per-chunk ranges of the workspace) lives in a
  * fixed device array of SPLITKV_NOALLOC_SCRATCH_BYTES that the library holds
  * on every device it runs on until the process ends. The call allocates and

@@ -255,8 +255,19 @@ BWD_CASES = [
 ]
 
 
+def bwd_ws(c, cs, store):
+    """No stored dS, room for all of it, or for about half (the rest recomputed)."""
+    if store == "none":
+        return None
+    args = (to_dev(c["s"]), to_dev(c["a"]), c["B"], cs, c["m"], c["hq"], c["hkv"], c["d"],
+            torch.bfloat16)
+    need = binding.splitkv_attn_bwd_ds_bytes(*args)
+    return binding.bwd_workspace(*args, ds_bytes=need if store == "all" else need // 2)
+
+
+@pytest.mark.parametrize("store", ["none", "all", "part"])
 @pytest.mark.parametrize("idx", range(len(BWD_CASES)))
-def test_bwd_bf16_small(idx):
+def test_bwd_bf16_small(idx, store):
     c = make_case(200 + idx, **BWD_CASES[idx])
     Q = c["q"].shape[0]
     # global forward quantities from the oracle over the whole context
@@ -270,7 +281,8 @@ def test_bwd_bf16_small(idx):
     dq = torch.zeros(c["q"].shape, dtype=torch.float32, device="cuda")
     dk, dv, delta = binding.splitkv_attn_bwd(to_dev(c["s"]), to_dev(c["a"]), c["B"], cs, c["m"],
                                              to_dev(c["q"]), to_dev(c["k"]), to_dev(c["v"]),
-                                             to_dev(o_bf), to_dev(c["do"]), to_dev(lse32), dq)
+                                             to_dev(o_bf), to_dev(c["do"]), to_dev(lse32), dq,
+                                             workspace=bwd_ws(c, cs, store))
     torch.cuda.synchronize()
     dq_ref, dk_ref, dv_ref = oracle.attn_bwd(c["B"], c["s"], c["a"], vals64(c["q"]),
                                              vals64(c["do"]), lse32.astype(np.float64), dl,

@@ -104,17 +104,28 @@ def test_fwd_full_size_sampled_rows(name):
     assert np.isfinite(got_l[~empty]).all()
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_bwd_full_size_sampled(name):
+def ds_workspace(w, sd, ad, cs):
+    """The backward workspace bench.py gives a rank: room for all of its dS."""
+    return binding.bwd_workspace(sd, ad, w.B, cs, w.m, w.hq, w.hkv, w.d, torch.bfloat16)
+
+
+# dq from the stored dS (as bench.py runs it) on every share; recomputed (the
+# minimum workspace, as the no-allocation entry point runs it) on two
+@pytest.mark.parametrize("name,store", [(n, True) for n in FULL] +
+                         [("weak8", False), ("qs8", False)])
+def test_bwd_full_size_sampled(name, store):
     sh = share(name)
     w = sh.w
     o_syn = inputs.gen_o_like(w, SEED, w.Q)
     lse_syn = inputs.gen_lse_like(w.Q, w.hq, SEED, center=10.0)
     do = inputs.gen_do(w, SEED)
     dq = torch.zeros((w.Q, w.hq, w.d), dtype=torch.float32, device="cuda")
+    ws = ds_workspace(w, sh.sd, sh.ad, sh.cs) if store else None
     dk, dv, delta = binding.splitkv_attn_bwd(sh.sd, sh.ad, w.B, sh.cs, w.m, sh.qd, sh.kd, sh.vd,
-                                             to_dev(o_syn), to_dev(do), to_dev(lse_syn), dq)
+                                             to_dev(o_syn), to_dev(do), to_dev(lse_syn), dq,
+                                             workspace=ws)
     torch.cuda.synchronize()
+    del ws
     g = np.random.default_rng(5)
     # dq: the last block (longest window) and a random block, all heads
     dq_rows = block_rows(np.unique([w.N - 1, int(g.integers(0, w.N - 1))]), w.B)
@@ -214,11 +225,14 @@ def test_step_full_size(name):
     dq = torch.zeros((w.Q, w.hq, w.d), dtype=torch.float32, device="cuda")
     delta = torch.empty((w.Q, w.hq), dtype=torch.float32, device="cuda")
     grads = []
+    ws = torch.empty(max(ds_workspace(w, sd, ad, cs).numel() for cs, _, _ in locs),
+                     dtype=torch.uint8, device="cuda")
     for p, (cs, k, v) in enumerate(locs):
         dk, dv, _ = binding.splitkv_attn_bwd(sd, ad, w.B, cs, w.m, qd, k, v, om if p == 0 else None,
-                                             dod, lm, dq, delta=delta)
+                                             dod, lm, dq, delta=delta, workspace=ws)
         grads.append((dk, dv))
     torch.cuda.synchronize()
+    del ws
     print("[step] %s: GPU step done" % name, flush=True)
 
     last = w.N - 1
