@@ -343,6 +343,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
   const int lds_wave = __builtin_amdgcn_readfirstlane(wave * 64 * 8);
   auto issue_chunk = [&](int64_t c, bf16_t* Qd, bf16_t* Dd, float* Md) {
+    const uint32_t qa = lds_addr(Qd), da = lds_addr(Dd), ma = lds_addr(Md);
     const int64_t vec0 = c * kQC;
     if (fast_chunks && vec0 + kQC <= n_vec) {
       // the chunk's kQC / G rows of all hq heads, as buffer resources
@@ -354,11 +355,11 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       for (int pp = 0; pp < QPASSES; ++pp) {
         const int r0 = RPP * pp;
         const uint32_t step = (uint32_t)((((int64_t)(r0 >> gshift)) * hq + (r0 & (G - 1))) * D * 2);
-        async_copy16_buf_asm(qr, lane_off, step, Qd + pp * kBwdThreads * 8 + lds_wave);
-        async_copy16_buf_asm(dr, lane_off, step, Dd + pp * kBwdThreads * 8 + lds_wave);
+        async_copy16_buf_asm(qr, lane_off, step, qa + (pp * kBwdThreads * 8 + lds_wave) * 2);
+        async_copy16_buf_asm(dr, lane_off, step, da + (pp * kBwdThreads * 8 + lds_wave) * 2);
       }
       if (wave == NW - 1 && lane < kQC)
-        async_copy16_asm(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
+        async_copy16_asm(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, ma);
       return;
     }
 #pragma unroll
@@ -371,10 +372,10 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const uint32_t rw = gshift >= 0 ? vec >> gshift : vec / (uint32_t)G;
       const int64_t idx = (int64_t)rw * hq + g * G + (vec - rw * G);
       const bf16_t* src = (tsel ? dout : q) + idx * D + (phys ^ swz_both<NS>(row)) * 8;
-      async_copy16_asm(src, (tsel ? Dd : Qd) + (uu - lane) * 8);
+      async_copy16_asm(src, (tsel ? da : qa) + (uu - lane) * 16);
     }
     if (wave == NW - 1 && lane < kQC)
-      async_copy16_asm(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, Md);
+      async_copy16_asm(meta + ((int64_t)g * n_qc + c) * (4 * kQC) + lane * 4, ma);
   };
 
   // Element offsets of this lane's transposing reads of Q and dO (rows t and
@@ -408,7 +409,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // `half` (the vector half and h2 add 2048 hv + 32 h2 as immediates).
   int ds_lane = (lane & 31) * (kDsKeys * 2) + 16 * half;
   asm volatile("" : "+v"(ds_lane));
-  bool stored_last = false;  // the last computed chunk stored its dS
+  bool stored_last = false;  // the last computed chunk issued its 4 dS stores
 
   // S = Q K^T and dP = dO V^T (lane = key, 16 vectors per lane), P, dS,
   // dV^T += dO^T P, dK^T += Q^T dS, for the chunk's 32-vector halves. The
@@ -428,20 +429,21 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     u32x4 opa[3], opb[3];
     int4 mlo[2], mhi[2];     // key intervals of 4 vectors (masked chunks only)
     u32x4 pu, su;            // P and dS of the current 16-vector step, bf16
-    // this wave's stored dS tile of the chunk (a scalar base; the lane offset
-    // and the step's immediate are added by the store)
+    // this wave's stored dS tile of the chunk as a buffer resource (scalar),
+    // of zero range when the chunk is not stored: the hardware then drops
+    // the stores, and every computed chunk issues the same 4 stores
     const bool st = dso != kDsNone;
-    stored_last = st;  // this chunk issues 4 stores
     const int64_t tile = (int64_t)g * ds_cap + (st ? dso : 0) + (kw0 / kDsKeys);
-    typedef __attribute__((address_space(1))) char gchar;
-    gchar* const dst = (gchar*)uniform_ptr(ds + tile * (kDsTileBytes / 2));
-    // dS of the current 16-vector step: one 16-byte store (a plain one: the
+    const __amdgpu_buffer_rsrc_t dsr =
+        make_rsrc(st ? uniform_ptr(ds + tile * (kDsTileBytes / 2)) : (const void*)ds,
+                  st ? (uint32_t)kDsTileBytes : 0u);
+    stored_last = true;
+    // dS of the current 16-vector step: one 16-byte store (lane offset in a
+    // VGPR, the step's offset as the scalar offset; a plain store: the
     // non-temporal form was 5% slower here)
     auto store_ds = [&](int hv, int h2) {
-      if (!st) return;
-      typedef __attribute__((address_space(1))) u32x4 gu32x4;
-      *reinterpret_cast<gu32x4*>(dst + (uint32_t)ds_lane + hv * (kDsTileBytes / 2) + 32 * h2) =
-          su;
+      __builtin_amdgcn_raw_buffer_store_b128(su, dsr, ds_lane, hv * (kDsTileBytes / 2) + 32 * h2,
+                                             0);
     };
 
     auto load_sd = [&](int hv, int ks, int b) {
@@ -969,12 +971,12 @@ attn_bwd_dq_ds_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ d
   const uint32_t k_off = tile_lane_offset<D, kDqThreads, kSwzBoth>((int64_t)hkv * D, tid);
   // a stored tile is copied as it lies (copy j takes bytes 1024 j + 16 lane)
   const uint32_t ds_src = (uint32_t)(lane * 16);
-  auto issue = [&](int t, bf16_t* St) {
+  auto issue = [&](int t, uint32_t sa) {  // sa: the stage's LDS byte address
     const int kg0 = lo + NG * t;
     const int k0 = kg0 * kDsKeys;
     // rows past the last key read as zero (their dS is zero)
     issue_tile_async_asm<D, KT, kDqThreads>(k + ((int64_t)k0 * hkv + g) * D, (int64_t)hkv * D,
-                                            k_off, St, tid, n_keys - k0);
+                                            k_off, sa, tid, n_keys - k0);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       const int kg = kg0 + gi;
@@ -988,7 +990,7 @@ attn_bwd_dq_ds_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ d
 #pragma unroll
       for (int j = 0; j < GCOPY; ++j)
         async_copy16_buf_asm<true>(r, ds_src, (uint32_t)(j * kWave * 16),
-                                   St + KT * D + (wave * NG + gi) * TE + j * kWave * 8);
+                                   sa + (KT * D + (wave * NG + gi) * TE + j * kWave * 8) * 2);
     }
   };
 
@@ -1071,7 +1073,7 @@ attn_bwd_dq_ds_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ d
     }
     // a bare barrier: __syncthreads' fence would wait for every copy in flight
     asm volatile("s_barrier" ::: "memory");
-    if (u < n_t) issue(u, ring + s_issue * SE);
+    if (u < n_t) issue(u, lds_addr(ring) + s_issue * SE * 2);
     if (t >= 0) compute(t, ring + s_comp * SE);
     s_issue = s_issue + 1 == NSTAGE ? 0 : s_issue + 1;
     if (t >= 0) s_comp = s_comp + 1 == NSTAGE ? 0 : s_comp + 1;

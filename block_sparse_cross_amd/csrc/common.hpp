@@ -180,13 +180,17 @@ __device__ __forceinline__ void async_copy16_buf(__amdgpu_buffer_rsrc_t r, uint3
 // three stages and waited for every copy in flight). The caller waits for the
 // copies itself (wait_vmcnt / wait_async) and must not use M0 or the
 // compiler's own LDS copies in the same kernel: the assembly sets M0 to the
-// wave's LDS destination. The LDS address is read from the first lane. NT
-// marks data read once (non-temporal: not kept in the caches).
+// wave's LDS destination, given as a 32-bit LDS byte address (lds_addr of a
+// __shared__ array plus an offset: a generic pointer would cost a null check
+// and 64-bit registers per copy). NT marks data read once (non-temporal: not
+// kept in the caches).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const lds_void_t*)p);
+}
 template <bool NT = false>
 __device__ __forceinline__ void async_copy16_buf_asm(__amdgpu_buffer_rsrc_t r, uint32_t lane_off,
-                                                     uint32_t scalar_off, void* lds_wave_base) {
-  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
-      (int)(uint32_t)(uintptr_t)((lds_void_t*)lds_wave_base));
+                                                     uint32_t scalar_off, uint32_t lds_wave) {
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_wave);
   if constexpr (NT)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                  :: "s"(lds), "v"(lane_off), "s"(r), "s"(scalar_off) : "memory");
@@ -194,10 +198,9 @@ __device__ __forceinline__ void async_copy16_buf_asm(__amdgpu_buffer_rsrc_t r, u
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :: "s"(lds), "v"(lane_off), "s"(r), "s"(scalar_off) : "memory");
 }
-// async_copy16 as inline assembly (see async_copy16_buf_asm).
-__device__ __forceinline__ void async_copy16_asm(const void* gsrc, void* lds_wave_base) {
-  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
-      (int)(uint32_t)(uintptr_t)((lds_void_t*)lds_wave_base));
+// async_copy16 as inline assembly (same conventions).
+__device__ __forceinline__ void async_copy16_asm(const void* gsrc, uint32_t lds_wave) {
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_wave);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds), "v"(gsrc) : "memory");
 }
@@ -249,10 +252,10 @@ __device__ __forceinline__ void issue_tile_async_off(const bf16_t* first, int64_
     async_copy16_buf(r, off, pass * step, tile + pass * THREADS * 8 + lds_off);
 }
 
-// issue_tile_async_off through async_copy16_buf_asm.
+// issue_tile_async_off through async_copy16_buf_asm (tile: LDS byte address).
 template <int D, int ROWS, int THREADS>
 __device__ __forceinline__ void issue_tile_async_asm(const bf16_t* first, int64_t row_stride,
-                                                     uint32_t lane_off, bf16_t* tile, int tid,
+                                                     uint32_t lane_off, uint32_t tile, int tid,
                                                      int valid_rows) {
   constexpr int NS = D / 8;
   constexpr int PASSES = ROWS * NS / THREADS;
@@ -265,7 +268,7 @@ __device__ __forceinline__ void issue_tile_async_asm(const bf16_t* first, int64_
   const int lds_off = __builtin_amdgcn_readfirstlane((tid >> 6) * 64 * 8);
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass)
-    async_copy16_buf_asm(r, lane_off, pass * step, tile + pass * THREADS * 8 + lds_off);
+    async_copy16_buf_asm(r, lane_off, pass * step, tile + (pass * THREADS * 8 + lds_off) * 2);
 }
 
 // Local (per-rank) key range of one block. The local buffer holds the rank's
