@@ -6,7 +6,9 @@ fixed cases. Each case draws its own mix of block size B, head grouping
 and count, local chunk subset, samples per batch, anchors per sample and
 logit scale, so that combinations the fixed cases do not pair up are covered
 too (for instance B = 1 with a group of 3, or one sample whose chunks are all
-local)."""
+local). A second sweep runs the whole method on random shapes: the GPU's plan
+over P ranks, every rank's forward, the merge and every rank's backward, against
+the oracle's unsplit attention over the whole context."""
 import numpy as np
 import pytest
 import torch
@@ -72,3 +74,75 @@ def test_sweep_fwd_and_bwd(i):
     assert_close_bf16(to_f64(dq), dq_ref, "dq")
     assert_close_bf16(to_f64(dk), dk_ref, "dk")
     assert_close_bf16(to_f64(dv), dv_ref, "dv")
+
+
+N_PROTOCOL = 12
+
+
+def draw_protocol(i):
+    """Parameters of whole-protocol case i: P ranks of J chunks of m positions."""
+    g = np.random.default_rng(9500 + i)
+    P, J = int(g.choice([2, 3, 4, 8])), int(g.integers(1, 5))
+    m = int(g.choice([16, 33, 64, 128]))
+    hq, hkv = [(4, 1), (6, 2), (8, 2), (32, 8)][g.integers(4)]
+    n_chunks = P * J
+    n_samples = int(g.choice([s for s in (1, 2, 3, 4) if (m * n_chunks) % s == 0]))
+    L = m * n_chunks // n_samples
+    A = int(min(g.choice([2, 6, 16]), L - L // 4))
+    return P, J, dict(B=int(g.choice([1, 5, 16])), hq=hq, hkv=hkv, d=int(g.choice([64, 128])),
+                      m=m, n_chunks=n_chunks, J=n_chunks, n_samples=n_samples, A=A,
+                      empty_block=bool(g.random() < 0.5))
+
+
+@pytest.mark.parametrize("i", range(N_PROTOCOL))
+def test_sweep_whole_protocol(i):
+    """The method end to end on one GPU: the GPU's plan (Eq. 6, LPT) splits the
+    context into P bundles of J chunks; every rank's partial forward (Eq. 3),
+    merged (Eq. 4), equals the unsplit attention over the whole context, and
+    every rank's backward (Algorithm 1, given the global o and lse) sums to the
+    unsplit dq and, put back at each key's place, gives the unsplit dk and dv."""
+    P, J, p = draw_protocol(i)
+    print("protocol case", i, "P", P, "J", J, p, flush=True)
+    c = make_case(9600 + i, **p)
+    Q, S, m = c["q"].shape[0], c["S"], c["m"]
+    sd, ad = to_dev(c["s"]), to_dev(c["a"])
+    _, _, bundles, _ = [t.cpu().numpy() for t in binding.splitkv_plan(sd, ad, c["B"], S, m, P, J)]
+    assert sorted(bundles.ravel().tolist()) == list(range(P * J))
+    qd, dod = to_dev(c["q"]), to_dev(c["do"])
+    ranks = []
+    for ids in bundles:
+        pos = oracle.local_key_positions(ids.astype(np.int64), m)
+        ranks.append((pos, to_dev(ids.astype(np.int64) * m), to_dev(c["kg"][pos]),
+                      to_dev(c["vg"][pos])))
+    # forward: every rank's partial, then the merge
+    parts = [binding.splitkv_attn_fwd(sd, ad, c["B"], cs, m, qd, k, v) for _, cs, k, v in ranks]
+    om, lm = binding.splitkv_lse_merge(torch.stack([x[0] for x in parts]),
+                                       torch.stack([x[1] for x in parts]))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partial_attn(np.arange(Q), c["B"], c["s"], c["a"], vals64(c["q"]),
+                                       np.arange(S), vals64(c["kg"]), vals64(c["vg"]),
+                                       c["d"] ** -0.5)
+    assert_lse(to_f64(lm), l_ref, "merged lse")
+    assert_close_bf16(to_f64(om), o_ref, "merged o")
+    # backward of every rank from the global o and lse; dq summed, dk and dv placed
+    o_bf = inputs.f32_to_bf16_bits(o_ref.astype(np.float32))
+    lse32 = l_ref.astype(np.float32)
+    od, ld = to_dev(o_bf), to_dev(lse32)
+    dq = torch.zeros(c["q"].shape, dtype=torch.float32, device="cuda")
+    dk = np.zeros(c["kg"].shape, dtype=np.float64)
+    dv = np.zeros(c["vg"].shape, dtype=np.float64)
+    for pos, cs, k, v in ranks:
+        ws = binding.bwd_workspace(sd, ad, c["B"], cs, m, c["hq"], c["hkv"], c["d"],
+                                   torch.bfloat16)
+        dk_p, dv_p, _ = binding.splitkv_attn_bwd(sd, ad, c["B"], cs, m, qd, k, v, od, dod, ld,
+                                                 dq, workspace=ws)
+        torch.cuda.synchronize()
+        dk[pos], dv[pos] = to_f64(dk_p), to_f64(dv_p)
+    dl = oracle.delta(vals64(o_bf), vals64(c["do"]))
+    dq_ref, dk_ref, dv_ref = oracle.attn_bwd(c["B"], c["s"], c["a"], vals64(c["q"]),
+                                             vals64(c["do"]), lse32.astype(np.float64), dl,
+                                             np.arange(S), vals64(c["kg"]), vals64(c["vg"]),
+                                             c["d"] ** -0.5, np.arange(Q), np.arange(S))
+    assert_close_bf16(to_f64(dq), dq_ref, "dq summed over ranks")
+    assert_close_bf16(dk, dk_ref, "dk")
+    assert_close_bf16(dv, dv_ref, "dv")
