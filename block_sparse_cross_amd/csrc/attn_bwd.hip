@@ -526,7 +526,6 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       if (ph < 2) load_sd(ph, i, x % 4);
       else if (ph < 4) load_upd(ph - 2, i / DT, i % DT, x % 4);
     };
-    auto dist = [](int) { return 3; };
     // The key intervals of 8-vector group jj of half hv (masked chunks) are
     // first used in piece NP (hv + 1) + 4 jj / EPP; they are loaded G = 4 / EPP
     // pieces earlier, when the group two back (same register slot) is done.
@@ -539,9 +538,7 @@ attn_bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     load_piece(2);
 #pragma unroll
     for (int pc = 0; pc < 4 * NP; ++pc) {
-#pragma unroll
-      for (int x = pc + 1; x <= pc + 3; ++x)
-        if (x >= 3 && x < 4 * NP && x - dist(x) == pc) load_piece(x);
+      if (pc + 3 < 4 * NP) load_piece(pc + 3);
       if constexpr (MASKED) {
 #pragma unroll
         for (int hv = 0; hv < NH; ++hv)
