@@ -8,7 +8,8 @@ logit scale, so that combinations the fixed cases do not pair up are covered
 too (for instance B = 1 with a group of 3, or one sample whose chunks are all
 local). A second sweep runs the whole method on random shapes: the GPU's plan
 over P ranks, every rank's forward, the merge and every rank's backward, against
-the oracle's unsplit attention over the whole context."""
+the oracle's unsplit attention over the whole context; a third adds the own-block
+keys (the whole mask) and the per-rank form of the merge."""
 import numpy as np
 import pytest
 import torch
@@ -146,3 +147,74 @@ def test_sweep_whole_protocol(i):
     assert_close_bf16(to_f64(dq), dq_ref, "dq summed over ranks")
     assert_close_bf16(dk, dk_ref, "dk")
     assert_close_bf16(dv, dv_ref, "dv")
+
+
+N_FULL_MASK = 8
+
+
+@pytest.mark.parametrize("i", range(N_FULL_MASK))
+def test_sweep_full_mask(i):
+    """The whole mask (Figure 1: each block's rows also attend the B tokens of
+    their own block) on random shapes: every rank's context partial plus the
+    own-block partial, merged over P + 1 partials by the one-kernel merge and
+    by the per-rank form (LSE reduction, then each partial rescaled and summed),
+    against the oracle's whole-mask attention; the backward of every rank and
+    of the own blocks, from the GPU's forward, against the oracle's whole-mask
+    backward."""
+    P, J, p = draw_protocol(100 + i)
+    p.pop("empty_block")
+    print("full-mask case", i, "P", P, "J", J, p, flush=True)
+    c = make_case(9700 + i, empty_block=False, **p)
+    g = np.random.default_rng(9800 + i)
+    Q, S, m, B = c["q"].shape[0], c["S"], c["m"], c["B"]
+    kb = inputs.normal_values(g, (Q, c["hkv"], c["d"]), c["d"] ** -0.5, "bf16")
+    vb = inputs.normal_values(g, (Q, c["hkv"], c["d"]), c["d"] ** -0.5, "bf16")
+    sd, ad = to_dev(c["s"]), to_dev(c["a"])
+    _, _, bundles, _ = [t.cpu().numpy() for t in binding.splitkv_plan(sd, ad, B, S, m, P, J)]
+    qd, dod, kbd, vbd = to_dev(c["q"]), to_dev(c["do"]), to_dev(kb), to_dev(vb)
+    bs, ba, bcs, blen = binding.own_block_local(sd, B)
+    ranks = []
+    for ids in bundles:
+        pos = oracle.local_key_positions(ids.astype(np.int64), m)
+        ranks.append((pos, to_dev(ids.astype(np.int64) * m), to_dev(c["kg"][pos]),
+                      to_dev(c["vg"][pos])))
+    parts = [binding.splitkv_attn_fwd(sd, ad, B, cs, m, qd, k, v) for _, cs, k, v in ranks]
+    parts.append(binding.splitkv_attn_fwd(bs, ba, B, bcs, blen, qd, kbd, vbd))
+    o_parts = torch.stack([x[0] for x in parts])
+    l_parts = torch.stack([x[1] for x in parts])
+    om, lm = binding.splitkv_lse_merge(o_parts, l_parts)
+    # per-rank form: the reduced lse, each partial rescaled to it, summed in fp32
+    lr = binding.splitkv_lse_reduce(l_parts)
+    o_sum = torch.zeros(c["q"].shape, dtype=torch.float32, device="cuda")
+    for x in parts:
+        o_sum += binding.splitkv_lse_rescale(x[0], x[1], lr, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    scale = c["d"] ** -0.5
+    o_ref, l_ref = oracle.full_mask_attn(B, c["s"], c["a"], vals64(c["q"]), np.arange(S),
+                                         vals64(c["kg"]), vals64(c["vg"]), vals64(kb),
+                                         vals64(vb), scale)
+    assert_lse(to_f64(lm), l_ref, "merged lse")
+    assert_close_bf16(to_f64(om), o_ref, "merged o")
+    assert_lse(to_f64(lr), l_ref, "reduced lse")
+    assert_close_bf16(to_f64(o_sum), o_ref, "sum of rescaled partials")
+    # backward from the GPU's own forward
+    dq = torch.zeros(c["q"].shape, dtype=torch.float32, device="cuda")
+    delta = torch.empty((Q, c["hq"]), dtype=torch.float32, device="cuda")
+    grads = []
+    for r, (_, cs, k, v) in enumerate(ranks):
+        ws = binding.bwd_workspace(sd, ad, B, cs, m, c["hq"], c["hkv"], c["d"], torch.bfloat16)
+        grads.append(binding.splitkv_attn_bwd(sd, ad, B, cs, m, qd, k, v, om if r == 0 else None,
+                                              dod, lm, dq, delta=delta, workspace=ws)[:2])
+    ws = binding.bwd_workspace(bs, ba, B, bcs, blen, c["hq"], c["hkv"], c["d"], torch.bfloat16)
+    dkb, dvb, _ = binding.splitkv_attn_bwd(bs, ba, B, bcs, blen, qd, kbd, vbd, None, dod, lm, dq,
+                                           delta=delta, workspace=ws)
+    torch.cuda.synchronize()
+    dq_ref, dk_ref, dv_ref, dkb_ref, dvb_ref = oracle.full_mask_bwd(
+        B, c["s"], c["a"], vals64(c["q"]), vals64(c["do"]), to_f64(om), to_f64(lm),
+        np.arange(S), vals64(c["kg"]), vals64(c["vg"]), vals64(kb), vals64(vb), scale)
+    assert_close_bf16(to_f64(dq), dq_ref, "dq")
+    for r, (pos, _, _, _) in enumerate(ranks):
+        assert_close_bf16(to_f64(grads[r][0]), dk_ref[pos], "dk rank %d" % r)
+        assert_close_bf16(to_f64(grads[r][1]), dv_ref[pos], "dv rank %d" % r)
+    assert_close_bf16(to_f64(dkb), dkb_ref, "dk (own blocks)")
+    assert_close_bf16(to_f64(dvb), dvb_ref, "dv (own blocks)")
