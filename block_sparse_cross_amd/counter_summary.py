@@ -4,6 +4,11 @@ passes of matrix-core and instruction counters, one of LDS counters) and the
 bench line one of them printed (for the plan's live pairs).
 
     python -m block_sparse_cross_amd.counter_summary PASS_A_DIR PASS_B_DIR LDS_DIR BENCH_LOG [--out FILE]
+    python -m block_sparse_cross_amd.counter_summary --trace TRACE_DIR
+
+The second form prints the per-kernel table of a `rocprofv3 --kernel-trace --stats`
+run (its kernel_stats.csv: calls, total, average, min and max time in
+microseconds, share of GPU time), as the kernel-trace profiles show it.
 
 Per kernel, means over its dispatches: the clock (GRBM_GUI_ACTIVE per XCD over
 the dispatch time), matrix-core busy (SQ_VALU_MFMA_BUSY_CYCLES over clock cycles
@@ -135,7 +140,39 @@ def summarize(dir_a: str, dir_b: str, dir_lds: str, bench_log: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def strip_params(name: str) -> str:
+    """A kernel's name without its trailing parameter list."""
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):
+        if name[i] == ")":
+            depth += 1
+        elif name[i] == "(":
+            depth -= 1
+            if depth == 0:
+                return name[:i]
+    return name
+
+
+def trace_table(d: str) -> str:
+    """The kernel_stats.csv of a kernel-trace run as a markdown table, by total time."""
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = sorted(csv.DictReader(open(f)), key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["| kernel | calls | total (us) | average (us) | min (us) | max (us) | % of GPU time |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = strip_params(re.sub(r"^void ", "", r["Name"].replace("(anonymous namespace)::", "")))
+        name = name[len("splitkv::"):] if name.startswith("splitkv::") else name
+        out.append("| %s | %s | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
+            name, r["Calls"], float(r["TotalDurationNs"]) / 1e3, float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
+    argv = sys.argv[1:] if argv is None else argv
+    if argv and argv[0] == "--trace":
+        sys.stdout.write(trace_table(argv[1]))
+        return 0
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("pass_a")
     ap.add_argument("pass_b")
